@@ -1,0 +1,89 @@
+"""Pins of the quantization references: OCP E4M3 code table, exhaustive
+round trips and ties; int8 hand values, ties and error bound."""
+import math
+
+import numpy as np
+
+from oracle import quant as Q
+
+
+def test_e4m3_table_values():
+    # Values from the OCP OFP8 E4M3 definition (bias 7, subnormal m * 2^-9).
+    assert Q.e4m3_decode(0x00) == 0.0
+    assert Q.e4m3_decode(0x01) == 2.0 ** -9
+    assert Q.e4m3_decode(0x07) == 7 * 2.0 ** -9
+    assert Q.e4m3_decode(0x08) == 2.0 ** -6
+    assert Q.e4m3_decode(0x38) == 1.0
+    assert Q.e4m3_decode(0x39) == 1.125
+    assert Q.e4m3_decode(0x7E) == 448.0
+    assert Q.e4m3_decode(0xFE) == -448.0
+    assert Q.e4m3_decode(0x77) == 240.0
+    assert math.isnan(Q.e4m3_decode(0x7F)) and math.isnan(Q.e4m3_decode(0xFF))
+    vals = [Q.e4m3_decode(c) for c in range(0x7F)]
+    assert all(a < b for a, b in zip(vals, vals[1:]))
+
+
+def test_e4m3_round_trip_all_codes():
+    codes = [c for c in range(256) if c not in (0x7F, 0xFF)]
+    vals = np.array([Q.e4m3_decode(c) for c in codes])
+    vals[codes.index(0x80)] = -0.0
+    enc = Q.e4m3_encode(vals)
+    assert list(enc) == codes
+
+
+def test_e4m3_ties_and_saturation():
+    cases = {
+        1.0625: 0x38,          # midpoint of 1.0 (0x38) and 1.125 (0x39) -> even 0x38
+        1.1875: 0x3A,          # midpoint of 1.125 and 1.25 -> even 0x3A
+        1.0624999: 0x38,
+        1.0625001: 0x39,
+        2.0 ** -10: 0x00,      # half the smallest subnormal -> 0 (even)
+        3 * 2.0 ** -10: 0x02,  # midpoint of codes 1 and 2 -> 2
+        432.0: 0x7E,           # midpoint of 416 (0x7D) and 448 (0x7E) -> even 0x7E
+        424.0: 0x7D,
+        449.0: 0x7E, 500.0: 0x7E, 1e6: 0x7E,
+        -1.0625: 0xB8, -500.0: 0xFE,
+    }
+    for x, c in cases.items():
+        assert int(Q.e4m3_encode(np.array([x]))[0]) == c, (x, hex(c))
+
+
+def test_int8_hand_values():
+    x = np.zeros((1, 1, 4, 8), np.float32)
+    x[0, 0, 0, :] = [127.0, 0.5, 1.5, 2.5, -0.5, -1.5, 63.4, -127.0]
+    codes, scales = Q.quantize_int8_blocks(x, block=128)
+    assert scales[0, 0, 0] == np.float32(1.0)
+    assert list(codes[0, 0, 0]) == [127, 0, 2, 2, 0, -2, 63, -127]
+    z = np.zeros((1, 1, 130, 4), np.float32)
+    c, s = Q.quantize_int8_blocks(z)
+    assert s.shape == (1, 1, 2) and not s.any() and not c.any()
+
+
+def test_int8_ragged_blocks_and_error_bound():
+    r = np.random.default_rng(0)
+    x = r.standard_normal((2, 3, 300, 16)).astype(np.float32)
+    codes, scales = Q.quantize_int8_blocks(x)
+    assert scales.shape == (2, 3, 3)
+    for i in range(3):
+        blk = x[:, :, 128 * i:128 * (i + 1)]
+        np.testing.assert_array_equal(scales[:, :, i], (np.abs(blk).max(axis=(2, 3)) / np.float32(127)).astype(np.float32))
+    deq = Q.dequantize_int8(codes, scales)
+    bound = np.repeat(scales, 128, axis=2)[:, :, :300, None] * 0.5 * (1 + 1e-6)
+    assert np.all(np.abs(deq - x) <= bound)
+    assert np.abs(codes).max() == 127
+
+
+def test_fp8_channels_scale_and_bound():
+    r = np.random.default_rng(1)
+    x = (r.standard_normal((1, 2, 257, 8)) * r.uniform(0.5, 2, (1, 2, 1, 8))).astype(np.float32)
+    codes, scales = Q.quantize_fp8_channels(x)
+    np.testing.assert_array_equal(scales, (np.abs(x).max(axis=2) / np.float32(448)).astype(np.float32))
+    deq = Q.dequantize_fp8(codes, scales)
+    # E4M3 has 3 mantissa bits: relative error <= 2^-4 for normals, plus the
+    # subnormal absolute step 2^-10 (half of 2^-9) in scaled units.
+    err = np.abs(deq - x)
+    bound = np.abs(x) * 2.0 ** -4 + scales[:, :, None, :] * 2.0 ** -10 + 1e-12
+    assert np.all(err <= bound)
+    # The absmax entry of every channel encodes to +-448 exactly.
+    dec = Q.e4m3_decode_array(codes)
+    assert np.allclose(np.abs(dec).max(axis=2), 448.0)
