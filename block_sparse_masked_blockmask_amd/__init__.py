@@ -1,0 +1,15 @@
+"""Block-sparse masked attention forward for MI355X (gfx950).
+
+The computation lives in libflexattn.so (HIP kernels behind the C ABI of
+include/flexattn.h); `flexattn` is its ctypes binding with the same entry-point names.
+"""
+from .flexattn import (  # noqa: F401
+    FA_BF16, FA_F32, FA_FP8_E4M3, FA_I8,
+    FA_MASK_CAUSAL, FA_MASK_DOC, FA_MASK_NONE, FA_MASK_PREFIX_LM, FA_MASK_WINDOW,
+    FA_SCORE_ALIBI, FA_SCORE_NONE, FA_SCORE_SOFTCAP,
+    FA_OK, FA_ERR_DEVICE, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED,
+    BlockMask, FlexAttnError, LIB_PATH,
+    flexattn_block_mask_build, flexattn_block_mask_count_bytes, flexattn_block_mask_index_bytes,
+    flexattn_block_mask_workspace_bytes, flexattn_fwd, flexattn_last_error, flexattn_version,
+    lib, tensor_desc,
+)

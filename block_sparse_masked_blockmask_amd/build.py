@@ -1,0 +1,62 @@
+"""Build the HIP library libflexattn.so in-tree for gfx950.
+
+Compiles every source under csrc/ with hipcc into one shared object next to this file.
+All HIP code is built with packed-fp32 instructions disabled (they are avoided on this
+hardware; hipcc's host pass warns that it does not know the feature, which is harmless).
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(HERE, "libflexattn.so")
+SOURCES = ["api.cpp", "blockmask.hip", "fwd.hip"]
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-result", "-I" + INCLUDE, "-I" + CSRC,
+]
+
+
+def build(verbose: bool = False) -> str:
+    """Compile all sources (always) and link libflexattn.so; returns its path."""
+    objdir = os.path.join(ROOT, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs = []
+    procs = []
+    for src in SOURCES:
+        obj = os.path.join(objdir, src + ".o")
+        cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        if src.endswith(".cpp"):
+            cmd[1:1] = ["-x", "hip"]
+        procs.append((src, cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
+        objs.append(obj)
+    failed = []
+    for src, cmd, pr in procs:
+        out, _ = pr.communicate()
+        text = out.decode(errors="replace")
+        if pr.returncode != 0:
+            failed.append((src, text))
+        elif verbose and text.strip():
+            print(text)
+    if failed:
+        msg = "\n".join(f"--- {s} ---\n{t}" for s, t in failed)
+        raise RuntimeError("HIP build failed:\n" + msg)
+    tmp = LIB + ".tmp"
+    link = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
+    r = subprocess.run(link, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n" + r.stdout.decode(errors="replace"))
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,229 @@
+// C-ABI layer: argument validation, error reporting and kernel selection. Every check happens
+// on the host before anything is enqueued, so a non-OK status never leaves partial writes.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "flexattn.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+fa_status fail(fa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+fa_status ok() {
+  g_last_error.clear();
+  return FA_OK;
+}
+
+int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+const int kValidMask = FA_MASK_DOC | FA_MASK_CAUSAL | FA_MASK_WINDOW | FA_MASK_PREFIX_LM;
+const int kValidScore = FA_SCORE_ALIBI | FA_SCORE_SOFTCAP;
+
+// Checks shared by the builder and the forward pass for the mask parameters.
+fa_status check_mask(int mask_kind, const fa_params* p, int Lq, int Lkv) {
+  if (mask_kind & ~kValidMask) return fail(FA_ERR_INVALID_ARG, "unknown mask_kind bits 0x%x", mask_kind);
+  if ((mask_kind & FA_MASK_PREFIX_LM) && (mask_kind & FA_MASK_CAUSAL))
+    return fail(FA_ERR_INVALID_ARG, "PREFIX_LM already contains causal; do not combine it with CAUSAL");
+  if (mask_kind != FA_MASK_NONE && p == nullptr) return fail(FA_ERR_INVALID_ARG, "params is NULL");
+  if ((mask_kind & FA_MASK_WINDOW) && p->window <= 0) return fail(FA_ERR_INVALID_ARG, "window must be > 0");
+  if ((mask_kind & FA_MASK_PREFIX_LM) && p->prefix_len < 0) return fail(FA_ERR_INVALID_ARG, "prefix_len must be >= 0");
+  if ((mask_kind & FA_MASK_DOC) && ((Lq > 0 && p->q_doc == nullptr) || (Lkv > 0 && p->kv_doc == nullptr)))
+    return fail(FA_ERR_INVALID_ARG, "DOC mask needs q_doc and kv_doc");
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* flexattn_last_error(void) { return g_last_error.c_str(); }
+
+int flexattn_version(void) { return 100; }
+
+size_t flexattn_block_mask_index_bytes(int Bm, int Hm, int q_len, int kv_len, int q_block, int kv_block) {
+  if (Bm <= 0 || Hm <= 0 || q_len < 0 || kv_len < 0 || q_block <= 0 || kv_block <= 0) return 0;
+  return (size_t)Bm * Hm * cdiv(q_len, q_block) * cdiv(kv_len, kv_block) * sizeof(int32_t);
+}
+
+size_t flexattn_block_mask_count_bytes(int Bm, int Hm, int q_len, int q_block) {
+  if (Bm <= 0 || Hm <= 0 || q_len < 0 || q_block <= 0) return 0;
+  return (size_t)Bm * Hm * cdiv(q_len, q_block) * sizeof(int32_t);
+}
+
+size_t flexattn_block_mask_workspace_bytes(int mask_kind, int B, int q_len, int kv_len, int q_block, int kv_block) {
+  if (!(mask_kind & FA_MASK_DOC) || B <= 0 || q_len < 0 || kv_len < 0 || q_block <= 0 || kv_block <= 0) return 0;
+  return (size_t)B * (cdiv(q_len, q_block) + cdiv(kv_len, kv_block)) * 2 * sizeof(int32_t);
+}
+
+fa_status flexattn_block_mask_build(int mask_kind, const fa_params* p, int B, int q_len, int kv_len,
+                                    fa_block_mask* out, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+  fa_status st = check_mask(mask_kind, p, q_len, kv_len);
+  if (st != FA_OK) return st;
+  if (out == nullptr) return fail(FA_ERR_INVALID_ARG, "out is NULL");
+  if (B <= 0 || B > 65535) return fail(FA_ERR_INVALID_ARG, "B must be in [1, 65535] (got %d)", B);
+  if (q_len < 0 || kv_len < 0) return fail(FA_ERR_INVALID_ARG, "negative sequence length");
+  if (out->q_len != q_len || out->kv_len != kv_len)
+    return fail(FA_ERR_INVALID_ARG, "out->q_len/kv_len (%d, %d) differ from q_len/kv_len (%d, %d)",
+                out->q_len, out->kv_len, q_len, kv_len);
+  if ((out->q_block != 64 && out->q_block != 128) || (out->kv_block != 64 && out->kv_block != 128))
+    return fail(FA_ERR_UNSUPPORTED, "block sizes must be 64 or 128 (got %d x %d)", out->q_block, out->kv_block);
+  if (out->n_qb != cdiv(q_len, out->q_block) || out->n_kvb != cdiv(kv_len, out->kv_block))
+    return fail(FA_ERR_INVALID_ARG, "n_qb/n_kvb (%d, %d) do not match ceil(len / block)", out->n_qb, out->n_kvb);
+  if (out->Hm != 1) return fail(FA_ERR_INVALID_ARG, "Hm must be 1: no mask flag depends on the head");
+  if ((mask_kind & FA_MASK_DOC) ? out->Bm != B : (out->Bm != 1 && out->Bm != B))
+    return fail(FA_ERR_INVALID_ARG, "Bm must be B with DOC, else 1 or B (got %d)", out->Bm);
+  if (out->n_qb > 0 && (!out->kv_num_blocks || !out->full_kv_num_blocks))
+    return fail(FA_ERR_INVALID_ARG, "BlockMask count arrays are NULL");
+  if (out->n_qb > 0 && out->n_kvb > 0 && (!out->kv_indices || !out->full_kv_indices))
+    return fail(FA_ERR_INVALID_ARG, "BlockMask index arrays are NULL");
+  const size_t need = flexattn_block_mask_workspace_bytes(mask_kind, B, q_len, kv_len, out->q_block, out->kv_block);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(FA_ERR_INVALID_ARG, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+  fa::BlockMaskArgs a{};
+  a.flags = mask_kind;
+  a.window = (mask_kind & FA_MASK_WINDOW) ? p->window : 0;
+  a.prefix_len = (mask_kind & FA_MASK_PREFIX_LM) ? p->prefix_len : 0;
+  a.B = B;
+  a.Lq = q_len;
+  a.Lkv = kv_len;
+  a.BQ = out->q_block;
+  a.BK = out->kv_block;
+  a.nqb = out->n_qb;
+  a.nkvb = out->n_kvb;
+  a.Bm = out->Bm;
+  a.q_doc = (mask_kind & FA_MASK_DOC) ? p->q_doc : nullptr;
+  a.kv_doc = (mask_kind & FA_MASK_DOC) ? p->kv_doc : nullptr;
+  if (need > 0) {
+    a.qsum = static_cast<int*>(workspace);
+    a.kvsum = a.qsum + (size_t)B * a.nqb * 2;
+  }
+  a.kv_num = out->kv_num_blocks;
+  a.kv_idx = out->kv_indices;
+  a.full_num = out->full_kv_num_blocks;
+  a.full_idx = out->full_kv_indices;
+  hipError_t e = fa::launch_block_mask(a, stream);
+  if (e != hipSuccess) return fail(FA_ERR_DEVICE, "block mask launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+static fa_status check_tensor(const fa_tensor* t, const char* name, int elem_align) {
+  if (t == nullptr) return fail(FA_ERR_INVALID_ARG, "%s is NULL", name);
+  if (t->B < 0 || t->H <= 0 || t->L < 0 || t->D <= 0) return fail(FA_ERR_INVALID_ARG, "%s has invalid shape", name);
+  if (t->data == nullptr && (int64_t)t->B * t->L > 0) return fail(FA_ERR_INVALID_ARG, "%s->data is NULL", name);
+  if (!aligned16(t->data)) return fail(FA_ERR_INVALID_ARG, "%s->data must be 16-byte aligned", name);
+  if (t->stride_b < 0 || t->stride_h < 0 || t->stride_l < t->D)
+    return fail(FA_ERR_INVALID_ARG, "%s strides must be non-negative with stride_l >= D", name);
+  if (t->stride_b % elem_align || t->stride_h % elem_align || t->stride_l % elem_align)
+    return fail(FA_ERR_INVALID_ARG, "%s strides must be multiples of %d elements", name, elem_align);
+  if (t->scale != nullptr) return fail(FA_ERR_INVALID_ARG, "%s->scale must be NULL for this dtype", name);
+  return FA_OK;
+}
+
+fa_status flexattn_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_block_mask* bm,
+                       int mask_kind, int score_kind, const fa_params* p, fa_tensor* out, float* lse,
+                       hipStream_t stream) {
+  if (!q || !k || !v || !out) return fail(FA_ERR_INVALID_ARG, "q, k, v and out must not be NULL");
+  const int dt = q->dtype;
+  if (k->dtype != dt || v->dtype != dt || out->dtype != dt)
+    return fail(FA_ERR_INVALID_ARG, "q, k, v and out must share one dtype");
+  if (dt != FA_F32 && dt != FA_BF16)
+    return fail(FA_ERR_UNSUPPORTED, "dtype %d is not served by flexattn_fwd (f32 or bf16)", dt);
+  const int ea = dt == FA_BF16 ? 8 : 4;
+  fa_status st;
+  if ((st = check_tensor(q, "q", ea)) != FA_OK) return st;
+  if ((st = check_tensor(k, "k", ea)) != FA_OK) return st;
+  if ((st = check_tensor(v, "v", ea)) != FA_OK) return st;
+  if ((st = check_tensor(out, "out", ea)) != FA_OK) return st;
+  if (q->D != 128 || k->D != 128 || v->D != 128 || out->D != 128)
+    return fail(FA_ERR_UNSUPPORTED, "head dim must be 128 (got q %d, k %d, v %d)", q->D, k->D, v->D);
+  if (k->B != q->B || v->B != q->B || out->B != q->B) return fail(FA_ERR_INVALID_ARG, "batch sizes differ");
+  if (k->H != v->H || k->L != v->L) return fail(FA_ERR_INVALID_ARG, "k and v shapes differ");
+  if (q->H % k->H != 0) return fail(FA_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", q->H, k->H);
+  if (out->H != q->H || out->L != q->L) return fail(FA_ERR_INVALID_ARG, "out shape differs from q");
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(FA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  if ((st = check_mask(mask_kind, p, q->L, k->L)) != FA_OK) return st;
+  if (score_kind & ~kValidScore) return fail(FA_ERR_INVALID_ARG, "unknown score_kind bits 0x%x", score_kind);
+  if (score_kind != FA_SCORE_NONE && p == nullptr) return fail(FA_ERR_INVALID_ARG, "params is NULL");
+  if ((score_kind & FA_SCORE_ALIBI) && p->alibi_slopes == nullptr)
+    return fail(FA_ERR_INVALID_ARG, "ALIBI needs alibi_slopes");
+  if ((score_kind & FA_SCORE_SOFTCAP) && !(p->softcap > 0.f) )
+    return fail(FA_ERR_INVALID_ARG, "SOFTCAP needs softcap > 0");
+
+  const int B = q->B, Lq = q->L, Lkv = k->L;
+  int kv_block = 128;
+  fa::FwdArgs a{};
+  if (bm == nullptr) {
+    if (mask_kind != FA_MASK_NONE) return fail(FA_ERR_INVALID_ARG, "a BlockMask is required unless mask_kind is NONE");
+    a.all_full = 1;
+    a.Bm = a.Hm = 1;
+    a.nqb = cdiv(Lq, 128);
+    a.nkvb = cdiv(Lkv, kv_block);
+  } else {
+    if (bm->q_len != Lq || bm->kv_len != Lkv)
+      return fail(FA_ERR_INVALID_ARG, "BlockMask was built for lengths (%d, %d), not (%d, %d)", bm->q_len, bm->kv_len, Lq, Lkv);
+    if (bm->q_block != 128) return fail(FA_ERR_UNSUPPORTED, "q_block must be 128 (got %d)", bm->q_block);
+    if (bm->kv_block != 64 && bm->kv_block != 128)
+      return fail(FA_ERR_UNSUPPORTED, "kv_block must be 64 or 128 (got %d)", bm->kv_block);
+    if (bm->n_qb != cdiv(Lq, bm->q_block) || bm->n_kvb != cdiv(Lkv, bm->kv_block))
+      return fail(FA_ERR_INVALID_ARG, "BlockMask n_qb/n_kvb do not match its lengths and block sizes");
+    if (bm->Bm != 1 && bm->Bm != B) return fail(FA_ERR_INVALID_ARG, "BlockMask Bm must be 1 or B");
+    if (bm->Hm != 1 && bm->Hm != q->H) return fail(FA_ERR_INVALID_ARG, "BlockMask Hm must be 1 or Hq");
+    if (bm->n_qb > 0 && (!bm->kv_num_blocks || !bm->full_kv_num_blocks || (bm->n_kvb > 0 && (!bm->kv_indices || !bm->full_kv_indices))))
+      return fail(FA_ERR_INVALID_ARG, "BlockMask arrays are NULL");
+    kv_block = bm->kv_block;
+    a.all_full = 0;
+    a.Bm = bm->Bm;
+    a.Hm = bm->Hm;
+    a.nqb = bm->n_qb;
+    a.nkvb = bm->n_kvb;
+    a.kv_num = bm->kv_num_blocks;
+    a.kv_idx = bm->kv_indices;
+    a.full_num = bm->full_kv_num_blocks;
+    a.full_idx = bm->full_kv_indices;
+  }
+  const int64_t total = (int64_t)B * q->H * a.nqb;
+  if (total > 0x7fffffff) return fail(FA_ERR_UNSUPPORTED, "grid too large (%lld workgroups)", (long long)total);
+
+  a.q = q->data; a.k = k->data; a.v = v->data; a.o = out->data; a.lse = lse;
+  a.q_sb = q->stride_b; a.q_sh = q->stride_h; a.q_sl = q->stride_l;
+  a.k_sb = k->stride_b; a.k_sh = k->stride_h; a.k_sl = k->stride_l;
+  a.v_sb = v->stride_b; a.v_sh = v->stride_h; a.v_sl = v->stride_l;
+  a.o_sb = out->stride_b; a.o_sh = out->stride_h; a.o_sl = out->stride_l;
+  a.B = B; a.Hq = q->H; a.Hkv = k->H; a.Lq = Lq; a.Lkv = Lkv; a.group = q->H / k->H;
+  a.flags = mask_kind;
+  a.window = (mask_kind & FA_MASK_WINDOW) ? p->window : 0;
+  a.prefix_len = (mask_kind & FA_MASK_PREFIX_LM) ? p->prefix_len : 0;
+  a.q_doc = (mask_kind & FA_MASK_DOC) ? p->q_doc : nullptr;
+  a.kv_doc = (mask_kind & FA_MASK_DOC) ? p->kv_doc : nullptr;
+  const float sm = (p && p->sm_scale > 0.f) ? p->sm_scale : 1.0f / std::sqrt((float)q->D);
+  a.sm_scale = sm;
+  a.scale_log2 = sm * 1.4426950408889634f;
+  a.softcap = (score_kind & FA_SCORE_SOFTCAP) ? p->softcap : 0.f;
+  a.inv_softcap = (score_kind & FA_SCORE_SOFTCAP) ? 1.0f / p->softcap : 0.f;
+  a.slopes = (score_kind & FA_SCORE_ALIBI) ? p->alibi_slopes : nullptr;
+  a.total_wg = (int)total;
+  hipError_t e = fa::launch_fwd(a, dt == FA_BF16 ? 1 : 0, kv_block, score_kind, stream);
+  if (e != hipSuccess) return fail(FA_ERR_DEVICE, "forward launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

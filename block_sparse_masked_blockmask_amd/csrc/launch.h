@@ -1,0 +1,52 @@
+// Kernel argument blocks and launchers (host side). The C-ABI layer (api.cpp) validates every
+// argument and then calls these; they only enqueue work on the given stream.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct BlockMaskArgs {
+  int flags, window, prefix_len;
+  int B, Lq, Lkv, BQ, BK, nqb, nkvb, Bm;
+  const int* q_doc;
+  const int* kv_doc;
+  int* qsum;    // [B][nqb][2] min, max document id of each query block (DOC only)
+  int* kvsum;   // [B][nkvb][2]
+  int* kv_num;
+  int* kv_idx;
+  int* full_num;
+  int* full_idx;
+};
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int64_t q_sb, q_sh, q_sl;
+  int64_t k_sb, k_sh, k_sl;
+  int64_t v_sb, v_sh, v_sl;
+  int64_t o_sb, o_sh, o_sl;
+  int B, Hq, Hkv, Lq, Lkv, group;
+  // BlockMask (all_full = 1: no BlockMask, every tile is full)
+  const int* kv_num;
+  const int* kv_idx;
+  const int* full_num;
+  const int* full_idx;
+  int Bm, Hm, nqb, nkvb, all_full;
+  // mask_mod / score_mod
+  int flags, window, prefix_len;
+  const int* q_doc;
+  const int* kv_doc;
+  float sm_scale, scale_log2, softcap, inv_softcap;
+  const float* slopes;
+  int total_wg;
+};
+
+hipError_t launch_block_mask(const BlockMaskArgs& a, hipStream_t stream);
+// dtype 0 = f32, 1 = bf16; kv_block in {64, 128}; score bits FA_SCORE_*.
+hipError_t launch_fwd(const FwdArgs& a, int dtype, int kv_block, int score, hipStream_t stream);
+
+}  // namespace fa

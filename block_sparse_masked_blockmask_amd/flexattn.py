@@ -1,0 +1,195 @@
+"""Python binding of libflexattn.so (ctypes): argument marshalling only.
+
+Every entry point has the name of the C function it calls (include/flexattn.h) and only
+turns torch tensors into the ABI's descriptors; all computation happens in the HIP kernels.
+PyTorch provides device memory and the current stream. If the library is not built, every
+call raises: there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_float, c_int, c_int32, c_int64, c_size_t, c_void_p
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libflexattn.so")
+
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_DEVICE = 0, 1, 2, 3
+FA_F32, FA_BF16, FA_I8, FA_FP8_E4M3 = 0, 1, 2, 3
+FA_MASK_NONE, FA_MASK_DOC, FA_MASK_CAUSAL, FA_MASK_WINDOW, FA_MASK_PREFIX_LM = 0, 1, 2, 4, 8
+FA_SCORE_NONE, FA_SCORE_ALIBI, FA_SCORE_SOFTCAP = 0, 1, 2
+
+
+class FaTensor(ctypes.Structure):
+    _fields_ = [("data", c_void_p), ("dtype", c_int32), ("B", c_int32), ("H", c_int32),
+                ("L", c_int32), ("D", c_int32), ("stride_b", c_int64), ("stride_h", c_int64),
+                ("stride_l", c_int64), ("scale", c_void_p)]
+
+
+class FaParams(ctypes.Structure):
+    _fields_ = [("sm_scale", c_float), ("window", c_int32), ("prefix_len", c_int32),
+                ("softcap", c_float), ("alibi_slopes", c_void_p), ("q_doc", c_void_p),
+                ("kv_doc", c_void_p)]
+
+
+class FaBlockMask(ctypes.Structure):
+    _fields_ = [("Bm", c_int32), ("Hm", c_int32), ("q_len", c_int32), ("kv_len", c_int32),
+                ("q_block", c_int32), ("kv_block", c_int32), ("n_qb", c_int32), ("n_kvb", c_int32),
+                ("kv_num_blocks", c_void_p), ("kv_indices", c_void_p),
+                ("full_kv_num_blocks", c_void_p), ("full_kv_indices", c_void_p)]
+
+
+class FlexAttnError(RuntimeError):
+    def __init__(self, status: int, reason: str):
+        super().__init__(f"flexattn status {status}: {reason}")
+        self.status = status
+        self.reason = reason
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libflexattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+        L = ctypes.CDLL(LIB_PATH)
+        L.flexattn_block_mask_index_bytes.argtypes = [c_int] * 6
+        L.flexattn_block_mask_index_bytes.restype = c_size_t
+        L.flexattn_block_mask_count_bytes.argtypes = [c_int] * 4
+        L.flexattn_block_mask_count_bytes.restype = c_size_t
+        L.flexattn_block_mask_workspace_bytes.argtypes = [c_int] * 6
+        L.flexattn_block_mask_workspace_bytes.restype = c_size_t
+        L.flexattn_block_mask_build.argtypes = [c_int, POINTER(FaParams), c_int, c_int, c_int,
+                                                POINTER(FaBlockMask), c_void_p, c_size_t, c_void_p]
+        L.flexattn_block_mask_build.restype = c_int
+        L.flexattn_fwd.argtypes = [POINTER(FaTensor), POINTER(FaTensor), POINTER(FaTensor),
+                                   POINTER(FaBlockMask), c_int, c_int, POINTER(FaParams),
+                                   POINTER(FaTensor), c_void_p, c_void_p]
+        L.flexattn_fwd.restype = c_int
+        L.flexattn_last_error.argtypes = []
+        L.flexattn_last_error.restype = ctypes.c_char_p
+        L.flexattn_version.argtypes = []
+        L.flexattn_version.restype = c_int
+        _lib = L
+    return _lib
+
+
+def flexattn_last_error() -> str:
+    return lib().flexattn_last_error().decode()
+
+
+def flexattn_version() -> int:
+    return lib().flexattn_version()
+
+
+def _check(status: int):
+    if status != FA_OK:
+        raise FlexAttnError(status, flexattn_last_error())
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+_DTYPES = {torch.float32: FA_F32, torch.bfloat16: FA_BF16, torch.int8: FA_I8, torch.uint8: FA_FP8_E4M3}
+
+
+def tensor_desc(t: torch.Tensor, scale: Optional[torch.Tensor] = None) -> FaTensor:
+    """Descriptor of a [B, H, L, D] tensor whose last dimension is contiguous."""
+    if t.dim() != 4:
+        raise ValueError("attention tensors are [B, H, L, D]")
+    if t.stride(3) != 1:
+        raise ValueError("the D dimension must be contiguous")
+    B, H, L, D = t.shape
+    return FaTensor(t.data_ptr(), _DTYPES[t.dtype], B, H, L, D, t.stride(0), t.stride(1), t.stride(2),
+                    _ptr(scale))
+
+
+def flexattn_block_mask_index_bytes(Bm, Hm, q_len, kv_len, q_block, kv_block) -> int:
+    return lib().flexattn_block_mask_index_bytes(Bm, Hm, q_len, kv_len, q_block, kv_block)
+
+
+def flexattn_block_mask_count_bytes(Bm, Hm, q_len, q_block) -> int:
+    return lib().flexattn_block_mask_count_bytes(Bm, Hm, q_len, q_block)
+
+
+def flexattn_block_mask_workspace_bytes(mask_kind, B, q_len, kv_len, q_block, kv_block) -> int:
+    return lib().flexattn_block_mask_workspace_bytes(mask_kind, B, q_len, kv_len, q_block, kv_block)
+
+
+class BlockMask:
+    """Device BlockMask: the four int32 arrays plus their dimensions (caller-owned memory)."""
+
+    def __init__(self, Bm, Hm, q_len, kv_len, q_block, kv_block, device):
+        self.Bm, self.Hm, self.q_len, self.kv_len = Bm, Hm, q_len, kv_len
+        self.q_block, self.kv_block = q_block, kv_block
+        self.n_qb = -(-q_len // q_block)
+        self.n_kvb = -(-kv_len // kv_block)
+        z = dict(dtype=torch.int32, device=device)
+        self.kv_num_blocks = torch.empty((Bm, Hm, self.n_qb), **z)
+        self.full_kv_num_blocks = torch.empty((Bm, Hm, self.n_qb), **z)
+        self.kv_indices = torch.empty((Bm, Hm, self.n_qb, self.n_kvb), **z)
+        self.full_kv_indices = torch.empty((Bm, Hm, self.n_qb, self.n_kvb), **z)
+
+    def as_struct(self) -> FaBlockMask:
+        return FaBlockMask(self.Bm, self.Hm, self.q_len, self.kv_len, self.q_block, self.kv_block,
+                           self.n_qb, self.n_kvb, self.kv_num_blocks.data_ptr(), self.kv_indices.data_ptr(),
+                           self.full_kv_num_blocks.data_ptr(), self.full_kv_indices.data_ptr())
+
+
+def _params(window=0, prefix_len=0, softcap=0.0, alibi_slopes=None, q_doc=None, kv_doc=None, sm_scale=0.0):
+    return FaParams(float(sm_scale), int(window), int(prefix_len), float(softcap), _ptr(alibi_slopes),
+                    _ptr(q_doc), _ptr(kv_doc))
+
+
+def flexattn_block_mask_build(mask_kind: int, B: int, q_len: int, kv_len: int, q_block: int = 128,
+                              kv_block: int = 128, *, q_doc=None, kv_doc=None, window: int = 0,
+                              prefix_len: int = 0, device=None, stream=None, out: Optional[BlockMask] = None,
+                              workspace: Optional[torch.Tensor] = None) -> BlockMask:
+    """Build a BlockMask on the device (create_block_mask of the FlexAttention guide)."""
+    if device is None:
+        device = q_doc.device if q_doc is not None else torch.device("cuda", torch.cuda.current_device())
+    if out is None:
+        Bm = B if (mask_kind & FA_MASK_DOC) else 1
+        out = BlockMask(Bm, 1, q_len, kv_len, q_block, kv_block, device)
+    ws_bytes = flexattn_block_mask_workspace_bytes(mask_kind, B, q_len, kv_len, q_block, kv_block)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=device)
+    p = _params(window=window, prefix_len=prefix_len, q_doc=q_doc, kv_doc=kv_doc)
+    s = out.as_struct()
+    _check(lib().flexattn_block_mask_build(mask_kind, ctypes.byref(p), B, q_len, kv_len, ctypes.byref(s),
+                                           _ptr(workspace), workspace.numel() if workspace is not None else 0,
+                                           _stream(stream)))
+    return out
+
+
+def flexattn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_mask: Optional[BlockMask] = None,
+                 mask_kind: int = FA_MASK_NONE, score_kind: int = FA_SCORE_NONE, *, window: int = 0,
+                 prefix_len: int = 0, softcap: float = 0.0, alibi_slopes=None, q_doc=None, kv_doc=None,
+                 sm_scale: float = 0.0, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                 return_lse: bool = True, stream=None):
+    """Forward pass; returns (out, lse). lse is None when return_lse is False and none is given."""
+    if out is None:
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != tuple(q.shape[:3])):
+        raise ValueError("lse must be a contiguous float32 [B, Hq, Lq] tensor")
+    tq, tk, tv, to = tensor_desc(q), tensor_desc(k), tensor_desc(v), tensor_desc(out)
+    p = _params(window=window, prefix_len=prefix_len, softcap=softcap, alibi_slopes=alibi_slopes,
+                q_doc=q_doc, kv_doc=kv_doc, sm_scale=sm_scale)
+    bm = ctypes.byref(block_mask.as_struct()) if block_mask is not None else None
+    _check(lib().flexattn_fwd(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), bm, mask_kind, score_kind,
+                              ctypes.byref(p), ctypes.byref(to), _ptr(lse), _stream(stream)))
+    return out, lse

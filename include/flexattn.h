@@ -1,0 +1,151 @@
+/*
+ * flexattn.h — C ABI of the block-sparse masked attention forward for MI355X (gfx950).
+ *
+ * The operation (FlexAttention guide, "The Core Design Principles"):
+ *     out_i = sum_j softmax_j( score_mod(q_i . k_j * sm_scale) restricted to mask_mod(i, j) ) v_j
+ * computed tile by tile with an online softmax; tiles that the mask leaves empty are never
+ * loaded, using a precomputed BlockMask (guide, "Systems Mechanics", item 1: full tiles run
+ * without mask branches, empty tiles are skipped, partial tiles are masked per token).
+ *
+ * Because score_mod and mask_mod are user functions on that page, this ABI exposes a fixed set
+ * of them as bit flags (below). All predicates use absolute token positions.
+ *
+ * Conventions shared by every entry point:
+ *   - Every buffer is owned by the caller. The library allocates no device memory and never
+ *     synchronises the host; all work is enqueued on the caller's `stream` and is asynchronous.
+ *     Kernel faults surface at the caller's next synchronisation.
+ *   - Device pointers must point into memory of the current HIP device.
+ *   - On any status other than FA_OK nothing has been enqueued and no output has been written;
+ *     flexattn_last_error() gives the reason. There is no silent fallback path.
+ *   - Calls are thread safe; calls that overlap on the same output buffers race.
+ */
+#ifndef FLEXATTN_H
+#define FLEXATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = 1,   /* caller bug: null/misaligned pointer, shape mismatch, bad flags */
+  FA_ERR_UNSUPPORTED = 2,   /* valid request outside what this library serves (reason given) */
+  FA_ERR_DEVICE = 3         /* HIP reported an error while enqueuing (reason given) */
+} fa_status;
+
+typedef enum {
+  FA_F32 = 0,        /* float32 */
+  FA_BF16 = 1,       /* bfloat16 */
+  FA_I8 = 2,         /* int8 codes with float32 scales (quantized form) */
+  FA_FP8_E4M3 = 3    /* OCP E4M3 codes with float32 scales (quantized form) */
+} fa_dtype;
+
+/* mask_mod flags; the enabled predicates are ANDed (the guide's demo ANDs causal and window).
+ *   DOC       q_doc[b][i] == kv_doc[b][j]   (guide, "Production Engineering" 1: document
+ *             packing; also TiRex2's grouped variate attention, where packed variates of
+ *             unrelated groups are masked — TiRex2 PR "perf: expose FlexAttention loader
+ *             override", "Context")
+ *   CAUSAL    i >= j                        (guide, "Implementation" demo)
+ *   WINDOW    i - j < window                (guide demo's sliding window; strict, so the demo's
+ *             "<= 512" is window = 513)
+ *   PREFIX_LM j < prefix_len || i >= j      (guide, "Production Engineering" 2; it contains
+ *             causal, so PREFIX_LM together with CAUSAL is rejected as FA_ERR_INVALID_ARG) */
+enum { FA_MASK_NONE = 0, FA_MASK_DOC = 1, FA_MASK_CAUSAL = 2, FA_MASK_WINDOW = 4, FA_MASK_PREFIX_LM = 8 };
+
+/* score_mod flags, applied to the scaled score s in this order:
+ *   ALIBI     s - alibi_slopes[h] * |i - j|   (guide demo; h is the query head)
+ *   SOFTCAP   softcap * tanh(s / softcap)     (guide, "The Problem": logit soft-capping) */
+enum { FA_SCORE_NONE = 0, FA_SCORE_ALIBI = 1, FA_SCORE_SOFTCAP = 2 };
+
+/* A [B, H, L, D] tensor in device memory; element strides, the D dimension contiguous.
+ * `scale` (device, float32) is used by the quantized dtypes only and must be NULL otherwise. */
+typedef struct {
+  void* data;
+  int32_t dtype;                 /* fa_dtype */
+  int32_t B, H, L, D;
+  int64_t stride_b, stride_h, stride_l;
+  const float* scale;
+} fa_tensor;
+
+typedef struct {
+  float sm_scale;                /* <= 0 selects 1/sqrt(D) */
+  int32_t window;                /* WINDOW: must be > 0 */
+  int32_t prefix_len;            /* PREFIX_LM: must be >= 0 */
+  float softcap;                 /* SOFTCAP: C, must be > 0 */
+  const float* alibi_slopes;     /* ALIBI: float32 [Hq], device */
+  const int32_t* q_doc;          /* DOC: int32 [B][Lq], device, contiguous */
+  const int32_t* kv_doc;         /* DOC: int32 [B][Lkv], device, contiguous; may alias q_doc */
+} fa_params;
+
+/* BlockMask (guide, "Systems Mechanics" 1; field names as in FlexAttention's BlockMask).
+ * For each mask row (bm, hm) and query block qb, the kv blocks whose tiles are partial
+ * (kv_indices) and full (full_kv_indices), each list ascending with its length in the
+ * matching *_num_blocks entry and the unused tail set to 0. Shapes (int32, device):
+ *   kv_num_blocks, full_kv_num_blocks : [Bm][Hm][n_qb]
+ *   kv_indices, full_kv_indices       : [Bm][Hm][n_qb][n_kvb]
+ * n_qb = ceil(q_len / q_block), n_kvb = ceil(kv_len / kv_block). Bm is 1 (one row set for
+ * every batch) or B; Hm is 1 or Hq. A tile is classified over its in-range pairs only, so a
+ * ragged edge tile whose in-range pairs are all allowed is full. */
+typedef struct {
+  int32_t Bm, Hm, q_len, kv_len, q_block, kv_block, n_qb, n_kvb;
+  int32_t* kv_num_blocks;
+  int32_t* kv_indices;
+  int32_t* full_kv_num_blocks;
+  int32_t* full_kv_indices;
+} fa_block_mask;
+
+/* Bytes of ONE index array ([Bm][Hm][n_qb][n_kvb] int32) and of ONE count array
+ * ([Bm][Hm][n_qb] int32) for the given dimensions; 0 on invalid dimensions. */
+size_t flexattn_block_mask_index_bytes(int Bm, int Hm, int q_len, int kv_len, int q_block, int kv_block);
+size_t flexattn_block_mask_count_bytes(int Bm, int Hm, int q_len, int q_block);
+
+/* Device scratch needed by flexattn_block_mask_build (per-block document-id ranges when DOC is
+ * set, else 0). */
+size_t flexattn_block_mask_workspace_bytes(int mask_kind, int B, int q_len, int kv_len,
+                                           int q_block, int kv_block);
+
+/* Build a BlockMask on the device by classifying every (q block, kv block) tile as full,
+ * partial or empty under mask_kind (guide, "Systems Mechanics" 1: create_block_mask evaluates
+ * the mask over each block's bounding box). The caller fills `out`'s dimensions (Bm, Hm, q_len,
+ * kv_len, q_block, kv_block, n_qb, n_kvb) and its four array pointers; Bm must be B when DOC is
+ * set (1 or B otherwise), Hm must be 1 (no flag depends on the head). q_block and kv_block are
+ * 64 or 128. Reads p->q_doc / p->kv_doc (DOC), p->window (WINDOW), p->prefix_len (PREFIX_LM).
+ * `workspace` must hold flexattn_block_mask_workspace_bytes(...) bytes (may be NULL if 0).
+ * Classification is exact: the lists equal exhaustive evaluation of every in-range pair. */
+fa_status flexattn_block_mask_build(int mask_kind, const fa_params* p, int B, int q_len, int kv_len,
+                                    fa_block_mask* out, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
+
+/* Forward pass. q [B][Hq][Lq][D], k and v [B][Hkv][Lkv][D], out [B][Hq][Lq][D] (same dtype as q),
+ * lse [B][Hq][Lq] float32 contiguous (natural log; may be NULL). Supported envelope:
+ *   - D = 128;
+ *   - dtypes: all FA_F32 (float32 MFMA, fp32 softmax) or all FA_BF16 (bf16 MFMA with fp32
+ *     accumulation and softmax; P rounded to bf16 before P.V);
+ *   - Hq a multiple of Hkv (GQA: query head h reads kv head h / (Hq / Hkv));
+ *   - data pointers 16-byte aligned and stride_b/h/l multiples of 8 elements (bf16) or
+ *     4 elements (f32);
+ *   - bm->q_block = 128 and bm->kv_block in {64, 128}.
+ * `bm` may be NULL only when mask_kind is FA_MASK_NONE: every tile is then full.
+ * The kernel trusts the BlockMask for which tiles to visit and evaluates mask_kind on partial
+ * tiles (and on the ragged last kv block) only, like FlexAttention: a BlockMask built for a
+ * different mask gives results for that mask's tile set.
+ * A query row with no allowed key produces out = 0 and lse = -inf. */
+fa_status flexattn_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v,
+                       const fa_block_mask* bm, int mask_kind, int score_kind, const fa_params* p,
+                       fa_tensor* out, float* lse, hipStream_t stream);
+
+/* Reason for the last non-OK status returned on this thread ("" if none). */
+const char* flexattn_last_error(void);
+
+/* ABI version (major * 100 + minor). */
+int flexattn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLEXATTN_H */

@@ -1,0 +1,154 @@
+"""CPU checks of the C ABI: the library loads, exports every declared entry point, sizes
+are right, and argument validation rejects bad calls before anything is enqueued
+(these calls return before any HIP API call, so no GPU is needed)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import block_sparse_masked_blockmask_amd as fa
+from block_sparse_masked_blockmask_amd.flexattn import FaBlockMask, FaParams, FaTensor
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flexattn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(flexattn_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 7
+    lib = fa.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\sT\s(flexattn_\w+)", out))
+    assert set(names) <= exported, set(names) - exported
+
+
+def test_struct_sizes_match_abi():
+    # fa_tensor: ptr, 5 x int32, 3 x int64, ptr with natural alignment.
+    assert ctypes.sizeof(FaTensor) == 8 + 4 * 5 + 4 + 8 * 3 + 8
+    assert ctypes.sizeof(FaParams) == 4 * 4 + 8 * 3
+    assert ctypes.sizeof(FaBlockMask) == 4 * 8 + 8 * 4
+
+
+def test_sizes():
+    assert fa.flexattn_block_mask_index_bytes(2, 1, 300, 200, 128, 64) == 2 * 3 * 4 * 4
+    assert fa.flexattn_block_mask_count_bytes(2, 1, 300, 128) == 2 * 3 * 4
+    assert fa.flexattn_block_mask_workspace_bytes(fa.FA_MASK_CAUSAL, 2, 300, 200, 128, 64) == 0
+    assert fa.flexattn_block_mask_workspace_bytes(fa.FA_MASK_DOC, 2, 300, 200, 128, 64) == 2 * (3 + 4) * 8
+    assert fa.flexattn_block_mask_index_bytes(0, 1, 10, 10, 128, 128) == 0
+    assert fa.flexattn_version() >= 100
+
+
+def _t(dtype=fa.FA_BF16, B=1, H=2, L=100, D=128, data=256):
+    return FaTensor(data, dtype, B, H, L, D, H * L * D, L * D, D, None)
+
+
+def _fwd(q, k, v, out, bm=None, mask=0, score=0, p=None):
+    lib = fa.lib()
+    p = p or FaParams(0.0, 0, 0, 0.0, None, None, None)
+    return lib.flexattn_fwd(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v),
+                            None if bm is None else ctypes.byref(bm), mask, score, ctypes.byref(p),
+                            ctypes.byref(out), None, None)
+
+
+@pytest.mark.parametrize("case,status,needle", [
+    ("null", fa.FA_ERR_INVALID_ARG, "must not be NULL"),
+    ("d64", fa.FA_ERR_UNSUPPORTED, "head dim"),
+    ("gqa", fa.FA_ERR_INVALID_ARG, "multiple of Hkv"),
+    ("dtype_mix", fa.FA_ERR_INVALID_ARG, "share one dtype"),
+    ("i8", fa.FA_ERR_UNSUPPORTED, "dtype"),
+    ("prefix_causal", fa.FA_ERR_INVALID_ARG, "PREFIX_LM"),
+    ("no_bm", fa.FA_ERR_INVALID_ARG, "BlockMask is required"),
+    ("misaligned", fa.FA_ERR_INVALID_ARG, "16-byte aligned"),
+    ("stride", fa.FA_ERR_INVALID_ARG, "multiples of 8"),
+    ("window0", fa.FA_ERR_INVALID_ARG, "window"),
+    ("softcap0", fa.FA_ERR_INVALID_ARG, "softcap"),
+    ("alibi_null", fa.FA_ERR_INVALID_ARG, "alibi"),
+    ("bm_len", fa.FA_ERR_INVALID_ARG, "built for lengths"),
+    ("bm_qblock", fa.FA_ERR_UNSUPPORTED, "q_block"),
+    ("doc_null", fa.FA_ERR_INVALID_ARG, "q_doc"),
+])
+def test_fwd_validation(case, status, needle):
+    q, k, v, o = _t(), _t(), _t(), _t()
+    bm = None
+    mask = score = 0
+    p = None
+    if case == "null":
+        st = fa.lib().flexattn_fwd(None, None, None, None, 0, 0, None, None, None, None)
+        assert st == status and needle in fa.flexattn_last_error()
+        return
+    if case == "d64":
+        q, k, v, o = _t(D=64), _t(D=64), _t(D=64), _t(D=64)
+    if case == "gqa":
+        q, o = _t(H=3), _t(H=3)
+    if case == "dtype_mix":
+        k = _t(dtype=fa.FA_F32)
+    if case == "i8":
+        q, k, v, o = (_t(dtype=fa.FA_I8) for _ in range(4))
+    if case == "prefix_causal":
+        mask = fa.FA_MASK_PREFIX_LM | fa.FA_MASK_CAUSAL
+        p = FaParams(0.0, 0, 4, 0.0, None, None, None)
+    if case == "no_bm":
+        mask = fa.FA_MASK_CAUSAL
+    if case == "misaligned":
+        q = _t(data=258)
+    if case == "stride":
+        q = FaTensor(256, fa.FA_BF16, 1, 2, 100, 128, 2 * 100 * 128, 100 * 130 + 4, 130, None)
+    if case == "window0":
+        mask = fa.FA_MASK_WINDOW
+        bm = FaBlockMask(1, 1, 100, 100, 128, 128, 1, 1, 64, 64, 64, 64)
+    if case == "softcap0":
+        score = fa.FA_SCORE_SOFTCAP
+    if case == "alibi_null":
+        score = fa.FA_SCORE_ALIBI
+    if case == "bm_len":
+        mask = fa.FA_MASK_CAUSAL
+        bm = FaBlockMask(1, 1, 90, 100, 128, 128, 1, 1, 64, 64, 64, 64)
+    if case == "bm_qblock":
+        mask = fa.FA_MASK_CAUSAL
+        bm = FaBlockMask(1, 1, 100, 100, 64, 128, 2, 1, 64, 64, 64, 64)
+    if case == "doc_null":
+        mask = fa.FA_MASK_DOC
+    st = _fwd(q, k, v, o, bm, mask, score, p)
+    assert st == status, (st, fa.flexattn_last_error())
+    assert needle in fa.flexattn_last_error(), fa.flexattn_last_error()
+
+
+def test_block_mask_build_validation():
+    lib = fa.lib()
+    p = FaParams(0.0, 0, 0, 0.0, None, None, None)
+    bm = FaBlockMask(1, 1, 100, 100, 128, 128, 1, 1, 64, 64, 64, 64)
+    st = lib.flexattn_block_mask_build(fa.FA_MASK_CAUSAL, ctypes.byref(p), 1, 100, 120, ctypes.byref(bm), None, 0, None)
+    assert st == fa.FA_ERR_INVALID_ARG and "kv_len" in fa.flexattn_last_error()
+    bm2 = FaBlockMask(1, 1, 100, 100, 32, 128, 4, 1, 64, 64, 64, 64)
+    st = lib.flexattn_block_mask_build(fa.FA_MASK_CAUSAL, ctypes.byref(p), 1, 100, 100, ctypes.byref(bm2), None, 0, None)
+    assert st == fa.FA_ERR_UNSUPPORTED
+    bm3 = FaBlockMask(1, 1, 100, 100, 128, 128, 1, 1, 64, 64, 64, 64)
+    pd = FaParams(0.0, 0, 0, 0.0, None, 64, 64)
+    st = lib.flexattn_block_mask_build(fa.FA_MASK_DOC, ctypes.byref(pd), 2, 100, 100, ctypes.byref(bm3), None, 0, None)
+    assert st == fa.FA_ERR_INVALID_ARG and "Bm" in fa.flexattn_last_error()
+    bm4 = FaBlockMask(2, 1, 100, 100, 128, 128, 1, 1, 64, 64, 64, 64)
+    st = lib.flexattn_block_mask_build(fa.FA_MASK_DOC, ctypes.byref(pd), 2, 100, 100, ctypes.byref(bm4), None, 0, None)
+    assert st == fa.FA_ERR_INVALID_ARG and "workspace" in fa.flexattn_last_error()
+    st = lib.flexattn_block_mask_build(fa.FA_MASK_WINDOW, ctypes.byref(p), 1, 100, 100, ctypes.byref(bm), None, 0, None)
+    assert st == fa.FA_ERR_INVALID_ARG and "window" in fa.flexattn_last_error()
+    st = lib.flexattn_block_mask_build(64, ctypes.byref(p), 1, 100, 100, ctypes.byref(bm), None, 0, None)
+    assert st == fa.FA_ERR_INVALID_ARG and "unknown" in fa.flexattn_last_error()
+
+
+def test_product_path_does_not_import_oracle():
+    pkg = os.path.join(ROOT, "block_sparse_masked_blockmask_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.replace("oracles", ""), f
