@@ -1,0 +1,263 @@
+"""Benchmark of the block-sparse masked attention forward on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+One step is one pass of the whole hot path over one batch of synthetic input already
+resident in HBM: the BlockMask build followed by the forward pass. The default workload is
+grouped variate attention at scale (4096 packed groups with sizes uniform in [2, 64],
+H=4, head dim 128, bf16, document-id mask). Prints ONE JSON line.
+
+Metric: effective TFLOP/s counted on unmasked FLOPs (4 * D per allowed (query, key) pair per
+query head: Q.K^T and P.V), plus algorithmic HBM GB/s (Q, K, V, document ids and the
+BlockMask lists read once; O and LSE written once). The roofline entry is for the forward
+kernel alone, timed with HIP events on the stream it is launched on.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "block-sparse attn fwd effective TFLOP/s (unmasked FLOPs) + HBM GB/s, 1 GPU"
+DEFAULT_WORKLOAD = "grouped_variate_4096g_bf16"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2516.6
+FP32_PEAK_TFLOPS = 157.3
+CPU_SAMPLE_BLOCKS = 6   # query blocks (x all heads) of the oracle timed on the host
+KERNEL_SOURCES = ["block_sparse_masked_blockmask_amd/csrc/fwd.hip",
+                  "block_sparse_masked_blockmask_amd/csrc/device_common.h"]
+
+
+def allowed_pairs(w) -> int:
+    """Exact number of allowed (query, key) pairs per query head, from the mask structure."""
+    total = 0
+    for b in range(w.B):
+        if w.doc and not w.causal and w.window is None and w.prefix_len is None:
+            qa = np.unique(w.q_doc[b], return_counts=True)
+            ka = dict(zip(*np.unique(w.kv_doc[b], return_counts=True)))
+            total += int(sum(int(c) * int(ka.get(d, 0)) for d, c in zip(*qa)))
+        elif w.doc and w.causal and w.window is None and w.prefix_len is None and w.Lq == w.Lkv \
+                and np.array_equal(w.q_doc[b], w.kv_doc[b]) and np.all(np.diff(w.q_doc[b]) >= 0):
+            _, c = np.unique(w.q_doc[b], return_counts=True)
+            total += int(sum(int(n) * (int(n) + 1) // 2 for n in c))
+        elif not w.doc and w.causal and w.prefix_len is None and w.Lq == w.Lkv:
+            i = np.arange(w.Lq, dtype=np.int64)
+            per_row = i + 1 if w.window is None else np.minimum(i + 1, w.window)
+            total += int(per_row.sum())
+        elif not (w.doc or w.causal or w.window is not None or w.prefix_len is not None):
+            total += w.Lq * w.Lkv
+        else:
+            raise NotImplementedError("pair count for this mask combination")
+    return total
+
+
+def algorithmic_bytes(w, bm) -> int:
+    el = 2 if w.dtype == "bf16" else 4
+    qkvo = (2 * w.B * w.Hq * w.Lq + 2 * w.B * w.Hkv * w.Lkv) * w.D * el
+    lse = w.B * w.Hq * w.Lq * 4
+    docs = (w.B * (w.Lq + w.Lkv) * 4) if w.doc else 0
+    lists = 0
+    if bm is not None:
+        counts = 2 * bm.kv_num_blocks.numel() * 4
+        live = int(bm.kv_num_blocks.sum().item() + bm.full_kv_num_blocks.sum().item())
+        lists = counts + live * 4
+    return qkvo + lse + docs + lists
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str, launches_per_dispatch: float = 1.0):
+    """HBM traffic per forward launch from the committed rocprofv3 counter summary, scaled by
+    the copy-kernel calibration it records; None if absent or taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"fwd_{workload}_counters.md")
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"^traffic-json: (\{.*\})\s*$", open(path).read(), re.M)
+    if not m:
+        return None
+    d = json.loads(m.group(1))
+    if d.get("source_sha") != source_hash():
+        return None
+    return int(d["hbm_bytes_per_launch"])
+
+
+def rows_allowed(w, b, rows) -> int:
+    """Allowed (query, key) pairs of the given query rows (metric bookkeeping)."""
+    i = np.asarray(rows, dtype=np.int64)[:, None]
+    j = np.arange(w.Lkv, dtype=np.int64)[None, :]
+    ok = np.ones((i.shape[0], w.Lkv), dtype=bool)
+    if w.doc:
+        ok &= w.q_doc[b][i] == w.kv_doc[b][j]
+    if w.causal:
+        ok &= i >= j
+    if w.window is not None:
+        ok &= (i - j) < w.window
+    if w.prefix_len is not None:
+        ok &= (j < w.prefix_len) | (i >= j)
+    return int(ok.sum())
+
+
+def cpu_baseline(w, spec):
+    """The oracle as it stands on the host cores, on a bounded sample of query rows."""
+    from oracle import attention as ref_attn
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    qf, kf, vf = w.qkv_f32()
+    rng = np.random.default_rng(0)
+    nqb = -(-w.Lq // 128)
+    blocks = sorted(rng.choice(nqb, size=min(CPU_SAMPLE_BLOCKS, nqb), replace=False).tolist())
+    n_pairs = 0
+    t0 = time.perf_counter()
+    n_rows = 0
+    for hq in range(w.Hq):
+        b = hq % w.B
+        for qb in blocks:
+            rows = np.arange(qb * 128, min(w.Lq, qb * 128 + 128))
+            ref_attn.attention_rows(qf, kf, vf, spec, b, hq, rows)
+            n_rows += len(rows)
+            n_pairs += rows_allowed(w, b, rows)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * w.D * n_pairs
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{n_rows} query rows ({len(blocks)} query blocks x {w.Hq} heads), all "
+                      f"{w.Lkv} keys each, numpy fp64 dense rows; {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--kv-block", type=int, default=128)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device copy (HBM counter calibration for rocprofv3)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark measures one GPU; multi-GPU runs are not part of "
+                                   "this build (the path shards by heads or groups with no exchange)"}))
+        sys.exit(2)
+
+    import torch
+    dev = torch.device("cuda", 0)
+    if args.copy_calibration:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n}))
+        return
+
+    import block_sparse_masked_blockmask_amd as fa
+    from workloads import make_workload
+
+    t_gen = time.perf_counter()
+    w = make_workload(args.workload)
+    mk = (fa.FA_MASK_DOC if w.doc else 0) | (fa.FA_MASK_CAUSAL if w.causal else 0) \
+        | (fa.FA_MASK_WINDOW if w.window is not None else 0) | (fa.FA_MASK_PREFIX_LM if w.prefix_len is not None else 0)
+    sk = (fa.FA_SCORE_ALIBI if w.alibi_slopes is not None else 0) | (fa.FA_SCORE_SOFTCAP if w.softcap else 0)
+
+    def dev_tensor(x):
+        if w.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    q, k, v = dev_tensor(w.q), dev_tensor(w.k), dev_tensor(w.v)
+    qd = torch.from_numpy(w.q_doc).to(dev) if w.doc else None
+    kd = torch.from_numpy(w.kv_doc).to(dev) if w.doc else None
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    bm = fa.BlockMask(w.B if w.doc else 1, 1, w.Lq, w.Lkv, 128, args.kv_block, dev)
+    ws_bytes = fa.flexattn_block_mask_workspace_bytes(mk, w.B, w.Lq, w.Lkv, 128, args.kv_block)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    gen_s = time.perf_counter() - t_gen
+
+    def step(ev=None):
+        fa.flexattn_block_mask_build(mk, w.B, w.Lq, w.Lkv, 128, args.kv_block, q_doc=qd, kv_doc=kd,
+                                     window=w.window or 0, prefix_len=w.prefix_len or 0, out=bm,
+                                     workspace=ws, stream=stream)
+        if ev is not None:
+            ev[0].record(stream)
+        fa.flexattn_fwd(q, k, v, bm, mk, sk, window=w.window or 0, prefix_len=w.prefix_len or 0,
+                        softcap=w.softcap or 0.0, q_doc=qd, kv_doc=kd, out=out, lse=lse, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms = [a.elapsed_time(b) for a, b in events]
+    fwd_avg_ms = float(np.mean(fwd_ms))
+    ms_per_step = wall * 1e3 / args.steps
+
+    pairs = allowed_pairs(w)
+    flops = 4.0 * w.D * pairs * w.Hq
+    abytes = algorithmic_bytes(w, bm)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    fwd_tflops = flops / (fwd_avg_ms * 1e-3) / 1e12
+    fwd_gbs = abytes / (fwd_avg_ms * 1e-3) / 1e9
+    hbm_bound = (flops / abytes) < (BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9))
+    traffic = read_traffic(args.workload)
+    if w.dtype == "f32":
+        roof = {"bound": "mfma", "achieved": fwd_tflops, "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s"}
+    elif hbm_bound:
+        roof = {"bound": "hbm", "achieved": fwd_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": fwd_tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = traffic
+    roof["kernel"] = "fwd_bf16_kernel" if w.dtype == "bf16" else "fwd_f32_kernel"
+    roof["algorithmic_bytes"] = abytes
+    roof["unmasked_flops"] = flops
+    roof["avg_launch_ms"] = fwd_avg_ms
+
+    rec = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded numpy PCG64)",
+        "config": {"workload": args.workload, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Lq": w.Lq, "Lkv": w.Lkv,
+                   "D": w.D, "mask": mk, "score": sk, "q_block": 128, "kv_block": args.kv_block,
+                   "step": "block_mask_build + fwd"},
+        "hbm_gbs": abytes / (ms_per_step * 1e-3) / 1e9,
+        "fwd_only": {"ms": fwd_avg_ms, "tflops": fwd_tflops, "gbs": fwd_gbs},
+        "roofline": roof,
+        "input_gen_s": gen_s,
+    }
+    if not args.no_cpu_baseline:
+        spec = dict(doc=w.doc, causal=w.causal, window=w.window, prefix_len=w.prefix_len, q_doc=w.q_doc,
+                    kv_doc=w.kv_doc, alibi_slopes=w.alibi_slopes, softcap=w.softcap)
+        rec["cpu_baseline"] = cpu_baseline(w, spec)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()
