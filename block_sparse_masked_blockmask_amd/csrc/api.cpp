@@ -132,6 +132,7 @@ static fa_status check_tensor(const fa_tensor* t, const char* name, int elem_ali
   if (!aligned16(t->data)) return fail(FA_ERR_INVALID_ARG, "%s->data must be 16-byte aligned", name);
   if (t->stride_b < 0 || t->stride_h < 0 || t->stride_l < t->D)
     return fail(FA_ERR_INVALID_ARG, "%s strides must be non-negative with stride_l >= D", name);
+  if (t->stride_l > (1 << 24)) return fail(FA_ERR_UNSUPPORTED, "%s->stride_l above 2^24 elements", name);
   if (t->stride_b % elem_align || t->stride_h % elem_align || t->stride_l % elem_align)
     return fail(FA_ERR_INVALID_ARG, "%s strides must be multiples of %d elements", name, elem_align);
   if (t->scale != nullptr) return fail(FA_ERR_INVALID_ARG, "%s->scale must be NULL for this dtype", name);

@@ -19,6 +19,8 @@
 // head-dim channel.
 #include <hip/hip_runtime.h>
 
+#include <climits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -94,184 +96,424 @@ __device__ __forceinline__ float score_log2(const FwdArgs& a, float acc, int qi,
 
 // ---------------------------------------------------------------------------------------------
 // bf16 kernel
+//
+// Keys are processed in steps of 64 (a 128-key BlockMask tile is two steps). K and V rows of a
+// step live in LDS (16 KB each, swizzled 16-byte chunks) in two buffers: while one step is
+// computed, the next step's K, V (and document ids) stream into the other buffer with
+// global_load_lds_dwordx4, which writes LDS directly without passing through registers. The two
+// buffers are distinct LDS objects selected at compile time (the step loop is unrolled by two):
+// the compiler then knows that reads of one buffer do not depend on the transfers into the
+// other and does not wait for them. BlockMask list entries are fetched two steps ahead.
+// At 64 KB of LDS and <= 256 VGPRs, two workgroups share a CU.
+//
+// Mask evaluation (partial tiles only). Causal, window and prefix-LM together allow, for a
+// query i, exactly one key interval [lo, hi): causal gives hi = i + 1, prefix-LM gives
+// hi = max(prefix_len, i + 1), window gives lo = i - window + 1, and the key count bounds hi.
+// Each score therefore needs one unsigned compare, plus one document-id compare under DOC.
+// Before any product, each wave drops the 32x32 (query x key) sub-blocks that its mask makes
+// entirely empty: their probabilities are exactly 0, so skipping both products changes nothing.
+//
+// Online softmax with a lazily updated maximum: the running maximum m (log2 units) is raised
+// only when a row's new maximum exceeds it by more than kRescaleSlack, so most steps skip the
+// O and l rescale. Probabilities exp2(t - m) then stay below 2^kRescaleSlack, far from fp32 and
+// bf16 limits, and out = O / l and lse = (m + log2 l) ln 2 are unchanged whichever m is used.
 // ---------------------------------------------------------------------------------------------
-template <int BK, int SCORE>
-__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
-  constexpr int NB = BK / 32;               // 32-key sub-blocks per tile
-  constexpr int CHUNKS = BK * 16 / 256;     // 16-byte chunks per thread per K (or V) tile
-  __shared__ __attribute__((aligned(16))) unsigned char sK[BK * 256];
-  __shared__ __attribute__((aligned(16))) unsigned char sV[BK * 256];
-  __shared__ int sDoc[BK];
+namespace {
 
-  const WorkItem it = decode_work(a);
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int hl = lane >> 5, lq = lane & 31;
-  const int qi = it.qb * kBQ + wave * 32 + lq;
-  const bool q_in = qi < a.Lq;
+constexpr int kStep = 64;
+constexpr int kStepBytes = kStep * 256;
+constexpr float kRescaleSlack = 8.0f;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-  const __bf16* qp = (const __bf16*)a.q + it.b * a.q_sb + it.hq * a.q_sh;
-  const __bf16* kp = (const __bf16*)a.k + it.b * a.k_sb + it.hkv * a.k_sh;
-  const __bf16* vp = (const __bf16*)a.v + it.b * a.v_sb + it.hkv * a.v_sh;
+__shared__ __attribute__((aligned(1024))) unsigned char g_k0[kStepBytes];
+__shared__ __attribute__((aligned(1024))) unsigned char g_v0[kStepBytes];
+__shared__ __attribute__((aligned(1024))) unsigned char g_k1[kStepBytes];
+__shared__ __attribute__((aligned(1024))) unsigned char g_v1[kStepBytes];
+__shared__ __attribute__((aligned(16))) int g_d0[kStep];
+__shared__ __attribute__((aligned(16))) int g_d1[kStep];
 
-  // Q^T as the B operand: lane holds Q[qi][16*ks + 8*hl .. +8] for ks = 0..7.
-  bf16x8 qreg[8];
+template <int B> __device__ __forceinline__ unsigned char* kbuf() { return B ? g_k1 : g_k0; }
+template <int B> __device__ __forceinline__ unsigned char* vbuf() { return B ? g_v1 : g_v0; }
+template <int B> __device__ __forceinline__ int* dbuf() { return B ? g_d1 : g_d0; }
+
+__device__ __forceinline__ void dma16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 4, 0, 0);
+}
+// The compiler does not track the LDS writes of global_load_lds; wait for them explicitly.
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ int wave_min32(int x) {
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    if (q_in) {
-      qreg[ks] = *(const bf16x8*)(qp + (int64_t)qi * a.q_sl + ks * 16 + hl * 8);
-    } else {
-      qreg[ks] = bf16x8{};
+  for (int o = 16; o > 0; o >>= 1) x = min(x, __shfl_xor(x, o, 64));
+  return __builtin_amdgcn_readfirstlane(x);
+}
+__device__ __forceinline__ int wave_max32(int x) {
+#pragma unroll
+  for (int o = 16; o > 0; o >>= 1) x = max(x, __shfl_xor(x, o, 64));
+  return __builtin_amdgcn_readfirstlane(x);
+}
+
+struct StepInfo {
+  int kv0;
+  bool ok, masked;
+};
+
+// Per-lane constants of one workgroup.
+struct Ctx {
+  int wave, lane, hl, lq, g16, s16;
+  int qw0, qw1, qi;
+  bool q_in, doc;
+  int qdoc, qd_min, qd_max;
+  int lo, hi;            // allowed key interval of this lane's query (index predicates + bounds)
+  float slope;
+  const __bf16* kp;
+  const __bf16* vp;
+  const int* kvdoc;
+  int koff, voff;        // element offset of this lane's 16-byte DMA chunk in segment 0 of a step
+  // Byte offsets within a K or V step buffer of this lane's operand reads (swizzle applied):
+  // kx[ks] for the K operand of k-step ks (row lq), vx[2*db + j] for the transposed V reads of
+  // channel block db at rows base (j = 0) and base + 8 (j = 1). Other rows add 256 * rows.
+  int kx[8], vx[8];
+};
+
+struct State {
+  f32x16 oacc[4];
+  float m_run, l_run;
+};
+
+// Rows past the end are clamped to the last key: they hold finite data and are masked.
+template <int B>
+__device__ __forceinline__ void issue_step(const FwdArgs& a, const Ctx& c, const StepInfo& si) {
+  const __bf16* kb = c.kp + (int64_t)si.kv0 * a.k_sl;
+  const __bf16* vb = c.vp + (int64_t)si.kv0 * a.v_sl;
+  if (si.kv0 + kStep <= a.Lkv) {
+    // Segment i*4 + wave holds rows 16*i + 4*wave + lane/16; the chunk swizzle depends on the
+    // row modulo 16 only, so segments differ by a whole number of 16-row strides.
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int seg = i * 4 + c.wave;  // 1 KB segment = 4 rows; lane writes 16 bytes at lane * 16
+      dma16(kb + (int64_t)(16 * i) * a.k_sl + c.koff, kbuf<B>() + seg * 1024);
+      dma16(vb + (int64_t)(16 * i) * a.v_sl + c.voff, vbuf<B>() + seg * 1024);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int seg = i * 4 + c.wave;
+      const int r = seg * 4 + (c.lane >> 4);
+      const int ch = (c.lane & 15) ^ swz(r);
+      const int64_t kv = min(si.kv0 + r, a.Lkv - 1);
+      dma16(c.kp + kv * a.k_sl + ch * 8, kbuf<B>() + seg * 1024);
+      dma16(c.vp + kv * a.v_sl + ch * 8, vbuf<B>() + seg * 1024);
     }
   }
-  const int qdoc = ((a.flags & FA_MASK_DOC) && q_in) ? a.q_doc[(int64_t)it.b * a.Lq + qi] : 0;
-  const float slope = (SCORE & FA_SCORE_ALIBI) ? a.slopes[it.hq] : 0.f;
-  const MaskSpec ms{a.flags, a.window, a.prefix_len};
+  if (c.doc && si.masked && c.wave == 0) dma4(c.kvdoc + min(si.kv0 + c.lane, a.Lkv - 1), dbuf<B>());
+}
 
-  f32x16 oacc[4];
+template <int B, int SCORE, bool MASKED>
+__device__ __forceinline__ void compute_step(const FwdArgs& a, const Ctx& c, const bf16x8 (&qreg)[8], State& st,
+                                             const int kv0) {
+  const unsigned char* sK = kbuf<B>();
+  const unsigned char* sV = vbuf<B>();
+  const int* sD = dbuf<B>();
+  // The offsets are re-defined here (no instruction is emitted) so that the compiler forms
+  // buffer + offset inside the loop, where the buffer address folds into the instruction's
+  // immediate offset, instead of keeping one hoisted register per buffer and offset.
+  int kx[8], vx[8];
 #pragma unroll
-  for (int db = 0; db < 4; ++db) oacc[db] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int i = 0; i < 8; ++i) {
+    kx[i] = c.kx[i];
+    vx[i] = c.vx[i];
+    asm volatile("" : "+v"(kx[i]), "+v"(vx[i]));
+  }
 
-  const TileList tl = tile_list(a, it);
-  const int ntiles = tl.nfull + tl.npart;
-
-  const int g16 = lane >> 4, s16 = lane & 15;  // 16-lane group and index for transposed reads
-
-  for (int t = 0; t < ntiles; ++t) {
-    const bool partial = t >= tl.nfull;
-    const int kb = partial ? tl.part[t - tl.nfull] : (a.all_full ? t : tl.full[t]);
-    if (kb < 0 || kb >= a.nkvb) continue;  // corrupt index: skip rather than read out of range
-    const int kv0 = kb * BK;
-    const bool masked = partial || (kv0 + BK > a.Lkv);
-
-    __syncthreads();  // all waves are done reading the previous tile
-    {
-      bf16x8 kr[CHUNKS], vr[CHUNKS];
+  // Live 32-key sub-blocks for this wave (wave-uniform).
+  unsigned live = 3;
+  if constexpr (MASKED) {
+    live = 0;
 #pragma unroll
-      for (int c = 0; c < CHUNKS; ++c) {
-        const int id = tid + c * 256, r = id >> 4, ch = id & 15;
-        const int kv = kv0 + r;
-        if (kv < a.Lkv) {
-          kr[c] = *(const bf16x8*)(kp + (int64_t)kv * a.k_sl + ch * 8);
-          vr[c] = *(const bf16x8*)(vp + (int64_t)kv * a.v_sl + ch * 8);
-        } else {
-          kr[c] = bf16x8{};
-          vr[c] = bf16x8{};
-        }
+    for (int nb = 0; nb < 2; ++nb) {
+      const int k0 = kv0 + nb * 32;
+      if (k0 >= a.Lkv || c.qw0 >= a.Lq) continue;
+      const int k1 = min(k0 + 31, a.Lkv - 1);
+      bool dead = false;
+      if (a.flags & FA_MASK_CAUSAL) dead = dead || c.qw1 < k0;
+      if (a.flags & FA_MASK_WINDOW) dead = dead || c.qw0 - k1 >= a.window;
+      if (a.flags & FA_MASK_PREFIX_LM) dead = dead || (k0 >= a.prefix_len && c.qw1 < k0);
+      if (c.doc && !dead) {
+        const int d = sD[min(nb * 32 + c.lq, k1 - kv0)];
+        dead = wave_max32(d) < c.qd_min || wave_min32(d) > c.qd_max;
       }
-#pragma unroll
-      for (int c = 0; c < CHUNKS; ++c) {
-        const int id = tid + c * 256, r = id >> 4, ch = id & 15;
-        *(bf16x8*)(sK + tile_off(r, ch)) = kr[c];
-        *(bf16x8*)(sV + tile_off(r, ch)) = vr[c];
-      }
-      if (masked && (a.flags & FA_MASK_DOC) && tid < BK) {
-        const int kv = kv0 + tid;
-        sDoc[tid] = kv < a.Lkv ? a.kv_doc[(int64_t)it.b * a.Lkv + kv] : 0;
-      }
+      if (!dead) live |= 1u << nb;
     }
-    __syncthreads();
+    live = __builtin_amdgcn_readfirstlane(live);
+    if (!live) return;
+  }
 
-    // S^T = K Q^T for NB sub-blocks of 32 keys.
-    f32x16 sacc[NB];
+  // S^T = K Q^T for the live 32-key sub-blocks.
+  f32x16 sacc[2];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      sacc[nb] = f32x16{};
-      const int r = nb * 32 + lq;
+  for (int nb = 0; nb < 2; ++nb) {
+    if (MASKED && !(live & (1u << nb))) continue;
+    sacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(sK + nb * 32 * 256 + kx[0]), qreg[0],
+                                                       f32x16{}, 0, 0, 0);
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8 kf = *(const bf16x8*)(sK + tile_off(r, 2 * ks + hl));
-        sacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[ks], sacc[nb], 0, 0, 0);
-      }
+    for (int ks = 1; ks < 8; ++ks) {
+      const bf16x8 kf = *(const bf16x8*)(sK + nb * 32 * 256 + kx[ks]);
+      sacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[ks], sacc[nb], 0, 0, 0);
     }
+    // Schedule: 4 operand reads ahead, then one read per product (bounds live operands).
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (k < 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  }
 
-    // Scores in the log2 domain, mask on partial (and ragged) tiles, running max.
-    float mx = -INFINITY;
+  // Scores (log2 domain) and the mask. Without a score_mod the 1/sqrt(d) * log2(e) scale is
+  // folded into the exponent below, and the maximum is taken on the raw products.
+  float mx = -INFINITY;
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
+  for (int nb = 0; nb < 2; ++nb) {
+    if (MASKED && !(live & (1u << nb))) continue;
+    const int kbase = kv0 + nb * 32 + c.hl * 4;   // key of element i is kbase + (i/4)*8 + i%4
+    // kbase - lo, kept opaque so that the compiler does not hoist one loop-invariant register
+    // per element out of the step loop (it would otherwise spill).
+    int rel = kbase - c.lo;
+    asm volatile("" : "+v"(rel));
+    const unsigned span = (unsigned)(c.hi - c.lo);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int kv = kv0 + nb * 32 + (i >> 2) * 8 + hl * 4 + (i & 3);
-        float x = score_log2<SCORE>(a, sacc[nb][i], qi, kv, slope);
-        if (masked) {
-          const int kvdoc = (a.flags & FA_MASK_DOC) ? sDoc[kv - kv0] : 0;
-          const bool keep = kv < a.Lkv && mask_pair(ms, qi, kv, qdoc, kvdoc);
+    for (int g = 0; g < 4; ++g) {
+      i32x4 kd4 = i32x4{};
+      if constexpr (MASKED) {
+        if (c.doc) kd4 = *(const i32x4*)(sD + (kbase - kv0) + g * 8);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = g * 4 + e;
+        const int kv = kbase + g * 8 + e;
+        float x = SCORE == 0 ? sacc[nb][i] : score_log2<SCORE>(a, sacc[nb][i], c.qi, kv, c.slope);
+        if constexpr (MASKED) {
+          bool keep = (unsigned)(rel + g * 8 + e) < span;
+          if (c.doc) keep = keep && kd4[e] == c.qdoc;
           x = keep ? x : -INFINITY;
         }
         sacc[nb][i] = x;
         mx = fmaxf(mx, x);
       }
     }
-    mx = half_swap_max(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    m_run = m_new;
+  }
+  mx = half_swap_max(mx);
+  const float scale = SCORE == 0 ? a.scale_log2 : 1.0f;
+  const float m_cand = fmaxf(st.m_run, mx * scale);
+  const bool raise = m_cand > st.m_run + kRescaleSlack;
+  if (__builtin_amdgcn_readfirstlane(__ballot(raise) != 0)) {
+    // Rows that keep m (including rows still at -inf) must get alpha = 1 exactly; a raised row
+    // coming from -inf gets exp2(-inf) = 0.
+    const float m_new = raise ? m_cand : st.m_run;
+    const float alpha = raise ? fast_exp2(st.m_run - m_new) : 1.0f;
+    st.l_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) st.oacc[db] *= alpha;
+    st.m_run = m_new;
+  }
+  const float m_eff = st.m_run == -INFINITY ? 0.f : st.m_run;  // rows with no allowed key so far
 
-    // P = exp2(t - m); P^T goes straight into the B operand of O^T = V^T P^T as bf16.
-    float rs = 0.f;
-    bf16x8 pb[NB][2];
+  // P = exp2(t - m); P^T goes straight into the B operand of O^T = V^T P^T as bf16.
+  bf16x8 pb[2][2];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
+  for (int nb = 0; nb < 2; ++nb) {
+    if (MASKED && !(live & (1u << nb))) continue;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = fast_exp2(sacc[nb][i] - m_use);
-        rs += p;
-        pb[nb][i >> 3][i & 7] = (__bf16)p;
+    for (int i = 0; i < 16; ++i) {
+      const float p = fast_exp2(fmaf(sacc[nb][i], scale, -m_eff));
+      st.l_run += p;
+      pb[nb][i >> 3][i & 7] = (__bf16)p;
+    }
+  }
+
+  // O^T += V^T P^T. A operand (V^T: row = channel, k = key) by transposed LDS reads: in each
+  // 16-lane group, source lane s points at key row base + s/4 and channels d0 + 4*(s%4); lane i
+  // of the group then receives V[base + j][d0 + i], j = 0..3.
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      if (MASKED && !(live & (1u << nb))) continue;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int rows = (nb * 32 + h * 16) * 256;  // the swizzle depends on the row modulo 16
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sV + rows + vx[2 * db]));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sV + rows + vx[2 * db + 1]));
+        // Whole-vector concatenation and bit cast (element-wise bf16 inserts of the i16 lanes
+        // were observed to be folded into a broadcast of element 0).
+        const i16x8 cat = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        st.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, cat), pb[nb][h],
+                                                              st.oacc[db], 0, 0, 0);
       }
     }
-    l_run = l_run * alpha + rs;
+    if constexpr (!MASKED) {
+      // Schedule: 4 transposed reads ahead, then two reads per product.
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
 #pragma unroll
-    for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
-
-    // O^T += V^T P^T. A operand (V^T, row = channel d, k = key) via transposed LDS reads: in each
-    // 16-lane group, source lane s points at row (key) base + s/4, channels d0 + 4*(s%4); lane i
-    // of the group then receives V[base + j][d0 + i] for j = 0..3.
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      const int d = db * 32 + 16 * (g16 & 1) + 4 * (s16 & 3);
-      const int ch = d >> 3, boff = (d & 7) * 2;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int r0 = nb * 32 + h * 16 + (g16 >> 1) * 4 + (s16 >> 2);
-          const int r1 = r0 + 8;
-          typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_i16x4*)(sV + tile_off(r0, ch) + boff));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_i16x4*)(sV + tile_off(r1, ch) + boff));
-          // Whole-vector concatenation and bit cast (element-wise bf16 inserts of the i16
-          // lanes were observed to be folded into a broadcast of element 0).
-          const i16x8 cat = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          const bf16x8 vf = __builtin_bit_cast(bf16x8, cat);
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[nb][h], oacc[db], 0, 0, 0);
-        }
+      for (int k = 0; k < 4; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        if (k < 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
       }
+    }
+  }
+}
+
+template <int B, int SCORE>
+__device__ __forceinline__ void run_step(const FwdArgs& a, const Ctx& c, const bf16x8 (&qreg)[8], State& st,
+                                         const StepInfo& cur) {
+  if (!cur.ok) return;
+  if (cur.masked) {
+    compute_step<B, SCORE, true>(a, c, qreg, st, cur.kv0);
+  } else {
+    compute_step<B, SCORE, false>(a, c, qreg, st, cur.kv0);
+  }
+}
+
+}  // namespace
+
+template <int TB, int SCORE>
+__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
+  constexpr int HALVES = TB / kStep;  // steps per BlockMask tile
+
+  const WorkItem it = decode_work(a);
+  Ctx c;
+  c.wave = threadIdx.x >> 6;
+  c.lane = threadIdx.x & 63;
+  c.hl = c.lane >> 5;
+  c.lq = c.lane & 31;
+  c.g16 = c.lane >> 4;
+  c.s16 = c.lane & 15;
+  c.qw0 = it.qb * kBQ + c.wave * 32;
+  c.qw1 = min(c.qw0 + 31, a.Lq - 1);
+  c.qi = c.qw0 + c.lq;
+  c.q_in = c.qi < a.Lq;
+  c.doc = (a.flags & FA_MASK_DOC) != 0;
+  c.kp = (const __bf16*)a.k + it.b * a.k_sb + it.hkv * a.k_sh;
+  c.vp = (const __bf16*)a.v + it.b * a.v_sb + it.hkv * a.v_sh;
+  c.kvdoc = c.doc ? a.kv_doc + (int64_t)it.b * a.Lkv : nullptr;
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) c.kx[ks] = tile_off(c.lq, 2 * ks + c.hl);
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    // In each 16-lane group, source lane s points at key row base + s/4, channels d0 + 4*(s%4).
+    const int d = db * 32 + 16 * (c.g16 & 1) + 4 * (c.s16 & 3);
+    const int r0 = (c.g16 >> 1) * 4 + (c.s16 >> 2);
+    c.vx[2 * db] = tile_off(r0, d >> 3) + (d & 7) * 2;
+    c.vx[2 * db + 1] = tile_off(r0 + 8, d >> 3) + (d & 7) * 2;
+  }
+  {
+    const int r = c.wave * 4 + (c.lane >> 4);  // row of this lane in segment 0 (of wave)
+    const int ch = (c.lane & 15) ^ swz(r);
+    c.koff = r * (int)a.k_sl + ch * 8;
+    c.voff = r * (int)a.v_sl + ch * 8;
+  }
+  {
+    int lo = INT_MIN / 2, hi = a.Lkv;
+    if (a.flags & FA_MASK_CAUSAL) hi = min(hi, c.qi + 1);
+    if (a.flags & FA_MASK_PREFIX_LM) hi = min(hi, max(a.prefix_len, c.qi + 1));
+    if (a.flags & FA_MASK_WINDOW) lo = c.qi - a.window + 1;
+    c.lo = lo;
+    c.hi = max(hi, lo);
+  }
+
+  const TileList tl = tile_list(a, it);
+  const int nsteps = (tl.nfull + tl.npart) * HALVES;
+  // List entry of the tile of step s (one load, the same address in every lane).
+  auto entry = [&](int s) -> int {
+    const int t = s / HALVES;
+    if (a.all_full) return t;
+    return t < tl.nfull ? tl.full[t] : tl.part[t - tl.nfull];
+  };
+  auto info = [&](int s, int kb) {
+    StepInfo si;
+    si.kv0 = kb * TB + (s % HALVES) * kStep;
+    // A corrupt index is skipped rather than read out of range; so is a half past the end.
+    si.ok = kb >= 0 && kb < a.nkvb && si.kv0 < a.Lkv;
+    si.masked = (s / HALVES >= tl.nfull) || (si.kv0 + kStep > a.Lkv);
+    return si;
+  };
+
+  StepInfo cur{0, false, false};
+  if (nsteps > 0) {
+    cur = info(0, __builtin_amdgcn_readfirstlane(entry(0)));
+    if (cur.ok) issue_step<0>(a, c, cur);
+  }
+  int e_next = nsteps > 1 ? entry(1) : 0;  // in flight until the first wait
+
+  // Q^T as the B operand: lane holds Q[qi][16*ks + 8*hl .. +8] for ks = 0..7.
+  const __bf16* qp = (const __bf16*)a.q + it.b * a.q_sb + it.hq * a.q_sh;
+  bf16x8 qreg[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks)
+    qreg[ks] = c.q_in ? *(const bf16x8*)(qp + (int64_t)c.qi * a.q_sl + ks * 16 + c.hl * 8) : bf16x8{};
+  c.qdoc = (c.doc && c.q_in) ? a.q_doc[(int64_t)it.b * a.Lq + c.qi] : 0;
+  c.qd_min = c.qd_max = 0;
+  if (c.doc) {
+    c.qd_min = wave_min32(c.q_in ? c.qdoc : INT_MAX);
+    c.qd_max = wave_max32(c.q_in ? c.qdoc : INT_MIN);
+  }
+  c.slope = (SCORE & FA_SCORE_ALIBI) ? a.slopes[it.hq] : 0.f;
+
+  State st;
+#pragma unroll
+  for (int db = 0; db < 4; ++db) st.oacc[db] = f32x16{};
+  st.m_run = -INFINITY;
+  st.l_run = 0.f;
+
+  // Two steps per iteration: even steps compute from buffer 0, odd steps from buffer 1.
+  for (int s = 0; s < nsteps; s += 2) {
+    {
+      wait_vmem();      // this wave's transfers for step s (and entry e_next) have landed
+      __syncthreads();  // all transfers landed; buffer 1 (step s-1) is no longer read
+      StepInfo nxt{0, false, false};
+      if (s + 1 < nsteps) nxt = info(s + 1, __builtin_amdgcn_readfirstlane(e_next));
+      if (nxt.ok) issue_step<1>(a, c, nxt);
+      if (s + 2 < nsteps) e_next = entry(s + 2);
+      run_step<0, SCORE>(a, c, qreg, st, cur);
+      cur = nxt;
+    }
+    if (s + 1 < nsteps) {
+      wait_vmem();
+      __syncthreads();
+      StepInfo nxt{0, false, false};
+      if (s + 2 < nsteps) nxt = info(s + 2, __builtin_amdgcn_readfirstlane(e_next));
+      if (nxt.ok) issue_step<0>(a, c, nxt);
+      if (s + 3 < nsteps) e_next = entry(s + 3);
+      run_step<1, SCORE>(a, c, qreg, st, cur);
+      cur = nxt;
     }
   }
 
   // Epilogue: combine the two halves' row sums, normalise, store O (bf16) and the natural-log lse.
-  const float l_tot = half_swap_sum(l_run);
+  const float l_tot = half_swap_sum(st.l_run);
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-  if (q_in) {
-    __bf16* op = (__bf16*)a.o + it.b * a.o_sb + it.hq * a.o_sh + (int64_t)qi * a.o_sl;
+  if (c.q_in) {
+    __bf16* op = (__bf16*)a.o + it.b * a.o_sb + it.hq * a.o_sh + (int64_t)c.qi * a.o_sl;
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
         bf16x4 o4;
-        o4[0] = (__bf16)(oacc[db][gq * 4 + 0] * inv);
-        o4[1] = (__bf16)(oacc[db][gq * 4 + 1] * inv);
-        o4[2] = (__bf16)(oacc[db][gq * 4 + 2] * inv);
-        o4[3] = (__bf16)(oacc[db][gq * 4 + 3] * inv);
-        *(bf16x4*)(op + db * 32 + gq * 8 + hl * 4) = o4;
+        o4[0] = (__bf16)(st.oacc[db][gq * 4 + 0] * inv);
+        o4[1] = (__bf16)(st.oacc[db][gq * 4 + 1] * inv);
+        o4[2] = (__bf16)(st.oacc[db][gq * 4 + 2] * inv);
+        o4[3] = (__bf16)(st.oacc[db][gq * 4 + 3] * inv);
+        *(bf16x4*)(op + db * 32 + gq * 8 + c.hl * 4) = o4;
       }
     }
-    if (a.lse && hl == 0) {
-      a.lse[((int64_t)it.b * a.Hq + it.hq) * a.Lq + qi] =
-          l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+    if (a.lse && c.hl == 0) {
+      a.lse[((int64_t)it.b * a.Hq + it.hq) * a.Lq + c.qi] =
+          l_tot > 0.f ? (st.m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
     }
   }
 }
