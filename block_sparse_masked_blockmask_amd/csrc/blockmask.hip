@@ -6,11 +6,13 @@
 // is classified by one workgroup:
 //   1. closed forms decide most tiles exactly: the index predicates (causal, window, prefix-LM)
 //      are monotone in q - kv or kv, so their all-true / all-false conditions are corner tests;
-//      document ids use per-block [min, max] ranges (equal single ids: full; disjoint: empty);
+//      document ids use per-block summaries: [min, max] (equal single ids: full; disjoint:
+//      empty) and a "dense" flag (consecutive ids differ by 0 or 1, so every id in [min, max]
+//      occurs in the block; two dense blocks with overlapping ranges then share an id);
 //   2. tiles that the closed forms cannot settle are evaluated pair by pair by the whole
 //      workgroup (exact for any ids, sorted or not);
-//   3. a block-wide ballot scan writes the full and partial lists in ascending kv order and
-//      zero-fills their tails.
+//   3. each thread owns a run of consecutive kv blocks; one block-wide scan of the per-thread
+//      counts writes the full and partial lists in ascending order; their tails are zeroed.
 #include <hip/hip_runtime.h>
 
 #include "device_common.h"
@@ -18,41 +20,70 @@
 
 namespace fa {
 
+namespace {
+
+constexpr int kPerThread = 8;                 // kv blocks owned by one thread per chunk
+constexpr int kChunk = 256 * kPerThread;      // kv blocks classified per pass of a workgroup
+
+__device__ __forceinline__ int wave_reduce_min(int x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = min(x, __shfl_xor(x, o, 64));
+  return x;
+}
+__device__ __forceinline__ int wave_reduce_max(int x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = max(x, __shfl_xor(x, o, 64));
+  return x;
+}
+
+}  // namespace
+
+// One wave per (batch, block) of either side: [min id, max id, dense flag].
 __global__ __launch_bounds__(256) void bm_summaries(BlockMaskArgs a) {
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  const int w = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int nq = a.B * a.nqb, nk = a.B * a.nkvb;
+  if (w >= nq + nk) return;
   const int* ids;
   int lo, hi;
   int* dst;
-  if (t < nq) {
-    const int b = t / a.nqb, blk = t % a.nqb;
+  if (w < nq) {
+    const int b = w / a.nqb, blk = w % a.nqb;
     ids = a.q_doc + (int64_t)b * a.Lq;
     lo = blk * a.BQ;
     hi = min(a.Lq, lo + a.BQ);
-    dst = a.qsum + 2 * t;
-  } else if (t < nq + nk) {
-    const int u = t - nq;
+    dst = a.qsum + 3 * w;
+  } else {
+    const int u = w - nq;
     const int b = u / a.nkvb, blk = u % a.nkvb;
     ids = a.kv_doc + (int64_t)b * a.Lkv;
     lo = blk * a.BK;
     hi = min(a.Lkv, lo + a.BK);
-    dst = a.kvsum + 2 * u;
-  } else {
-    return;
+    dst = a.kvsum + 3 * u;
   }
-  int mn = ids[lo], mx = ids[lo];
-  for (int i = lo + 1; i < hi; ++i) {
+  int mn = INT_MAX, mx = INT_MIN;
+  bool step_ok = true;
+  for (int i = lo + lane; i < hi; i += 64) {
     const int d = ids[i];
     mn = min(mn, d);
     mx = max(mx, d);
+    if (i > lo) {
+      const int inc = d - ids[i - 1];
+      step_ok = step_ok && (inc == 0 || inc == 1);
+    }
   }
-  dst[0] = mn;
-  dst[1] = mx;
+  mn = wave_reduce_min(mn);
+  mx = wave_reduce_max(mx);
+  const bool dense = __ballot(!step_ok) == 0;
+  if (lane == 0) {
+    dst[0] = mn;
+    dst[1] = mx;
+    dst[2] = dense ? 1 : 0;
+  }
 }
 
 // Class codes: 0 empty, 1 partial, 2 full, 3 undecided by closed forms.
 __device__ __forceinline__ int classify_closed(const BlockMaskArgs& a, int q0, int q1, int k0, int k1,
-                                               int qmin, int qmax, int kmin, int kmax) {
+                                               int qmin, int qmax, int qdense, int kmin, int kmax, int kdense) {
   const int dmin = q0 - (k1 - 1), dmax = (q1 - 1) - k0;  // range of q - kv over the box
   bool all = true, none = false;
   if (a.flags & FA_MASK_CAUSAL) {
@@ -67,20 +98,25 @@ __device__ __forceinline__ int classify_closed(const BlockMaskArgs& a, int q0, i
     all = all && ((k1 - 1 < a.prefix_len) || dmin >= 0);
     none = none || (k0 >= a.prefix_len && dmax < 0);
   }
+  const bool index_all = all;
   if (a.flags & FA_MASK_DOC) {
     all = all && (qmin == qmax && kmin == kmax && qmin == kmin);
     none = none || (qmax < kmin || kmax < qmin);
   }
   if (all) return 2;
   if (none) return 0;
-  // Without document ids, causal and window together allow exactly the pairs with q - kv in
-  // [0, window): the box's q - kv values form one integer interval, and each predicate alone
-  // was not all-false, so the interval meets [0, window) and some pair is allowed. Prefix-LM
-  // alone is one predicate that is not all-false. Everything else is settled exhaustively.
   if (!(a.flags & FA_MASK_DOC)) {
+    // Causal and window together allow exactly the pairs with q - kv in [0, window): the box's
+    // q - kv values form one integer interval, and each predicate alone was not all-false, so
+    // the interval meets [0, window) and some pair is allowed. Prefix-LM alone is one
+    // predicate that is not all-false.
     if (!(a.flags & FA_MASK_PREFIX_LM)) return 1;
     if (!(a.flags & FA_MASK_WINDOW)) return 1;
+    return 3;
   }
+  // Document ids with every index predicate true on the whole box: the tile is non-empty iff
+  // the blocks share an id, which dense blocks with overlapping ranges do.
+  if (index_all && qdense && kdense) return 1;
   return 3;
 }
 
@@ -89,18 +125,20 @@ __global__ __launch_bounds__(256) void bm_classify(BlockMaskArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   __shared__ int s_qdoc[128];
   __shared__ int s_kvdoc[128];
-  __shared__ int s_amb[256];
-  __shared__ int s_res[256];
+  __shared__ int s_amb[kChunk];
+  __shared__ unsigned char s_res[kChunk];
   __shared__ int s_namb;
-  __shared__ int s_wf[4], s_wp[4];
+  __shared__ int s_wtot[4];
 
   const int q0 = qb * a.BQ, q1 = min(a.Lq, q0 + a.BQ);
   const bool doc = (a.flags & FA_MASK_DOC) != 0;
   const MaskSpec ms{a.flags, a.window, a.prefix_len};
-  int qmin = 0, qmax = 0;
+  int qmin = 0, qmax = 0, qdense = 0;
   if (doc) {
-    qmin = a.qsum[2 * (b * a.nqb + qb)];
-    qmax = a.qsum[2 * (b * a.nqb + qb) + 1];
+    const int* qs = a.qsum + 3 * (b * a.nqb + qb);
+    qmin = qs[0];
+    qmax = qs[1];
+    qdense = qs[2];
     if (tid < a.BQ) s_qdoc[tid] = (q0 + tid < q1) ? a.q_doc[(int64_t)b * a.Lq + q0 + tid] : 0;
   }
   const int64_t row = (int64_t)b * a.nqb + qb;  // Hm = 1
@@ -108,26 +146,40 @@ __global__ __launch_bounds__(256) void bm_classify(BlockMaskArgs a) {
   int* part_idx = a.kv_idx + row * a.nkvb;
   int nfull = 0, npart = 0;
 
-  for (int c0 = 0; c0 < a.nkvb; c0 += 256) {
-    const int kb = c0 + tid;
-    int cls = -1;
-    if (kb < a.nkvb) {
-      const int k0 = kb * a.BK, k1 = min(a.Lkv, k0 + a.BK);
-      int kmin = 0, kmax = 0;
-      if (doc) {
-        kmin = a.kvsum[2 * (b * a.nkvb + kb)];
-        kmax = a.kvsum[2 * (b * a.nkvb + kb) + 1];
+  for (int c0 = 0; c0 < a.nkvb; c0 += kChunk) {
+    // 1. closed forms for this thread's run of kv blocks (summaries loaded up front).
+    const int kb0 = c0 + tid * kPerThread;
+    int kmn[kPerThread], kmx[kPerThread], kdn[kPerThread];
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      kmn[j] = kmx[j] = kdn[j] = 0;
+      if (doc && kb0 + j < a.nkvb) {
+        const int* ks = a.kvsum + 3 * (b * a.nkvb + kb0 + j);
+        kmn[j] = ks[0];
+        kmx[j] = ks[1];
+        kdn[j] = ks[2];
       }
-      cls = classify_closed(a, q0, q1, k0, k1, qmin, qmax, kmin, kmax);
     }
     if (tid == 0) s_namb = 0;
     __syncthreads();
-    if (cls == 3) s_amb[atomicAdd(&s_namb, 1)] = kb;
+    int cls[kPerThread];
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      const int kb = kb0 + j;
+      cls[j] = -1;
+      if (kb < a.nkvb) {
+        const int k0 = kb * a.BK, k1 = min(a.Lkv, k0 + a.BK);
+        cls[j] = classify_closed(a, q0, q1, k0, k1, qmin, qmax, qdense, kmn[j], kmx[j], kdn[j]);
+        if (cls[j] == 3) s_amb[atomicAdd(&s_namb, 1)] = tid * kPerThread + j;
+      }
+    }
     __syncthreads();
+
+    // 2. undecided tiles: every in-range pair, evaluated by the whole workgroup.
     const int namb = s_namb;
     for (int ai = 0; ai < namb; ++ai) {
-      const int kbA = s_amb[ai];
-      const int k0 = kbA * a.BK, k1 = min(a.Lkv, k0 + a.BK);
+      const int loc = s_amb[ai];
+      const int k0 = (c0 + loc) * a.BK, k1 = min(a.Lkv, k0 + a.BK);
       if (doc && tid < a.BK) s_kvdoc[tid] = (k0 + tid < k1) ? a.kv_doc[(int64_t)b * a.Lkv + k0 + tid] : 0;
       __syncthreads();
       bool any = false;
@@ -137,35 +189,41 @@ __global__ __launch_bounds__(256) void bm_classify(BlockMaskArgs a) {
         if (i < q1 && j < k1) any = any || mask_pair(ms, i, j, doc ? s_qdoc[ii] : 0, doc ? s_kvdoc[jj] : 0);
       }
       any = __syncthreads_or(any);
-      if (tid == 0) s_res[kbA - c0] = any ? 1 : 0;
+      if (tid == 0) s_res[loc] = any ? 1 : 0;
       __syncthreads();
     }
-    if (cls == 3) cls = s_res[tid];
 
-    // Ascending compaction: ballot within each wave, then across the 4 waves.
-    const bool isF = cls == 2, isP = cls == 1;
-    const uint64_t bf = __ballot(isF), bp = __ballot(isP);
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    const int pf = __popcll(bf & below), pp = __popcll(bp & below);
-    if (lane == 0) {
-      s_wf[wave] = __popcll(bf);
-      s_wp[wave] = __popcll(bp);
+    // 3. ascending compaction: exclusive scan of (full, partial) counts packed in one int.
+    int packed = 0;
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      if (cls[j] == 3) cls[j] = s_res[tid * kPerThread + j];
+      packed += (cls[j] == 2 ? 1 : 0) + (cls[j] == 1 ? 0x10000 : 0);
     }
+    int incl = packed;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int up = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += up;
+    }
+    if (lane == 63) s_wtot[wave] = incl;
     __syncthreads();
-    int basef = nfull, basep = npart, totf = 0, totp = 0;
+    int base = 0, tot = 0;
+#pragma unroll
     for (int w = 0; w < 4; ++w) {
-      if (w < wave) {
-        basef += s_wf[w];
-        basep += s_wp[w];
-      }
-      totf += s_wf[w];
-      totp += s_wp[w];
+      if (w < wave) base += s_wtot[w];
+      tot += s_wtot[w];
     }
-    if (isF) full_idx[basef + pf] = kb;
-    if (isP) part_idx[basep + pp] = kb;
-    nfull += totf;
-    npart += totp;
-    __syncthreads();
+    const int excl = base + incl - packed;
+    int pf = nfull + (excl & 0xffff), pp = npart + (excl >> 16);
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      if (cls[j] == 2) full_idx[pf++] = kb0 + j;
+      if (cls[j] == 1) part_idx[pp++] = kb0 + j;
+    }
+    nfull += tot & 0xffff;
+    npart += tot >> 16;
+    __syncthreads();  // s_namb, s_amb, s_res and s_wtot are reused by the next chunk
   }
   for (int j = nfull + tid; j < a.nkvb; j += 256) full_idx[j] = 0;
   for (int j = npart + tid; j < a.nkvb; j += 256) part_idx[j] = 0;
@@ -178,8 +236,8 @@ __global__ __launch_bounds__(256) void bm_classify(BlockMaskArgs a) {
 hipError_t launch_block_mask(const BlockMaskArgs& a, hipStream_t stream) {
   if (a.nqb == 0) return hipSuccess;
   if (a.flags & FA_MASK_DOC) {
-    const int n = a.B * (a.nqb + a.nkvb);
-    hipLaunchKernelGGL(bm_summaries, dim3((n + 255) / 256), dim3(256), 0, stream, a);
+    const int n = a.B * (a.nqb + a.nkvb);  // one wave each, four waves per workgroup
+    hipLaunchKernelGGL(bm_summaries, dim3((n + 3) / 4), dim3(256), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

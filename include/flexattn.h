@@ -103,8 +103,8 @@ typedef struct {
 size_t flexattn_block_mask_index_bytes(int Bm, int Hm, int q_len, int kv_len, int q_block, int kv_block);
 size_t flexattn_block_mask_count_bytes(int Bm, int Hm, int q_len, int q_block);
 
-/* Device scratch needed by flexattn_block_mask_build (per-block document-id ranges when DOC is
- * set, else 0). */
+/* Device scratch needed by flexattn_block_mask_build (per-block document-id summaries when DOC
+ * is set: 12 bytes per query block and per kv block and batch; else 0). */
 size_t flexattn_block_mask_workspace_bytes(int mask_kind, int B, int q_len, int kv_len,
                                            int q_block, int kv_block);
 

@@ -58,15 +58,20 @@ SPECS = [
 
 @pytest.mark.parametrize("si", range(len(SPECS)))
 @pytest.mark.parametrize("shape", [(2, 333, 333, 128, 128), (1, 700, 517, 64, 128), (2, 260, 390, 128, 64), (1, 64, 64, 64, 64)])
-@pytest.mark.parametrize("sorted_ids", [True, False])
-def test_random_cases_bit_exact(si, shape, sorted_ids):
+@pytest.mark.parametrize("ids", ["runs", "unsorted", "gapped"])
+def test_random_cases_bit_exact(si, shape, ids):
+    """runs: packed documents with consecutive ids; unsorted: independent random ids;
+    gapped: sorted runs whose ids skip values (ranges overlap without a shared id)."""
     B, Lq, Lkv, BQ, BK = shape
     spec = dict(SPECS[si])
-    if not spec.get("doc") and not sorted_ids:
+    if not spec.get("doc") and ids != "runs":
         pytest.skip("ids only matter with the document mask")
     if spec.get("doc"):
-        w = random_case(1000 + si, B=B, Lq=Lq, Lkv=Lkv, D=8, doc=True, n_docs=9, doc_sorted=sorted_ids)
+        w = random_case(1000 + si, B=B, Lq=Lq, Lkv=Lkv, D=8, doc=True, n_docs=9, doc_sorted=ids != "unsorted")
         spec["q_doc"], spec["kv_doc"] = w.q_doc, w.kv_doc
+        if ids == "gapped":
+            spec["q_doc"] = (w.q_doc * 2).astype(np.int32)
+            spec["kv_doc"] = (w.kv_doc * 2 + (1 if Lq != Lkv else 0)).astype(np.int32)
     got = build_gpu(spec, B, Lq, Lkv, BQ, BK)
     ref = ref_bm.block_mask(spec, B, Lq, Lkv, BQ, BK)
     assert_same(got, ref)
