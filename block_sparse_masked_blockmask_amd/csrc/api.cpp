@@ -139,10 +139,15 @@ static fa_status check_tensor(const fa_tensor* t, const char* name, int elem_ali
   return FA_OK;
 }
 
+static fa_status fwd_quantized(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_block_mask* bm,
+                               int mask_kind, int score_kind, const fa_params* p, fa_tensor* out, float* lse,
+                               hipStream_t stream);
+
 fa_status flexattn_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_block_mask* bm,
                        int mask_kind, int score_kind, const fa_params* p, fa_tensor* out, float* lse,
                        hipStream_t stream) {
   if (!q || !k || !v || !out) return fail(FA_ERR_INVALID_ARG, "q, k, v and out must not be NULL");
+  if (q->dtype == FA_I8) return fwd_quantized(q, k, v, bm, mask_kind, score_kind, p, out, lse, stream);
   const int dt = q->dtype;
   if (k->dtype != dt || v->dtype != dt || out->dtype != dt)
     return fail(FA_ERR_INVALID_ARG, "q, k, v and out must share one dtype");
@@ -226,5 +231,95 @@ fa_status flexattn_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* 
   if (e != hipSuccess) return fail(FA_ERR_DEVICE, "forward launch failed: %s", hipGetErrorString(e));
   return ok();
 }
+
+static fa_status check_q_tensor(const fa_tensor* t, const char* name, int dtype, int elem_align) {
+  if (t == nullptr) return fail(FA_ERR_INVALID_ARG, "%s is NULL", name);
+  if (t->dtype != dtype) return fail(FA_ERR_INVALID_ARG, "%s has dtype %d, expected %d", name, t->dtype, dtype);
+  if (t->B < 0 || t->H <= 0 || t->L < 0 || t->D != 128)
+    return fail(t->D != 128 ? FA_ERR_UNSUPPORTED : FA_ERR_INVALID_ARG, "%s must be [B, H, L, 128]", name);
+  if (t->data == nullptr && (int64_t)t->B * t->L > 0) return fail(FA_ERR_INVALID_ARG, "%s->data is NULL", name);
+  if (!aligned16(t->data)) return fail(FA_ERR_INVALID_ARG, "%s->data must be 16-byte aligned", name);
+  if (t->stride_b < 0 || t->stride_h < 0 || t->stride_l < t->D || t->stride_l > (1 << 24))
+    return fail(FA_ERR_INVALID_ARG, "%s has invalid strides", name);
+  if (t->stride_b % elem_align || t->stride_h % elem_align || t->stride_l % elem_align)
+    return fail(FA_ERR_INVALID_ARG, "%s strides must be multiples of %d elements", name, elem_align);
+  return FA_OK;
+}
+
+fa_status flexattn_quantize_qkv(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, fa_tensor* q8,
+                                fa_tensor* k8, fa_tensor* v8, hipStream_t stream) {
+  fa_status st;
+  if ((st = check_q_tensor(q, "q", FA_BF16, 8)) != FA_OK) return st;
+  if ((st = check_q_tensor(k, "k", FA_BF16, 8)) != FA_OK) return st;
+  if ((st = check_q_tensor(v, "v", FA_BF16, 8)) != FA_OK) return st;
+  if ((st = check_q_tensor(q8, "q8", FA_I8, 16)) != FA_OK) return st;
+  if ((st = check_q_tensor(k8, "k8", FA_I8, 16)) != FA_OK) return st;
+  if ((st = check_q_tensor(v8, "v8", FA_FP8_E4M3, 16)) != FA_OK) return st;
+  if (q->scale || k->scale || v->scale) return fail(FA_ERR_INVALID_ARG, "bf16 sources carry no scale");
+  if (!q8->scale || !k8->scale || !v8->scale) return fail(FA_ERR_INVALID_ARG, "q8, k8 and v8 need scale arrays");
+  if (q8->B != q->B || q8->H != q->H || q8->L != q->L || k8->B != k->B || k8->H != k->H || k8->L != k->L ||
+      v8->B != v->B || v8->H != v->H || v8->L != v->L)
+    return fail(FA_ERR_INVALID_ARG, "quantized outputs must have the shapes of their sources");
+  if ((int64_t)q->B * q->H > 65535 || (int64_t)k->B * k->H > 65535 || q->B > 65535)
+    return fail(FA_ERR_UNSUPPORTED, "B and H above the grid limits");
+  fa::QuantArgs a{};
+  auto src = [](const fa_tensor* t) {
+    return fa::QuantTensor{static_cast<const unsigned short*>(t->data), t->B, t->H, t->L, t->stride_b, t->stride_h, t->stride_l};
+  };
+  auto dst = [](fa_tensor* t, int nblocks) {
+    return fa::QuantOut{static_cast<signed char*>(t->data), const_cast<float*>(t->scale), nblocks, t->stride_b,
+                        t->stride_h, t->stride_l};
+  };
+  a.q = src(q);
+  a.k = src(k);
+  a.v = src(v);
+  a.q8 = dst(q8, cdiv(q->L, 128));
+  a.k8 = dst(k8, cdiv(k->L, 128));
+  a.v8 = dst(v8, 128);
+  hipError_t e = fa::launch_quantize(a, stream);
+  if (e != hipSuccess) return fail(FA_ERR_DEVICE, "quantize launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+static fa_status fwd_quantized(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_block_mask* bm,
+                               int mask_kind, int score_kind, const fa_params* p, fa_tensor* out, float* lse,
+                               hipStream_t stream) {
+  fa_status st;
+  if ((st = check_q_tensor(q, "q", FA_I8, 16)) != FA_OK) return st;
+  if ((st = check_q_tensor(k, "k", FA_I8, 16)) != FA_OK) return st;
+  if ((st = check_q_tensor(v, "v", FA_FP8_E4M3, 16)) != FA_OK) return st;
+  if ((st = check_q_tensor(out, "out", FA_BF16, 8)) != FA_OK) return st;
+  if (!q->scale || !k->scale || !v->scale) return fail(FA_ERR_INVALID_ARG, "quantized q, k and v need scale arrays");
+  if (out->scale) return fail(FA_ERR_INVALID_ARG, "out->scale must be NULL");
+  if (mask_kind != FA_MASK_NONE || score_kind != FA_SCORE_NONE || bm != nullptr)
+    return fail(FA_ERR_UNSUPPORTED, "the quantized form serves unmasked attention without score_mod (no BlockMask)");
+  if (k->B != q->B || v->B != q->B || out->B != q->B) return fail(FA_ERR_INVALID_ARG, "batch sizes differ");
+  if (k->H != v->H || k->L != v->L) return fail(FA_ERR_INVALID_ARG, "k and v shapes differ");
+  if (q->H % k->H != 0) return fail(FA_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", q->H, k->H);
+  if (out->H != q->H || out->L != q->L) return fail(FA_ERR_INVALID_ARG, "out shape differs from q");
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(FA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  const int64_t total = (int64_t)q->B * q->H * cdiv(q->L, 128);
+  if (total > 0x7fffffff) return fail(FA_ERR_UNSUPPORTED, "grid too large");
+  fa::QuantFwdArgs a{};
+  a.q = static_cast<const signed char*>(q->data);
+  a.k = static_cast<const signed char*>(k->data);
+  a.v = static_cast<const unsigned char*>(v->data);
+  a.o = static_cast<__bf16*>(out->data);
+  a.lse = lse;
+  a.q_sb = q->stride_b; a.q_sh = q->stride_h; a.q_sl = q->stride_l;
+  a.k_sb = k->stride_b; a.k_sh = k->stride_h; a.k_sl = k->stride_l;
+  a.v_sb = v->stride_b; a.v_sh = v->stride_h; a.v_sl = v->stride_l;
+  a.o_sb = out->stride_b; a.o_sh = out->stride_h; a.o_sl = out->stride_l;
+  a.q_scale = q->scale; a.k_scale = k->scale; a.v_scale = v->scale;
+  a.B = q->B; a.Hq = q->H; a.Hkv = k->H; a.Lq = q->L; a.Lkv = k->L; a.group = q->H / k->H;
+  a.nqb = cdiv(q->L, 128); a.nkb = cdiv(k->L, 128);
+  const float sm = (p && p->sm_scale > 0.f) ? p->sm_scale : 1.0f / std::sqrt(128.0f);
+  a.scale_log2 = sm * 1.4426950408889634f;
+  a.total_wg = (int)total;
+  hipError_t e = fa::launch_fwd_quant(a, stream);
+  if (e != hipSuccess) return fail(FA_ERR_DEVICE, "forward launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 
 }  // extern "C"

@@ -45,7 +45,41 @@ struct FwdArgs {
   int total_wg;
 };
 
+// Quantized form: bf16 sources and int8 / E4M3 outputs (element strides; int8 elements are bytes).
+struct QuantTensor {
+  const unsigned short* data;  // bf16 bit patterns
+  int B, H, L;
+  int64_t sb, sh, sl;
+};
+struct QuantOut {
+  signed char* data;           // int8 codes, or E4M3 codes for V
+  float* scale;                // Q/K: [B][H][nblocks]; V: [B][H][128]
+  int nblocks;
+  int64_t sb, sh, sl;
+};
+struct QuantArgs {
+  QuantTensor q, k, v;
+  QuantOut q8, k8, v8;
+};
+
+struct QuantFwdArgs {
+  const signed char* q;
+  const signed char* k;
+  const unsigned char* v;
+  __bf16* o;
+  float* lse;
+  int64_t q_sb, q_sh, q_sl, k_sb, k_sh, k_sl, v_sb, v_sh, v_sl, o_sb, o_sh, o_sl;
+  const float* q_scale;  // [B][Hq][nqb]
+  const float* k_scale;  // [B][Hkv][nkb]
+  const float* v_scale;  // [B][Hkv][128]
+  int B, Hq, Hkv, Lq, Lkv, group, nqb, nkb;
+  float scale_log2;      // sm_scale * log2(e)
+  int total_wg;
+};
+
 hipError_t launch_block_mask(const BlockMaskArgs& a, hipStream_t stream);
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
+hipError_t launch_fwd_quant(const QuantFwdArgs& a, hipStream_t stream);
 // dtype 0 = f32, 1 = bf16; kv_block in {64, 128}; score bits FA_SCORE_*.
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int kv_block, int score, hipStream_t stream);
 

@@ -1,0 +1,415 @@
+// Quantized attention form (gfx950): int8 Q.K^T and OCP E4M3 P.V with bf16 output.
+//
+// FlashRT-Structures PR #1 ("LTX-2.5 attention forms"): the sage2 form runs Q.K^T on int8 and
+// P.V on fp8 with bf16 output; masked sites are refused. Granularity and rounding here:
+//   Q, K: one float32 scale per (batch, head, 128-token block), scale = amax / 127, code =
+//         round-to-nearest-even(x / scale) clamped to +-127 (amax 0: scale 0, codes 0);
+//   V:    one float32 scale per (batch, head, channel) over all tokens, scale = amax / 448, code
+//         = E4M3(x / scale), round-to-nearest-even; the quotient is clamped to +-448 first
+//         because the conversion instruction does not saturate (it returns NaN above 464);
+//   P:    the softmax numerators P in [0, 1] are coded as E4M3(448 P); the row sum uses the
+//         unrounded P; out = (sum_j P8_j V8_j) * scale_V / (448 * l).
+// The forward computes S^T = K8 Q8^T on v_mfma_i32_32x32x32_i8 (exact integer dot products,
+// then times scale_Q * scale_K * sm_scale) and O^T += V8^T P8^T on the 32x32x64 fp8 MFMA.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace fa {
+
+namespace {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+
+constexpr float kE4M3Max = 448.0f;
+
+__device__ __forceinline__ float bf16_to_f32(unsigned short b) { return __uint_as_float((unsigned)b << 16); }
+
+__device__ __forceinline__ float block_max_256(float x, float* s_red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) s_red[wave] = x;
+  __syncthreads();
+  x = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  return x;
+}
+
+}  // namespace
+
+// One workgroup per (128-token block, head, batch) of Q or K: absmax scale and int8 codes.
+__global__ __launch_bounds__(256) void quant_qk_kernel(QuantArgs a, int which) {
+  const QuantTensor& src = which == 0 ? a.q : a.k;
+  const QuantOut& dst = which == 0 ? a.q8 : a.k8;
+  const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  __shared__ float s_red[4];
+  const int tid = threadIdx.x;
+  const int r0 = blk * 128;
+  const int rows = min(128, src.L - r0);
+  // Thread t handles rows t/16 + 16*i (i = 0..7) and channels 8*(t%16) .. +8.
+  const unsigned short* base = src.data + b * src.sb + h * src.sh;
+  float x[8][8];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = tid / 16 + 16 * i;
+    if (r < rows) {
+      const i32x4 raw = *(const i32x4*)(base + (int64_t)(r0 + r) * src.sl + 8 * (tid % 16));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[i][2 * e] = bf16_to_f32((unsigned short)(raw[e] & 0xffff));
+        x[i][2 * e + 1] = bf16_to_f32((unsigned short)((unsigned)raw[e] >> 16));
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[i][e] = 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[i][e]));
+  }
+  amax = block_max_256(amax, s_red);
+  const float scale = amax / 127.0f;  // correctly rounded division
+  if (tid == 0) dst.scale[((int64_t)b * src.H + h) * dst.nblocks + blk] = scale;
+  signed char* out = dst.data + b * dst.sb + h * dst.sh;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = tid / 16 + 16 * i;
+    if (r >= rows) continue;
+    unsigned lo = 0, hi = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      int c = 0;
+      if (scale > 0.f) c = (int)fminf(fmaxf(rintf(x[i][e] / scale), -127.f), 127.f);
+      const unsigned byte = (unsigned)(c & 0xff);
+      if (e < 4) lo |= byte << (8 * e); else hi |= byte << (8 * (e - 4));
+    }
+    *(i32x2*)(out + (int64_t)(r0 + r) * dst.sl + 8 * (tid % 16)) = i32x2{(int)lo, (int)hi};
+  }
+}
+
+__global__ __launch_bounds__(256) void quant_zero_kernel(float* p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0.f;
+}
+
+// Pass 1 for V: per-channel maximum of |x| over a chunk of rows, folded into the scale array
+// as amax / 448 with an atomic max on the (non-negative) float bits. Rounding x -> x / 448 is
+// monotone, so the maximum of the rounded quotients is the rounded quotient of the maximum.
+__global__ __launch_bounds__(256) void quant_v_amax_kernel(QuantArgs a, int rows_per_wg) {
+  const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x;
+  __shared__ float s_part[16][128];
+  const unsigned short* base = a.v.data + b * a.v.sb + h * a.v.sh;
+  const int r_begin = chunk * rows_per_wg, r_end = min(a.v.L, r_begin + rows_per_wg);
+  float m[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int r = r_begin + tid / 16; r < r_end; r += 16) {
+    const i32x4 raw = *(const i32x4*)(base + (int64_t)r * a.v.sl + 8 * (tid % 16));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      m[2 * e] = fmaxf(m[2 * e], fabsf(bf16_to_f32((unsigned short)(raw[e] & 0xffff))));
+      m[2 * e + 1] = fmaxf(m[2 * e + 1], fabsf(bf16_to_f32((unsigned short)((unsigned)raw[e] >> 16))));
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s_part[tid / 16][8 * (tid % 16) + e] = m[e];
+  __syncthreads();
+  if (tid < 128) {
+    float mx = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s_part[i][tid]);
+    const float sc = mx / kE4M3Max;
+    atomicMax((unsigned int*)(a.v8.scale + ((int64_t)b * a.v.H + h) * 128 + tid), __float_as_uint(sc));
+  }
+}
+
+// Pass 2 for V: E4M3 codes of x / scale (scale 0: code 0).
+__global__ __launch_bounds__(256) void quant_v_encode_kernel(QuantArgs a, int rows_per_wg) {
+  const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const unsigned short* base = a.v.data + b * a.v.sb + h * a.v.sh;
+  unsigned char* out = (unsigned char*)a.v8.data + b * a.v8.sb + h * a.v8.sh;
+  const float* sc = a.v8.scale + ((int64_t)b * a.v.H + h) * 128 + 8 * (tid % 16);
+  float s[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s[e] = sc[e];
+  const int r_begin = chunk * rows_per_wg, r_end = min(a.v.L, r_begin + rows_per_wg);
+  for (int r = r_begin + tid / 16; r < r_end; r += 16) {
+    const i32x4 raw = *(const i32x4*)(base + (int64_t)r * a.v.sl + 8 * (tid % 16));
+    float y[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      y[2 * e] = bf16_to_f32((unsigned short)(raw[e] & 0xffff));
+      y[2 * e + 1] = bf16_to_f32((unsigned short)((unsigned)raw[e] >> 16));
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = s[e] > 0.f ? fminf(fmaxf(y[e] / s[e], -kE4M3Max), kE4M3Max) : 0.f;
+    int w0 = 0, w1 = 0;
+    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], w0, false);
+    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w0, true);
+    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], w1, false);
+    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], w1, true);
+    *(i32x2*)(out + (int64_t)r * a.v8.sl + 8 * (tid % 16)) = i32x2{w0, w1};
+  }
+}
+
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream) {
+  const int qb = (a.q.L + 127) / 128, kb = (a.k.L + 127) / 128;
+  if (a.q.B > 0 && qb > 0)
+    hipLaunchKernelGGL(quant_qk_kernel, dim3(qb, a.q.H, a.q.B), dim3(256), 0, stream, a, 0);
+  if (a.k.B > 0 && kb > 0)
+    hipLaunchKernelGGL(quant_qk_kernel, dim3(kb, a.k.H, a.k.B), dim3(256), 0, stream, a, 1);
+  const int nscale = a.v.B * a.v.H * 128;
+  if (nscale > 0) {
+    hipLaunchKernelGGL(quant_zero_kernel, dim3((nscale + 255) / 256), dim3(256), 0, stream, a.v8.scale, nscale);
+    if (a.v.L > 0) {
+      const int rows_per_wg = 512;
+      const int chunks = (a.v.L + rows_per_wg - 1) / rows_per_wg;
+      hipLaunchKernelGGL(quant_v_amax_kernel, dim3(chunks, a.v.H, a.v.B), dim3(256), 0, stream, a, rows_per_wg);
+      hipLaunchKernelGGL(quant_v_encode_kernel, dim3(chunks, a.v.H, a.v.B), dim3(256), 0, stream, a, rows_per_wg);
+    }
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
+// Quantized forward. One workgroup of 4 waves per (batch, query head, 128-query block); wave w
+// owns 32 queries, as in the bf16 kernel. Keys in steps of 64: the int8 K rows and fp8 V rows
+// of a step (8 KB each) stream into one of two LDS buffers with global_load_lds_dwordx4.
+//
+// LDS rows are 128 bytes (8 chunks of 16); chunk c of row r is stored at position c ^ ((r/2)%8),
+// which spreads 16 consecutive rows read at one chunk over distinct banks. V rows are stored
+// in a permuted order within each 16-row group (logical rows 0-3, 8-11, 4-7, 12-15), so that the
+// 8 consecutive physical rows returned by one ds_read_b64_tr_b8 are exactly the keys of one lane
+// half's softmax numerators, in accumulator order.
+// ---------------------------------------------------------------------------------------------
+namespace {
+
+constexpr int kQStep = 64;
+constexpr int kQStepBytes = kQStep * 128;
+
+__shared__ __attribute__((aligned(1024))) unsigned char q_k0[kQStepBytes];
+__shared__ __attribute__((aligned(1024))) unsigned char q_v0[kQStepBytes];
+__shared__ __attribute__((aligned(1024))) unsigned char q_k1[kQStepBytes];
+__shared__ __attribute__((aligned(1024))) unsigned char q_v1[kQStepBytes];
+
+template <int B> __device__ __forceinline__ unsigned char* qkbuf() { return B ? q_k1 : q_k0; }
+template <int B> __device__ __forceinline__ unsigned char* qvbuf() { return B ? q_v1 : q_v0; }
+
+__device__ __forceinline__ int qswz(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int qoff(int r, int chunk) { return r * 128 + ((chunk ^ qswz(r)) << 4); }
+// Logical row of physical row p within a 16-row group: 0-3, 8-11, 4-7, 12-15.
+__device__ __forceinline__ int vperm(int p) { return (p & ~15) | ((p & 3) | ((p & 4) << 1) | ((p & 8) >> 1)); }
+
+__device__ __forceinline__ void qdma16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void qwait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+struct QCtx {
+  int wave, lane, hl, lq, g16, s16, qi;
+  bool q_in;
+  const signed char* kp;
+  const unsigned char* vp;
+  const float* ks;   // K block scales of this (b, hkv)
+  float qscale;      // scale_Q * sm_scale * log2(e)
+};
+
+struct QState {
+  f32x16 oacc[4];
+  float m_run, l_run;
+};
+
+template <int B>
+__device__ __forceinline__ void qissue(const QuantFwdArgs& a, const QCtx& c, int kv0) {
+  // 8 KB per tensor = 8 segments of 1 KB (8 rows); wave w loads segments w and w + 4.
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int seg = i * 4 + c.wave;
+    const int p = seg * 8 + (c.lane >> 3);  // physical row written by this lane
+    const int pos = c.lane & 7;             // physical chunk position
+    const int kr = min(kv0 + p, a.Lkv - 1);
+    const int vr = min(kv0 + vperm(p), a.Lkv - 1);
+    qdma16(c.kp + (int64_t)kr * a.k_sl + ((pos ^ qswz(p)) << 4), qkbuf<B>() + seg * 1024);
+    qdma16(c.vp + (int64_t)vr * a.v_sl + ((pos ^ qswz(p)) << 4), qvbuf<B>() + seg * 1024);
+  }
+}
+
+template <int B>
+__device__ __forceinline__ void qcompute(const QuantFwdArgs& a, const QCtx& c, const i32x4 (&qreg)[4], QState& st,
+                                         int kv0, float kscale) {
+  const unsigned char* sK = qkbuf<B>();
+  const unsigned char* sV = qvbuf<B>();
+  // S^T = K8 Q8^T: exact int32 dot products, 4 k-steps of 32 channels per 32-key sub-block.
+  i32x16 iacc[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int r = nb * 32 + c.lq;
+    iacc[nb] = i32x16{};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const i32x4 kf = *(const i32x4*)(sK + qoff(r, 2 * ks + c.hl));
+      iacc[nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qreg[ks], iacc[nb], 0, 0, 0);
+    }
+  }
+  const float sc = c.qscale * kscale;
+  float t[2][16];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int kv = kv0 + nb * 32 + (i >> 2) * 8 + c.hl * 4 + (i & 3);
+      t[nb][i] = kv < a.Lkv ? (float)iacc[nb][i] * sc : -INFINITY;
+      mx = fmaxf(mx, t[nb][i]);
+    }
+  }
+  mx = half_swap_max(mx);
+  // Exact running maximum (P <= 1 keeps 448 P inside the E4M3 range).
+  const float m_new = fmaxf(st.m_run, mx);
+  const bool raise = m_new > st.m_run;
+  if (__builtin_amdgcn_readfirstlane(__ballot(raise) != 0)) {
+    const float alpha = raise ? fast_exp2(st.m_run - m_new) : 1.0f;
+    st.l_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) st.oacc[db] *= alpha;
+    st.m_run = m_new;
+  }
+  // P^T as the fp8 B operand: byte j of the 32 holds key position (j / 16, element j % 16).
+  i32x8 pb;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    const int nb = w >> 2, i0 = (w & 3) * 4;
+    const float p0 = fast_exp2(t[nb][i0] - st.m_run), p1 = fast_exp2(t[nb][i0 + 1] - st.m_run);
+    const float p2 = fast_exp2(t[nb][i0 + 2] - st.m_run), p3 = fast_exp2(t[nb][i0 + 3] - st.m_run);
+    st.l_run += (p0 + p1) + (p2 + p3);
+    int word = 0;
+    word = __builtin_amdgcn_cvt_pk_fp8_f32(p0 * kE4M3Max, p1 * kE4M3Max, word, false);
+    word = __builtin_amdgcn_cvt_pk_fp8_f32(p2 * kE4M3Max, p3 * kE4M3Max, word, true);
+    pb[w] = word;
+  }
+  // O^T += V8^T P8^T. Transposed reads: in each 16-lane group, source lane s points at physical
+  // row base + s/2 and channels d0 + 8*(s%2); lane i receives channel d0 + i of rows base..+7.
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    const int d = db * 32 + 16 * (c.g16 & 1) + 8 * (c.s16 & 1);
+    i32x8 vf;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int p = rr * 16 + (c.g16 >> 1) * 8 + (c.s16 >> 1);
+      const i32x2 v2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(sV + qoff(p, d >> 4) + (d & 15)));
+      vf[2 * rr] = v2[0];
+      vf[2 * rr + 1] = v2[1];
+    }
+    // Formats 0/0: both operands E4M3; scale exponents 127 mean a factor of 1.
+    st.oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pb, st.oacc[db], 0, 0, 0, 127, 0, 127);
+  }
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(256, 2) void fwd_quant_kernel(QuantFwdArgs a) {
+  int w = xcd_remap(blockIdx.x, a.total_wg);
+  const int g = w % a.group;
+  w /= a.group;
+  const int qb = a.nqb - 1 - (w % a.nqb);
+  w /= a.nqb;
+  const int hkv = w % a.Hkv, b = w / a.Hkv;
+  const int hq = hkv * a.group + g;
+
+  QCtx c;
+  c.wave = threadIdx.x >> 6;
+  c.lane = threadIdx.x & 63;
+  c.hl = c.lane >> 5;
+  c.lq = c.lane & 31;
+  c.g16 = c.lane >> 4;
+  c.s16 = c.lane & 15;
+  c.qi = qb * 128 + c.wave * 32 + c.lq;
+  c.q_in = c.qi < a.Lq;
+  c.kp = a.k + b * a.k_sb + hkv * a.k_sh;
+  c.vp = a.v + b * a.v_sb + hkv * a.v_sh;
+  c.ks = a.k_scale + ((int64_t)b * a.Hkv + hkv) * a.nkb;
+  c.qscale = a.q_scale[((int64_t)b * a.Hq + hq) * a.nqb + qb] * a.scale_log2;
+
+  const int nsteps = (a.Lkv + kQStep - 1) / kQStep;
+  // K scale of step s: a 64-key step lies inside one 128-key block. Each step's scale is loaded
+  // with its transfers, one step ahead, so that its wait is the step's own.
+  float ks_cur = 0.f;
+  if (nsteps > 0) {
+    qissue<0>(a, c, 0);
+    ks_cur = c.ks[0];
+  }
+
+  // Q8^T as the int8 B operand: lane holds Q8[qi][32*ks + 16*hl .. +16] for ks = 0..3.
+  const signed char* qp = a.q + b * a.q_sb + hq * a.q_sh;
+  i32x4 qreg[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+    qreg[ks] = c.q_in ? *(const i32x4*)(qp + (int64_t)c.qi * a.q_sl + ks * 32 + c.hl * 16) : i32x4{};
+
+  QState st;
+#pragma unroll
+  for (int db = 0; db < 4; ++db) st.oacc[db] = f32x16{};
+  st.m_run = -INFINITY;
+  st.l_run = 0.f;
+
+  for (int s = 0; s < nsteps; s += 2) {
+    qwait_vmem();
+    __syncthreads();
+    float ks_nxt = 0.f;
+    if (s + 1 < nsteps) {
+      qissue<1>(a, c, (s + 1) * kQStep);
+      ks_nxt = c.ks[((s + 1) * kQStep) >> 7];
+    }
+    qcompute<0>(a, c, qreg, st, s * kQStep, ks_cur);
+    ks_cur = ks_nxt;
+    if (s + 1 < nsteps) {
+      qwait_vmem();
+      __syncthreads();
+      if (s + 2 < nsteps) {
+        qissue<0>(a, c, (s + 2) * kQStep);
+        ks_nxt = c.ks[((s + 2) * kQStep) >> 7];
+      }
+      qcompute<1>(a, c, qreg, st, (s + 1) * kQStep, ks_cur);
+      ks_cur = ks_nxt;
+    }
+  }
+
+  // Epilogue: out = O * scale_V[channel] / (448 l), bf16; lse in natural log.
+  const float l_tot = half_swap_sum(st.l_run);
+  const float inv = l_tot > 0.f ? 1.0f / (kE4M3Max * l_tot) : 0.f;
+  if (c.q_in) {
+    const float* vs = a.v_scale + ((int64_t)b * a.Hkv + hkv) * 128;
+    __bf16* op = a.o + b * a.o_sb + hq * a.o_sh + (int64_t)c.qi * a.o_sl;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int d = db * 32 + gq * 8 + c.hl * 4;
+        const f32x4 s4 = *(const f32x4*)(vs + d);
+        bf16x4 o4;
+        o4[0] = (__bf16)(st.oacc[db][gq * 4 + 0] * s4[0] * inv);
+        o4[1] = (__bf16)(st.oacc[db][gq * 4 + 1] * s4[1] * inv);
+        o4[2] = (__bf16)(st.oacc[db][gq * 4 + 2] * s4[2] * inv);
+        o4[3] = (__bf16)(st.oacc[db][gq * 4 + 3] * s4[3] * inv);
+        *(bf16x4*)(op + d) = o4;
+      }
+    }
+    if (a.lse && c.hl == 0)
+      a.lse[((int64_t)b * a.Hq + hq) * a.Lq + c.qi] = l_tot > 0.f ? (st.m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
+hipError_t launch_fwd_quant(const QuantFwdArgs& a, hipStream_t stream) {
+  if (a.total_wg == 0) return hipSuccess;
+  hipLaunchKernelGGL(fwd_quant_kernel, dim3(a.total_wg), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace fa

@@ -71,6 +71,8 @@ def lib() -> ctypes.CDLL:
                                    POINTER(FaBlockMask), c_int, c_int, POINTER(FaParams),
                                    POINTER(FaTensor), c_void_p, c_void_p]
         L.flexattn_fwd.restype = c_int
+        L.flexattn_quantize_qkv.argtypes = [POINTER(FaTensor)] * 6 + [c_void_p]
+        L.flexattn_quantize_qkv.restype = c_int
         L.flexattn_last_error.argtypes = []
         L.flexattn_last_error.restype = ctypes.c_char_p
         L.flexattn_version.argtypes = []
@@ -103,6 +105,8 @@ def _ptr(t: Optional[torch.Tensor]):
 
 
 _DTYPES = {torch.float32: FA_F32, torch.bfloat16: FA_BF16, torch.int8: FA_I8, torch.uint8: FA_FP8_E4M3}
+if hasattr(torch, "float8_e4m3fn"):
+    _DTYPES[torch.float8_e4m3fn] = FA_FP8_E4M3
 
 
 def tensor_desc(t: torch.Tensor, scale: Optional[torch.Tensor] = None) -> FaTensor:
@@ -178,18 +182,44 @@ def flexattn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_mask: 
                  mask_kind: int = FA_MASK_NONE, score_kind: int = FA_SCORE_NONE, *, window: int = 0,
                  prefix_len: int = 0, softcap: float = 0.0, alibi_slopes=None, q_doc=None, kv_doc=None,
                  sm_scale: float = 0.0, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                 return_lse: bool = True, stream=None):
-    """Forward pass; returns (out, lse). lse is None when return_lse is False and none is given."""
+                 return_lse: bool = True, stream=None, q_scale=None, k_scale=None, v_scale=None):
+    """Forward pass; returns (out, lse). lse is None when return_lse is False and none is given.
+
+    For the quantized form pass the int8 q/k and E4M3 v codes with their scale arrays (as
+    returned by flexattn_quantize_qkv); out is then bf16.
+    """
     if out is None:
-        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+        odt = torch.bfloat16 if q.dtype == torch.int8 else q.dtype
+        out = torch.empty(q.shape, dtype=odt, device=q.device)
     if lse is None and return_lse:
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != tuple(q.shape[:3])):
         raise ValueError("lse must be a contiguous float32 [B, Hq, Lq] tensor")
-    tq, tk, tv, to = tensor_desc(q), tensor_desc(k), tensor_desc(v), tensor_desc(out)
+    tq, tk, tv, to = tensor_desc(q, q_scale), tensor_desc(k, k_scale), tensor_desc(v, v_scale), tensor_desc(out)
     p = _params(window=window, prefix_len=prefix_len, softcap=softcap, alibi_slopes=alibi_slopes,
                 q_doc=q_doc, kv_doc=kv_doc, sm_scale=sm_scale)
     bm = ctypes.byref(block_mask.as_struct()) if block_mask is not None else None
     _check(lib().flexattn_fwd(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), bm, mask_kind, score_kind,
                               ctypes.byref(p), ctypes.byref(to), _ptr(lse), _stream(stream)))
     return out, lse
+
+
+def flexattn_quantize_qkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, out=None, stream=None):
+    """Quantize bf16 q, k, v (flexattn_quantize_qkv). Returns a dict with q8, k8 (int8), v8
+    (uint8 E4M3 codes) and their float32 scales q_scale [B,H,ceil(L/128)], k_scale, v_scale
+    [B,H,128]; `out` may supply these tensors (same keys) to avoid allocation."""
+    def blocks(t):
+        return -(-t.shape[2] // 128)
+    if out is None:
+        out = {
+            "q8": torch.empty(q.shape, dtype=torch.int8, device=q.device),
+            "k8": torch.empty(k.shape, dtype=torch.int8, device=k.device),
+            "v8": torch.empty(v.shape, dtype=torch.uint8, device=v.device),
+            "q_scale": torch.empty((q.shape[0], q.shape[1], blocks(q)), dtype=torch.float32, device=q.device),
+            "k_scale": torch.empty((k.shape[0], k.shape[1], blocks(k)), dtype=torch.float32, device=k.device),
+            "v_scale": torch.empty((v.shape[0], v.shape[1], v.shape[3]), dtype=torch.float32, device=v.device),
+        }
+    descs = [tensor_desc(q), tensor_desc(k), tensor_desc(v), tensor_desc(out["q8"], out["q_scale"]),
+             tensor_desc(out["k8"], out["k_scale"]), tensor_desc(out["v8"], out["v_scale"])]
+    _check(lib().flexattn_quantize_qkv(*[ctypes.byref(d) for d in descs], _stream(stream)))
+    return out

@@ -120,11 +120,29 @@ fa_status flexattn_block_mask_build(int mask_kind, const fa_params* p, int B, in
                                     fa_block_mask* out, void* workspace, size_t workspace_bytes,
                                     hipStream_t stream);
 
-/* Forward pass. q [B][Hq][Lq][D], k and v [B][Hkv][Lkv][D], out [B][Hq][Lq][D] (same dtype as q),
+/* Quantize bf16 q, k, v for the quantized forward (the int8-QK / fp8-PV attention form of
+ * FlashRT-Structures PR #1, "LTX-2.5 attention forms"). All tensors are [B, H, L, 128] on the
+ * device, D contiguous; q, k, v are FA_BF16 with scale = NULL; q8 and k8 are FA_I8 and v8 is
+ * FA_FP8_E4M3, with the shapes of their sources, data 16-byte aligned and strides multiples of
+ * 16 elements. Outputs (caller-owned, written on `stream`):
+ *   q8/k8 data: int8 codes; q8->scale / k8->scale: float32 [B][H][ceil(L/128)], one scale per
+ *     128-token block: scale = amax / 127, code = round-half-even(x / scale) clamped to +-127
+ *     (amax = 0 gives scale 0 and codes 0);
+ *   v8 data: OCP E4M3 codes; v8->scale: float32 [B][H][128], one scale per channel over all
+ *     tokens: scale = amax / 448, code = E4M3(x / scale) rounded half-even (scale 0: code 0).
+ * The `scale` pointers of q8, k8 and v8 are written despite their const qualifier. */
+fa_status flexattn_quantize_qkv(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v,
+                                fa_tensor* q8, fa_tensor* k8, fa_tensor* v8, hipStream_t stream);
+
+/* Forward pass. q [B][Hq][Lq][D], k and v [B][Hkv][Lkv][D], out [B][Hq][Lq][D],
  * lse [B][Hq][Lq] float32 contiguous (natural log; may be NULL). Supported envelope:
  *   - D = 128;
- *   - dtypes: all FA_F32 (float32 MFMA, fp32 softmax) or all FA_BF16 (bf16 MFMA with fp32
- *     accumulation and softmax; P rounded to bf16 before P.V);
+ *   - dtypes: all FA_F32 (float32 MFMA, fp32 softmax); all FA_BF16 (bf16 MFMA with fp32
+ *     accumulation and softmax; P rounded to bf16 before P.V); or the quantized form q, k FA_I8
+ *     and v FA_FP8_E4M3 as written by flexattn_quantize_qkv (their scale arrays set) with out
+ *     FA_BF16: Q.K^T on int8 MFMA, P coded as E4M3(448 P), P.V on fp8 MFMA. The quantized form
+ *     serves unmasked attention only (mask_kind NONE, score_kind NONE, bm NULL; anything else is
+ *     FA_ERR_UNSUPPORTED, as the page's attention form refuses masked sites);
  *   - Hq a multiple of Hkv (GQA: query head h reads kv head h / (Hq / Hkv));
  *   - data pointers 16-byte aligned and stride_b/h/l multiples of 8 elements (bf16) or
  *     4 elements (f32);

@@ -117,9 +117,9 @@ def dequantize_fp8(codes, scales):
 def attention_dequantized(q8, sq, k8, sk, v8, sv, rows, b, h, *, sm_scale=None, round_p=True):
     """Diagnostic: unmasked fp64 attention on dequantized inputs for some rows.
 
-    P is rounded through E4M3 at a fixed x448 scale (P in [0, 1]); the row sum
-    uses the unrounded P. Parity unpinned: this only bounds how much of the
-    quantized form's error is the quantization itself.
+    P is rounded through E4M3 at a fixed x448 scale (P in [0, 1], relative to the
+    final row maximum); the row sum uses the unrounded P. Parity unpinned: this
+    only bounds how much of the quantized form's error is the quantization itself.
     """
     qh = dequantize_int8(q8[b:b + 1, h:h + 1], sq[b:b + 1, h:h + 1])[0, 0]
     kh = dequantize_int8(k8[b:b + 1, h:h + 1], sk[b:b + 1, h:h + 1])[0, 0]

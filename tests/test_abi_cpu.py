@@ -65,7 +65,7 @@ def _fwd(q, k, v, out, bm=None, mask=0, score=0, p=None):
     ("d64", fa.FA_ERR_UNSUPPORTED, "head dim"),
     ("gqa", fa.FA_ERR_INVALID_ARG, "multiple of Hkv"),
     ("dtype_mix", fa.FA_ERR_INVALID_ARG, "share one dtype"),
-    ("i8", fa.FA_ERR_UNSUPPORTED, "dtype"),
+    ("i8", fa.FA_ERR_INVALID_ARG, "expected 3"),
     ("prefix_causal", fa.FA_ERR_INVALID_ARG, "PREFIX_LM"),
     ("no_bm", fa.FA_ERR_INVALID_ARG, "BlockMask is required"),
     ("misaligned", fa.FA_ERR_INVALID_ARG, "16-byte aligned"),
@@ -152,3 +152,18 @@ def test_product_path_does_not_import_oracle():
             if f.endswith((".py", ".cpp", ".hip", ".h")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.replace("oracles", ""), f
+
+
+def test_quantize_validation():
+    lib = fa.lib()
+    q = _t()
+    q8 = FaTensor(256, fa.FA_I8, 1, 2, 100, 128, 2 * 100 * 128, 100 * 128, 128, 512)
+    v8 = FaTensor(256, fa.FA_FP8_E4M3, 1, 2, 100, 128, 2 * 100 * 128, 100 * 128, 128, 512)
+    call = lambda *ts: lib.flexattn_quantize_qkv(*[ctypes.byref(t) for t in ts], None)
+    bad = FaTensor(256, fa.FA_I8, 1, 2, 100, 128, 2 * 100 * 128, 100 * 128, 128, None)
+    assert call(q, q, q, bad, q8, v8) == fa.FA_ERR_INVALID_ARG and "scale" in fa.flexattn_last_error()
+    assert call(q, q, q, q8, q8, q8) == fa.FA_ERR_INVALID_ARG and "dtype" in fa.flexattn_last_error()
+    d64 = FaTensor(256, fa.FA_BF16, 1, 2, 100, 64, 2 * 100 * 64, 100 * 64, 64, None)
+    assert call(d64, q, q, q8, q8, v8) == fa.FA_ERR_UNSUPPORTED
+    short = FaTensor(256, fa.FA_I8, 1, 2, 99, 128, 2 * 100 * 128, 100 * 128, 128, 512)
+    assert call(q, q, q, short, q8, v8) == fa.FA_ERR_INVALID_ARG and "shapes" in fa.flexattn_last_error()
