@@ -32,8 +32,10 @@ DEFAULT_WORKLOAD = "grouped_variate_4096g_bf16"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2516.6
 FP32_PEAK_TFLOPS = 157.3
+INT8_FP8_PEAK_TOPS = 5033.2  # dense int8 / fp8 MFMA (2x bf16)
 CPU_SAMPLE_BLOCKS = 6   # query blocks (x all heads) of the oracle timed on the host
 KERNEL_SOURCES = ["block_sparse_masked_blockmask_amd/csrc/fwd.hip",
+                  "block_sparse_masked_blockmask_amd/csrc/quant.hip",
                   "block_sparse_masked_blockmask_amd/csrc/device_common.h"]
 
 
@@ -60,7 +62,13 @@ def allowed_pairs(w) -> int:
     return total
 
 
-def algorithmic_bytes(w, bm) -> int:
+def algorithmic_bytes(w, bm, quantized=False) -> int:
+    """Bytes the forward must move once: Q, K, V (and scales), document ids and BlockMask lists
+    read; O and LSE written."""
+    if quantized:
+        qkvo = (w.B * w.Hq * w.Lq + 2 * w.B * w.Hkv * w.Lkv) * w.D + w.B * w.Hq * w.Lq * w.D * 2
+        scales = 4 * (w.B * w.Hq * -(-w.Lq // 128) + w.B * w.Hkv * -(-w.Lkv // 128) + w.B * w.Hkv * w.D)
+        return qkvo + scales + w.B * w.Hq * w.Lq * 4
     el = 2 if w.dtype == "bf16" else 4
     qkvo = (2 * w.B * w.Hq * w.Lq + 2 * w.B * w.Hkv * w.Lkv) * w.D * el
     lse = w.B * w.Hq * w.Lq * 4
@@ -81,7 +89,7 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload: str, launches_per_dispatch: float = 1.0):
+def read_traffic(workload: str):
     """HBM traffic per forward launch from the committed rocprofv3 counter summary, scaled by
     the copy-kernel calibration it records; None if absent or taken on other kernel sources."""
     path = os.path.join(ROOT, "profiles", f"fwd_{workload}_counters.md")
@@ -148,6 +156,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--kv-block", type=int, default=128)
+    ap.add_argument("--quantized", action="store_true",
+                    help="int8-QK / fp8-PV form (unmasked workloads): step = quantize + quantized forward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (HBM counter calibration for rocprofv3)")
@@ -193,6 +203,21 @@ def main():
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     gen_s = time.perf_counter() - t_gen
+    if args.quantized:
+        if mk or sk or w.dtype != "bf16":
+            print(json.dumps({"error": "the quantized form serves unmasked bf16 workloads only"}))
+            sys.exit(2)
+        qbufs = fa.flexattn_quantize_qkv(q, k, v, stream=stream)
+        bm = None
+
+    def step_quant(ev=None):
+        fa.flexattn_quantize_qkv(q, k, v, out=qbufs, stream=stream)
+        if ev is not None:
+            ev[0].record(stream)
+        fa.flexattn_fwd(qbufs["q8"], qbufs["k8"], qbufs["v8"], q_scale=qbufs["q_scale"], k_scale=qbufs["k_scale"],
+                        v_scale=qbufs["v_scale"], out=out, lse=lse, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
 
     def step(ev=None):
         fa.flexattn_block_mask_build(mk, w.B, w.Lq, w.Lkv, 128, args.kv_block, q_doc=qd, kv_doc=kd,
@@ -205,6 +230,8 @@ def main():
         if ev is not None:
             ev[1].record(stream)
 
+    if args.quantized:
+        step = step_quant  # noqa: F811
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -221,13 +248,15 @@ def main():
 
     pairs = allowed_pairs(w)
     flops = 4.0 * w.D * pairs * w.Hq
-    abytes = algorithmic_bytes(w, bm)
+    abytes = algorithmic_bytes(w, bm, args.quantized)
     value = flops / (ms_per_step * 1e-3) / 1e12
     fwd_tflops = flops / (fwd_avg_ms * 1e-3) / 1e12
     fwd_gbs = abytes / (fwd_avg_ms * 1e-3) / 1e9
     hbm_bound = (flops / abytes) < (BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9))
-    traffic = read_traffic(args.workload)
-    if w.dtype == "f32":
+    traffic = read_traffic(args.workload + ("_quantized" if args.quantized else ""))
+    if args.quantized:
+        roof = {"bound": "mfma", "achieved": fwd_tflops, "peak": INT8_FP8_PEAK_TOPS, "unit": "TFLOP/s"}
+    elif w.dtype == "f32":
         roof = {"bound": "mfma", "achieved": fwd_tflops, "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s"}
     elif hbm_bound:
         roof = {"bound": "hbm", "achieved": fwd_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
@@ -235,7 +264,7 @@ def main():
         roof = {"bound": "mfma", "achieved": fwd_tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = traffic
-    roof["kernel"] = "fwd_bf16_kernel" if w.dtype == "bf16" else "fwd_f32_kernel"
+    roof["kernel"] = "fwd_quant_kernel" if args.quantized else ("fwd_bf16_kernel" if w.dtype == "bf16" else "fwd_f32_kernel")
     roof["algorithmic_bytes"] = abytes
     roof["unmasked_flops"] = flops
     roof["avg_launch_ms"] = fwd_avg_ms
@@ -243,10 +272,11 @@ def main():
     rec = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded numpy PCG64)",
+        "vs_baseline": None, "dtype": "i8/fp8e4m3->bf16" if args.quantized else w.dtype,
+        "data": "synthetic (seeded numpy PCG64)",
         "config": {"workload": args.workload, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Lq": w.Lq, "Lkv": w.Lkv,
                    "D": w.D, "mask": mk, "score": sk, "q_block": 128, "kv_block": args.kv_block,
-                   "step": "block_mask_build + fwd"},
+                   "step": "quantize_qkv + fwd (int8 QK, fp8 PV)" if args.quantized else "block_mask_build + fwd"},
         "hbm_gbs": abytes / (ms_per_step * 1e-3) / 1e9,
         "fwd_only": {"ms": fwd_avg_ms, "tflops": fwd_tflops, "gbs": fwd_gbs},
         "roofline": roof,
