@@ -155,7 +155,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--kv-block", type=int, default=128)
+    ap.add_argument("--kv-block", type=int, default=None, help="BlockMask kv block (default 64 bf16, 128 f32)")
+    ap.add_argument("--q-block", type=int, default=None, help="BlockMask q block (default 128)")
     ap.add_argument("--quantized", action="store_true",
                     help="int8-QK / fp8-PV form (unmasked workloads): step = quantize + quantized forward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -184,6 +185,10 @@ def main():
 
     t_gen = time.perf_counter()
     w = make_workload(args.workload)
+    if args.q_block is None:
+        args.q_block = 128
+    if args.kv_block is None:
+        args.kv_block = 64 if w.dtype == "bf16" else 128
     mk = (fa.FA_MASK_DOC if w.doc else 0) | (fa.FA_MASK_CAUSAL if w.causal else 0) \
         | (fa.FA_MASK_WINDOW if w.window is not None else 0) | (fa.FA_MASK_PREFIX_LM if w.prefix_len is not None else 0)
     sk = (fa.FA_SCORE_ALIBI if w.alibi_slopes is not None else 0) | (fa.FA_SCORE_SOFTCAP if w.softcap else 0)
@@ -198,8 +203,8 @@ def main():
     kd = torch.from_numpy(w.kv_doc).to(dev) if w.doc else None
     out = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
-    bm = fa.BlockMask(w.B if w.doc else 1, 1, w.Lq, w.Lkv, 128, args.kv_block, dev)
-    ws_bytes = fa.flexattn_block_mask_workspace_bytes(mk, w.B, w.Lq, w.Lkv, 128, args.kv_block)
+    bm = fa.BlockMask(w.B if w.doc else 1, 1, w.Lq, w.Lkv, args.q_block, args.kv_block, dev)
+    ws_bytes = fa.flexattn_block_mask_workspace_bytes(mk, w.B, w.Lq, w.Lkv, args.q_block, args.kv_block)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     gen_s = time.perf_counter() - t_gen
@@ -220,7 +225,7 @@ def main():
             ev[1].record(stream)
 
     def step(ev=None):
-        fa.flexattn_block_mask_build(mk, w.B, w.Lq, w.Lkv, 128, args.kv_block, q_doc=qd, kv_doc=kd,
+        fa.flexattn_block_mask_build(mk, w.B, w.Lq, w.Lkv, args.q_block, args.kv_block, q_doc=qd, kv_doc=kd,
                                      window=w.window or 0, prefix_len=w.prefix_len or 0, out=bm,
                                      workspace=ws, stream=stream)
         if ev is not None:
@@ -275,7 +280,7 @@ def main():
         "vs_baseline": None, "dtype": "i8/fp8e4m3->bf16" if args.quantized else w.dtype,
         "data": "synthetic (seeded numpy PCG64)",
         "config": {"workload": args.workload, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Lq": w.Lq, "Lkv": w.Lkv,
-                   "D": w.D, "mask": mk, "score": sk, "q_block": 128, "kv_block": args.kv_block,
+                   "D": w.D, "mask": mk, "score": sk, "q_block": args.q_block, "kv_block": args.kv_block,
                    "step": "quantize_qkv + fwd (int8 QK, fp8 PV)" if args.quantized else "block_mask_build + fwd"},
         "hbm_gbs": abytes / (ms_per_step * 1e-3) / 1e9,
         "fwd_only": {"ms": fwd_avg_ms, "tflops": fwd_tflops, "gbs": fwd_gbs},

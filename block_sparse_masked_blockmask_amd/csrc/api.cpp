@@ -84,8 +84,10 @@ fa_status flexattn_block_mask_build(int mask_kind, const fa_params* p, int B, in
   if (out->q_len != q_len || out->kv_len != kv_len)
     return fail(FA_ERR_INVALID_ARG, "out->q_len/kv_len (%d, %d) differ from q_len/kv_len (%d, %d)",
                 out->q_len, out->kv_len, q_len, kv_len);
-  if ((out->q_block != 64 && out->q_block != 128) || (out->kv_block != 64 && out->kv_block != 128))
-    return fail(FA_ERR_UNSUPPORTED, "block sizes must be 64 or 128 (got %d x %d)", out->q_block, out->kv_block);
+  if ((out->q_block != 64 && out->q_block != 128 && out->q_block != 256) ||
+      (out->kv_block != 64 && out->kv_block != 128))
+    return fail(FA_ERR_UNSUPPORTED, "block sizes must be q 64/128/256 and kv 64/128 (got %d x %d)", out->q_block,
+                out->kv_block);
   if (out->n_qb != cdiv(q_len, out->q_block) || out->n_kvb != cdiv(kv_len, out->kv_block))
     return fail(FA_ERR_INVALID_ARG, "n_qb/n_kvb (%d, %d) do not match ceil(len / block)", out->n_qb, out->n_kvb);
   if (out->Hm != 1) return fail(FA_ERR_INVALID_ARG, "Hm must be 1: no mask flag depends on the head");
@@ -175,18 +177,22 @@ fa_status flexattn_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* 
     return fail(FA_ERR_INVALID_ARG, "SOFTCAP needs softcap > 0");
 
   const int B = q->B, Lq = q->L, Lkv = k->L;
-  int kv_block = 128;
+  int kv_block = 128, q_block = 128;
   fa::FwdArgs a{};
   if (bm == nullptr) {
     if (mask_kind != FA_MASK_NONE) return fail(FA_ERR_INVALID_ARG, "a BlockMask is required unless mask_kind is NONE");
+    // 256-query workgroups (bf16) once they still give at least one per CU.
+    if (dt == FA_BF16 && (int64_t)B * q->H * cdiv(Lq, 256) >= 256) q_block = 256;
     a.all_full = 1;
     a.Bm = a.Hm = 1;
-    a.nqb = cdiv(Lq, 128);
+    a.nqb = cdiv(Lq, q_block);
     a.nkvb = cdiv(Lkv, kv_block);
   } else {
     if (bm->q_len != Lq || bm->kv_len != Lkv)
       return fail(FA_ERR_INVALID_ARG, "BlockMask was built for lengths (%d, %d), not (%d, %d)", bm->q_len, bm->kv_len, Lq, Lkv);
-    if (bm->q_block != 128) return fail(FA_ERR_UNSUPPORTED, "q_block must be 128 (got %d)", bm->q_block);
+    if (bm->q_block != 128 && !(dt == FA_BF16 && bm->q_block == 256))
+      return fail(FA_ERR_UNSUPPORTED, "q_block must be 128 (or 256 for bf16) (got %d)", bm->q_block);
+    q_block = bm->q_block;
     if (bm->kv_block != 64 && bm->kv_block != 128)
       return fail(FA_ERR_UNSUPPORTED, "kv_block must be 64 or 128 (got %d)", bm->kv_block);
     if (bm->n_qb != cdiv(Lq, bm->q_block) || bm->n_kvb != cdiv(Lkv, bm->kv_block))
@@ -227,7 +233,7 @@ fa_status flexattn_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* 
   a.inv_softcap = (score_kind & FA_SCORE_SOFTCAP) ? 1.0f / p->softcap : 0.f;
   a.slopes = (score_kind & FA_SCORE_ALIBI) ? p->alibi_slopes : nullptr;
   a.total_wg = (int)total;
-  hipError_t e = fa::launch_fwd(a, dt == FA_BF16 ? 1 : 0, kv_block, score_kind, stream);
+  hipError_t e = fa::launch_fwd(a, dt == FA_BF16 ? 1 : 0, q_block, kv_block, score_kind, stream);
   if (e != hipSuccess) return fail(FA_ERR_DEVICE, "forward launch failed: %s", hipGetErrorString(e));
   return ok();
 }

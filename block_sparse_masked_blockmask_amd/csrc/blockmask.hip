@@ -123,7 +123,7 @@ __device__ __forceinline__ int classify_closed(const BlockMaskArgs& a, int q0, i
 __global__ __launch_bounds__(256) void bm_classify(BlockMaskArgs a) {
   const int qb = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  __shared__ int s_qdoc[128];
+  __shared__ int s_qdoc[256];
   __shared__ int s_kvdoc[128];
   __shared__ int s_amb[kChunk];
   __shared__ unsigned char s_res[kChunk];

@@ -20,6 +20,7 @@
 #include <hip/hip_runtime.h>
 
 #include <climits>
+#include <type_traits>
 
 #include "device_common.h"
 #include "launch.h"
@@ -97,14 +98,20 @@ __device__ __forceinline__ float score_log2(const FwdArgs& a, float acc, int qi,
 // ---------------------------------------------------------------------------------------------
 // bf16 kernel
 //
-// Keys are processed in steps of 64 (a 128-key BlockMask tile is two steps). K and V rows of a
-// step live in LDS (16 KB each, swizzled 16-byte chunks) in two buffers: while one step is
-// computed, the next step's K, V (and document ids) stream into the other buffer with
-// global_load_lds_dwordx4, which writes LDS directly without passing through registers. The two
-// buffers are distinct LDS objects selected at compile time (the step loop is unrolled by two):
-// the compiler then knows that reads of one buffer do not depend on the transfers into the
-// other and does not wait for them. BlockMask list entries are fetched two steps ahead.
-// At 64 KB of LDS and <= 256 VGPRs, two workgroups share a CU.
+// A workgroup of WAVES waves (4 or 8) owns 32 * WAVES queries; every wave owns 32. Keys are
+// processed in steps of 64 (a 128-key BlockMask tile is two steps). K and V rows of a step live
+// in LDS (16 KB each, swizzled 16-byte chunks) in NBUF ring buffers: while one step is
+// computed, the next NBUF - 1 steps' K, V and document ids stream into the other buffers with
+// global_load_lds_dwordx4, which writes LDS directly without passing through registers. The
+// buffers are distinct LDS objects selected at compile time (the step loop is unrolled NBUF
+// times): the compiler then knows that reads of one buffer do not depend on the transfers into
+// the others and does not wait for them. Every step issues the same fixed number of transfers
+// per wave (past the end they re-read row 0 into the buffer just released), so the wait for a
+// step's data is one s_waitcnt with a constant count. BlockMask list entries are read 64 at a
+// time into one register and picked out with readlane.
+//   WAVES = 4, NBUF = 2: 64 KB of LDS, two workgroups per CU (128-query BlockMask blocks);
+//   WAVES = 8, NBUF = 4: 128 KB of LDS, one workgroup per CU, three steps in flight
+//   (256-query BlockMask blocks; K/V reads are shared by twice the queries).
 //
 // Mask evaluation (partial tiles only). Causal, window and prefix-LM together allow, for a
 // query i, exactly one key interval [lo, hi): causal gives hi = i + 1, prefix-LM gives
@@ -130,12 +137,22 @@ __shared__ __attribute__((aligned(1024))) unsigned char g_k0[kStepBytes];
 __shared__ __attribute__((aligned(1024))) unsigned char g_v0[kStepBytes];
 __shared__ __attribute__((aligned(1024))) unsigned char g_k1[kStepBytes];
 __shared__ __attribute__((aligned(1024))) unsigned char g_v1[kStepBytes];
+__shared__ __attribute__((aligned(1024))) unsigned char g_k2[kStepBytes];
+__shared__ __attribute__((aligned(1024))) unsigned char g_v2[kStepBytes];
+__shared__ __attribute__((aligned(1024))) unsigned char g_k3[kStepBytes];
+__shared__ __attribute__((aligned(1024))) unsigned char g_v3[kStepBytes];
 __shared__ __attribute__((aligned(16))) int g_d0[kStep];
 __shared__ __attribute__((aligned(16))) int g_d1[kStep];
+__shared__ __attribute__((aligned(16))) int g_d2[kStep];
+__shared__ __attribute__((aligned(16))) int g_d3[kStep];
 
-template <int B> __device__ __forceinline__ unsigned char* kbuf() { return B ? g_k1 : g_k0; }
-template <int B> __device__ __forceinline__ unsigned char* vbuf() { return B ? g_v1 : g_v0; }
-template <int B> __device__ __forceinline__ int* dbuf() { return B ? g_d1 : g_d0; }
+template <int B> __device__ __forceinline__ unsigned char* kbuf() {
+  return B == 0 ? g_k0 : B == 1 ? g_k1 : B == 2 ? g_k2 : g_k3;
+}
+template <int B> __device__ __forceinline__ unsigned char* vbuf() {
+  return B == 0 ? g_v0 : B == 1 ? g_v1 : B == 2 ? g_v2 : g_v3;
+}
+template <int B> __device__ __forceinline__ int* dbuf() { return B == 0 ? g_d0 : B == 1 ? g_d1 : B == 2 ? g_d2 : g_d3; }
 
 __device__ __forceinline__ void dma16(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, 0);
@@ -143,17 +160,30 @@ __device__ __forceinline__ void dma16(const void* g, void* lds) {
 __device__ __forceinline__ void dma4(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 4, 0, 0);
 }
-// The compiler does not track the LDS writes of global_load_lds; wait for them explicitly.
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// The compiler does not track the LDS writes of global_load_lds; wait for them explicitly:
+// at most N vector-memory operations of this wave may still be outstanding.
+template <int N> __device__ __forceinline__ void wait_vmem() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
+// Minimum / maximum over each 32-lane half (both halves hold the same values here), returned
+// wave-uniform. ds_swizzle in bit mode exchanges lanes l and l ^ m inside 32-lane groups with
+// the pattern as an immediate (pattern = m << 10 | 0x1f), so no lane-index registers are needed.
+template <int M> __device__ __forceinline__ int swz_xor(int x) { return __builtin_amdgcn_ds_swizzle(x, (M << 10) | 0x1f); }
 __device__ __forceinline__ int wave_min32(int x) {
-#pragma unroll
-  for (int o = 16; o > 0; o >>= 1) x = min(x, __shfl_xor(x, o, 64));
+  x = min(x, swz_xor<16>(x));
+  x = min(x, swz_xor<8>(x));
+  x = min(x, swz_xor<4>(x));
+  x = min(x, swz_xor<2>(x));
+  x = min(x, swz_xor<1>(x));
   return __builtin_amdgcn_readfirstlane(x);
 }
 __device__ __forceinline__ int wave_max32(int x) {
-#pragma unroll
-  for (int o = 16; o > 0; o >>= 1) x = max(x, __shfl_xor(x, o, 64));
+  x = max(x, swz_xor<16>(x));
+  x = max(x, swz_xor<8>(x));
+  x = max(x, swz_xor<4>(x));
+  x = max(x, swz_xor<2>(x));
+  x = max(x, swz_xor<1>(x));
   return __builtin_amdgcn_readfirstlane(x);
 }
 
@@ -172,8 +202,8 @@ struct Ctx {
   float slope;
   const __bf16* kp;
   const __bf16* vp;
-  const int* kvdoc;
-  int koff, voff;        // element offset of this lane's 16-byte DMA chunk in segment 0 of a step
+  const int* kvdoc;      // document ids of this batch, or a valid dummy address without DOC
+  int koff, voff;        // element offset of this lane's 16-byte DMA chunk in its first segment
   // Byte offsets within a K or V step buffer of this lane's operand reads (swizzle applied):
   // kx[ks] for the K operand of k-step ks (row lq), vx[2*db + j] for the transposed V reads of
   // channel block db at rows base (j = 0) and base + 8 (j = 1). Other rows add 256 * rows.
@@ -185,24 +215,31 @@ struct State {
   float m_run, l_run;
 };
 
+// Transfers of one step: 16 one-KB segments per tensor (4 rows each), WAVES waves issue
+// 16 / WAVES of each, plus one transfer of document ids (64 / WAVES per wave). The count per
+// wave is therefore the same for every step: 2 * 16 / WAVES + 1.
+template <int WAVES> constexpr int step_ops() { return 2 * (16 / WAVES) + 1; }
+
 // Rows past the end are clamped to the last key: they hold finite data and are masked.
-template <int B>
+template <int B, int WAVES>
 __device__ __forceinline__ void issue_step(const FwdArgs& a, const Ctx& c, const StepInfo& si) {
+  constexpr int SEGS = 16 / WAVES;  // segments per wave and tensor
   const __bf16* kb = c.kp + (int64_t)si.kv0 * a.k_sl;
   const __bf16* vb = c.vp + (int64_t)si.kv0 * a.v_sl;
   if (si.kv0 + kStep <= a.Lkv) {
-    // Segment i*4 + wave holds rows 16*i + 4*wave + lane/16; the chunk swizzle depends on the
-    // row modulo 16 only, so segments differ by a whole number of 16-row strides.
+    // Segment i*WAVES + wave holds rows 4*(i*WAVES + wave) + lane/16; the chunk swizzle depends
+    // on the row modulo 16 only, and segments of one wave differ by 4*WAVES rows (a multiple
+    // of 16), so they share the lane's chunk offset.
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int seg = i * 4 + c.wave;  // 1 KB segment = 4 rows; lane writes 16 bytes at lane * 16
-      dma16(kb + (int64_t)(16 * i) * a.k_sl + c.koff, kbuf<B>() + seg * 1024);
-      dma16(vb + (int64_t)(16 * i) * a.v_sl + c.voff, vbuf<B>() + seg * 1024);
+    for (int i = 0; i < SEGS; ++i) {
+      const int seg = i * WAVES + c.wave;
+      dma16(kb + (int64_t)(4 * WAVES * i) * a.k_sl + c.koff, kbuf<B>() + seg * 1024);
+      dma16(vb + (int64_t)(4 * WAVES * i) * a.v_sl + c.voff, vbuf<B>() + seg * 1024);
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int seg = i * 4 + c.wave;
+    for (int i = 0; i < SEGS; ++i) {
+      const int seg = i * WAVES + c.wave;
       const int r = seg * 4 + (c.lane >> 4);
       const int ch = (c.lane & 15) ^ swz(r);
       const int64_t kv = min(si.kv0 + r, a.Lkv - 1);
@@ -210,7 +247,11 @@ __device__ __forceinline__ void issue_step(const FwdArgs& a, const Ctx& c, const
       dma16(c.vp + kv * a.v_sl + ch * 8, vbuf<B>() + seg * 1024);
     }
   }
-  if (c.doc && si.masked && c.wave == 0) dma4(c.kvdoc + min(si.kv0 + c.lane, a.Lkv - 1), dbuf<B>());
+  constexpr int IDS = kStep / WAVES;  // document ids per wave (lanes 0..IDS-1)
+  if (c.lane < IDS) {
+    const int* src = c.doc ? c.kvdoc + min(si.kv0 + c.wave * IDS + c.lane, a.Lkv - 1) : c.kvdoc;
+    dma4(src, dbuf<B>() + c.wave * IDS);
+  }
 }
 
 template <int B, int SCORE, bool MASKED>
@@ -229,6 +270,8 @@ __device__ __forceinline__ void compute_step(const FwdArgs& a, const Ctx& c, con
     vx[i] = c.vx[i];
     asm volatile("" : "+v"(kx[i]), "+v"(vx[i]));
   }
+  int dx = 4 * c.hl;  // element offset of this lane's document ids in a step (same reason)
+  asm volatile("" : "+v"(dx));
 
   // Live 32-key sub-blocks for this wave (wave-uniform).
   unsigned live = 3;
@@ -244,7 +287,9 @@ __device__ __forceinline__ void compute_step(const FwdArgs& a, const Ctx& c, con
       if (a.flags & FA_MASK_WINDOW) dead = dead || c.qw0 - k1 >= a.window;
       if (a.flags & FA_MASK_PREFIX_LM) dead = dead || (k0 >= a.prefix_len && c.qw1 < k0);
       if (c.doc && !dead) {
-        const int d = sD[min(nb * 32 + c.lq, k1 - kv0)];
+        // lq recovered from kx[0] (row lq times 256 plus a chunk offset below 256), which is live
+        // here; c.lq itself would be kept in a spilled register.
+        const int d = sD[min(nb * 32 + (kx[0] >> 8), k1 - kv0)];
         dead = wave_max32(d) < c.qd_min || wave_min32(d) > c.qd_max;
       }
       if (!dead) live |= 1u << nb;
@@ -290,7 +335,7 @@ __device__ __forceinline__ void compute_step(const FwdArgs& a, const Ctx& c, con
     for (int g = 0; g < 4; ++g) {
       i32x4 kd4 = i32x4{};
       if constexpr (MASKED) {
-        if (c.doc) kd4 = *(const i32x4*)(sD + (kbase - kv0) + g * 8);
+        if (c.doc) kd4 = *(const i32x4*)(sD + dx + nb * 32 + g * 8);
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -368,22 +413,18 @@ __device__ __forceinline__ void compute_step(const FwdArgs& a, const Ctx& c, con
   }
 }
 
-template <int B, int SCORE>
-__device__ __forceinline__ void run_step(const FwdArgs& a, const Ctx& c, const bf16x8 (&qreg)[8], State& st,
-                                         const StepInfo& cur) {
-  if (!cur.ok) return;
-  if (cur.masked) {
-    compute_step<B, SCORE, true>(a, c, qreg, st, cur.kv0);
-  } else {
-    compute_step<B, SCORE, false>(a, c, qreg, st, cur.kv0);
-  }
-}
+template <int TB, int WAVES, int NBUF>
+struct StepPlan {
+  static constexpr int HALVES = TB / kStep;  // steps per BlockMask tile
+};
 
 }  // namespace
 
-template <int TB, int SCORE>
-__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
-  constexpr int HALVES = TB / kStep;  // steps per BlockMask tile
+template <int TB, int SCORE, int WAVES, int NBUF>
+__global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(FwdArgs a) {
+  constexpr int HALVES = TB / kStep;
+  constexpr int BQ = 32 * WAVES;
+  constexpr int OPS = step_ops<WAVES>();
 
   const WorkItem it = decode_work(a);
   Ctx c;
@@ -393,14 +434,14 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   c.lq = c.lane & 31;
   c.g16 = c.lane >> 4;
   c.s16 = c.lane & 15;
-  c.qw0 = it.qb * kBQ + c.wave * 32;
+  c.qw0 = it.qb * BQ + c.wave * 32;
   c.qw1 = min(c.qw0 + 31, a.Lq - 1);
   c.qi = c.qw0 + c.lq;
   c.q_in = c.qi < a.Lq;
   c.doc = (a.flags & FA_MASK_DOC) != 0;
   c.kp = (const __bf16*)a.k + it.b * a.k_sb + it.hkv * a.k_sh;
   c.vp = (const __bf16*)a.v + it.b * a.v_sb + it.hkv * a.v_sh;
-  c.kvdoc = c.doc ? a.kv_doc + (int64_t)it.b * a.Lkv : nullptr;
+  c.kvdoc = c.doc ? a.kv_doc + (int64_t)it.b * a.Lkv : (const int*)c.kp;
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) c.kx[ks] = tile_off(c.lq, 2 * ks + c.hl);
 #pragma unroll
@@ -412,7 +453,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
     c.vx[2 * db + 1] = tile_off(r0 + 8, d >> 3) + (d & 7) * 2;
   }
   {
-    const int r = c.wave * 4 + (c.lane >> 4);  // row of this lane in segment 0 (of wave)
+    const int r = c.wave * 4 + (c.lane >> 4);  // row of this lane in its first segment
     const int ch = (c.lane & 15) ^ swz(r);
     c.koff = r * (int)a.k_sl + ch * 8;
     c.voff = r * (int)a.v_sl + ch * 8;
@@ -427,28 +468,18 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   }
 
   const TileList tl = tile_list(a, it);
-  const int nsteps = (tl.nfull + tl.npart) * HALVES;
-  // List entry of the tile of step s (one load, the same address in every lane).
-  auto entry = [&](int s) -> int {
-    const int t = s / HALVES;
-    if (a.all_full) return t;
+  const int ntiles = tl.nfull + tl.npart;
+  const int nsteps = ntiles * HALVES;
+
+  // List entries, 64 per register: lane j holds the entry of tile chunk_base + j. Loaded first,
+  // so that waiting for them leaves the Q loads below in flight.
+  auto load_chunk = [&](int base) -> int {
+    const int t = base + c.lane;
+    if (a.all_full || t >= ntiles) return t;
     return t < tl.nfull ? tl.full[t] : tl.part[t - tl.nfull];
   };
-  auto info = [&](int s, int kb) {
-    StepInfo si;
-    si.kv0 = kb * TB + (s % HALVES) * kStep;
-    // A corrupt index is skipped rather than read out of range; so is a half past the end.
-    si.ok = kb >= 0 && kb < a.nkvb && si.kv0 < a.Lkv;
-    si.masked = (s / HALVES >= tl.nfull) || (si.kv0 + kStep > a.Lkv);
-    return si;
-  };
-
-  StepInfo cur{0, false, false};
-  if (nsteps > 0) {
-    cur = info(0, __builtin_amdgcn_readfirstlane(entry(0)));
-    if (cur.ok) issue_step<0>(a, c, cur);
-  }
-  int e_next = nsteps > 1 ? entry(1) : 0;  // in flight until the first wait
+  int chunk_base = 0;
+  int chunk = load_chunk(0);
 
   // Q^T as the B operand: lane holds Q[qi][16*ks + 8*hl .. +8] for ks = 0..7.
   const __bf16* qp = (const __bf16*)a.q + it.b * a.q_sb + it.hq * a.q_sh;
@@ -457,12 +488,25 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   for (int ks = 0; ks < 8; ++ks)
     qreg[ks] = c.q_in ? *(const bf16x8*)(qp + (int64_t)c.qi * a.q_sl + ks * 16 + c.hl * 8) : bf16x8{};
   c.qdoc = (c.doc && c.q_in) ? a.q_doc[(int64_t)it.b * a.Lq + c.qi] : 0;
-  c.qd_min = c.qd_max = 0;
-  if (c.doc) {
-    c.qd_min = wave_min32(c.q_in ? c.qdoc : INT_MAX);
-    c.qd_max = wave_max32(c.q_in ? c.qdoc : INT_MIN);
-  }
   c.slope = (SCORE & FA_SCORE_ALIBI) ? a.slopes[it.hq] : 0.f;
+
+  // Step s -> StepInfo (steps past the end re-read row 0 and are not computed).
+  auto info = [&](int s) {
+    StepInfo si{0, false, false};
+    if (s >= nsteps) return si;
+    const int t = s / HALVES;
+    if (t >= chunk_base + 64) {  // next 64 list entries (once per 64 tiles)
+      chunk_base = t & ~63;
+      chunk = load_chunk(chunk_base);
+    }
+    const int kb = a.all_full ? t : __builtin_amdgcn_readlane(chunk, t - chunk_base);
+    // A corrupt index is skipped rather than read out of range; so is a half past the end.
+    const int kv0 = kb * TB + (s % HALVES) * kStep;
+    si.ok = kb >= 0 && kb < a.nkvb && kv0 < a.Lkv;
+    si.kv0 = si.ok ? kv0 : 0;
+    si.masked = (t >= tl.nfull) || (kv0 + kStep > a.Lkv);
+    return si;
+  };
 
   State st;
 #pragma unroll
@@ -470,29 +514,49 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   st.m_run = -INFINITY;
   st.l_run = 0.f;
 
-  // Two steps per iteration: even steps compute from buffer 0, odd steps from buffer 1.
-  for (int s = 0; s < nsteps; s += 2) {
-    {
-      wait_vmem();      // this wave's transfers for step s (and entry e_next) have landed
-      __syncthreads();  // all transfers landed; buffer 1 (step s-1) is no longer read
-      StepInfo nxt{0, false, false};
-      if (s + 1 < nsteps) nxt = info(s + 1, __builtin_amdgcn_readfirstlane(e_next));
-      if (nxt.ok) issue_step<1>(a, c, nxt);
-      if (s + 2 < nsteps) e_next = entry(s + 2);
-      run_step<0, SCORE>(a, c, qreg, st, cur);
-      cur = nxt;
-    }
-    if (s + 1 < nsteps) {
-      wait_vmem();
-      __syncthreads();
-      StepInfo nxt{0, false, false};
-      if (s + 2 < nsteps) nxt = info(s + 2, __builtin_amdgcn_readfirstlane(e_next));
-      if (nxt.ok) issue_step<0>(a, c, nxt);
-      if (s + 3 < nsteps) e_next = entry(s + 3);
-      run_step<1, SCORE>(a, c, qreg, st, cur);
-      cur = nxt;
+  // Prologue: steps 0 .. NBUF-2 in flight. Without any step (no key, or an empty BlockMask
+  // row) nothing is transferred at all: the padding transfers below need one valid key row.
+  StepInfo ring[NBUF];
+  if (nsteps > 0) {
+#pragma unroll
+    for (int j = 0; j < NBUF - 1; ++j) {
+      ring[j] = info(j);
+      if (j == 0) issue_step<0, WAVES>(a, c, ring[j]);
+      if (j == 1) issue_step<1, WAVES>(a, c, ring[j]);
+      if (j == 2) issue_step<2, WAVES>(a, c, ring[j]);
     }
   }
+  c.qd_min = c.qd_max = 0;
+  if (c.doc) {
+    c.qd_min = wave_min32(c.q_in ? c.qdoc : INT_MAX);
+    c.qd_max = wave_max32(c.q_in ? c.qdoc : INT_MIN);
+  }
+
+  // One step: wait for its transfers (NBUF-2 later steps may stay in flight), make sure every
+  // wave is done with the buffer about to be refilled, refill it with step s + NBUF - 1, compute.
+  auto step = [&](auto bufc, int s) {
+    constexpr int B = decltype(bufc)::value;
+    constexpr int NB = (B + NBUF - 1) % NBUF;
+    wait_vmem<(NBUF - 2) * OPS>();
+    __syncthreads();
+    const StepInfo nxt = info(s + NBUF - 1);
+    issue_step<NB, WAVES>(a, c, nxt);
+    const StepInfo cur = ring[B];
+    ring[NB] = nxt;
+    if (cur.ok) {
+      if (cur.masked) compute_step<B, SCORE, true>(a, c, qreg, st, cur.kv0);
+      else compute_step<B, SCORE, false>(a, c, qreg, st, cur.kv0);
+    }
+  };
+  for (int s = 0; s < nsteps; s += NBUF) {
+    step(std::integral_constant<int, 0>{}, s);
+    if (s + 1 < nsteps) step(std::integral_constant<int, 1 % NBUF>{}, s + 1);
+    if constexpr (NBUF > 2) {
+      if (s + 2 < nsteps) step(std::integral_constant<int, 2 % NBUF>{}, s + 2);
+      if (s + 3 < nsteps) step(std::integral_constant<int, 3 % NBUF>{}, s + 3);
+    }
+  }
+  wait_vmem<0>();  // no transfer may outlive the workgroup's LDS
 
   // Epilogue: combine the two halves' row sums, normalise, store O (bf16) and the natural-log lse.
   const float l_tot = half_swap_sum(st.l_run);
@@ -666,9 +730,12 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_kernel(FwdArgs a) {
 
 // ---------------------------------------------------------------------------------------------
 template <int BK, int SCORE>
-static hipError_t launch_t(const FwdArgs& a, int dtype, hipStream_t stream) {
+static hipError_t launch_t(const FwdArgs& a, int dtype, int q_block, hipStream_t stream) {
   if (dtype == 1) {
-    hipLaunchKernelGGL((fwd_bf16_kernel<BK, SCORE>), dim3(a.total_wg), dim3(256), 0, stream, a);
+    if (q_block == 256)
+      hipLaunchKernelGGL((fwd_bf16_kernel<BK, SCORE, 8, 4>), dim3(a.total_wg), dim3(512), 0, stream, a);
+    else
+      hipLaunchKernelGGL((fwd_bf16_kernel<BK, SCORE, 4, 2>), dim3(a.total_wg), dim3(256), 0, stream, a);
   } else {
     hipLaunchKernelGGL((fwd_f32_kernel<BK, SCORE>), dim3(a.total_wg), dim3(256), 0, stream, a);
   }
@@ -676,18 +743,19 @@ static hipError_t launch_t(const FwdArgs& a, int dtype, hipStream_t stream) {
 }
 
 template <int BK>
-static hipError_t launch_bk(const FwdArgs& a, int dtype, int score, hipStream_t stream) {
+static hipError_t launch_bk(const FwdArgs& a, int dtype, int q_block, int score, hipStream_t stream) {
   switch (score) {
-    case 0: return launch_t<BK, 0>(a, dtype, stream);
-    case FA_SCORE_ALIBI: return launch_t<BK, FA_SCORE_ALIBI>(a, dtype, stream);
-    case FA_SCORE_SOFTCAP: return launch_t<BK, FA_SCORE_SOFTCAP>(a, dtype, stream);
-    default: return launch_t<BK, FA_SCORE_ALIBI | FA_SCORE_SOFTCAP>(a, dtype, stream);
+    case 0: return launch_t<BK, 0>(a, dtype, q_block, stream);
+    case FA_SCORE_ALIBI: return launch_t<BK, FA_SCORE_ALIBI>(a, dtype, q_block, stream);
+    case FA_SCORE_SOFTCAP: return launch_t<BK, FA_SCORE_SOFTCAP>(a, dtype, q_block, stream);
+    default: return launch_t<BK, FA_SCORE_ALIBI | FA_SCORE_SOFTCAP>(a, dtype, q_block, stream);
   }
 }
 
-hipError_t launch_fwd(const FwdArgs& a, int dtype, int kv_block, int score, hipStream_t stream) {
+hipError_t launch_fwd(const FwdArgs& a, int dtype, int q_block, int kv_block, int score, hipStream_t stream) {
   if (a.total_wg == 0) return hipSuccess;
-  return kv_block == 64 ? launch_bk<64>(a, dtype, score, stream) : launch_bk<128>(a, dtype, score, stream);
+  return kv_block == 64 ? launch_bk<64>(a, dtype, q_block, score, stream)
+                        : launch_bk<128>(a, dtype, q_block, score, stream);
 }
 
 }  // namespace fa

@@ -80,7 +80,8 @@ struct QuantFwdArgs {
 hipError_t launch_block_mask(const BlockMaskArgs& a, hipStream_t stream);
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
 hipError_t launch_fwd_quant(const QuantFwdArgs& a, hipStream_t stream);
-// dtype 0 = f32, 1 = bf16; kv_block in {64, 128}; score bits FA_SCORE_*.
-hipError_t launch_fwd(const FwdArgs& a, int dtype, int kv_block, int score, hipStream_t stream);
+// dtype 0 = f32, 1 = bf16; q_block 128 (f32, bf16) or 256 (bf16); kv_block in {64, 128};
+// score bits FA_SCORE_*.
+hipError_t launch_fwd(const FwdArgs& a, int dtype, int q_block, int kv_block, int score, hipStream_t stream);
 
 }  // namespace fa

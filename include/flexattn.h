@@ -112,8 +112,8 @@ size_t flexattn_block_mask_workspace_bytes(int mask_kind, int B, int q_len, int 
  * partial or empty under mask_kind (guide, "Systems Mechanics" 1: create_block_mask evaluates
  * the mask over each block's bounding box). The caller fills `out`'s dimensions (Bm, Hm, q_len,
  * kv_len, q_block, kv_block, n_qb, n_kvb) and its four array pointers; Bm must be B when DOC is
- * set (1 or B otherwise), Hm must be 1 (no flag depends on the head). q_block and kv_block are
- * 64 or 128. Reads p->q_doc / p->kv_doc (DOC), p->window (WINDOW), p->prefix_len (PREFIX_LM).
+ * set (1 or B otherwise), Hm must be 1 (no flag depends on the head). q_block is 64, 128 or
+ * 256 and kv_block is 64 or 128. Reads p->q_doc / p->kv_doc (DOC), p->window (WINDOW), p->prefix_len (PREFIX_LM).
  * `workspace` must hold flexattn_block_mask_workspace_bytes(...) bytes (may be NULL if 0).
  * Classification is exact: the lists equal exhaustive evaluation of every in-range pair. */
 fa_status flexattn_block_mask_build(int mask_kind, const fa_params* p, int B, int q_len, int kv_len,
@@ -146,8 +146,9 @@ fa_status flexattn_quantize_qkv(const fa_tensor* q, const fa_tensor* k, const fa
  *   - Hq a multiple of Hkv (GQA: query head h reads kv head h / (Hq / Hkv));
  *   - data pointers 16-byte aligned and stride_b/h/l multiples of 8 elements (bf16) or
  *     4 elements (f32);
- *   - bm->q_block = 128 and bm->kv_block in {64, 128}.
- * `bm` may be NULL only when mask_kind is FA_MASK_NONE: every tile is then full.
+ *   - bm->q_block = 128, or 256 for bf16 (256-query workgroups), and bm->kv_block in {64, 128}.
+ * `bm` may be NULL only when mask_kind is FA_MASK_NONE: every tile is then full (bf16 uses
+ * 256-query workgroups when that still gives at least 256 of them).
  * The kernel trusts the BlockMask for which tiles to visit and evaluates mask_kind on partial
  * tiles (and on the ragged last kv block) only, like FlexAttention: a BlockMask built for a
  * different mask gives results for that mask's tile set.

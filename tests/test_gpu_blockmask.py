@@ -57,7 +57,8 @@ SPECS = [
 
 
 @pytest.mark.parametrize("si", range(len(SPECS)))
-@pytest.mark.parametrize("shape", [(2, 333, 333, 128, 128), (1, 700, 517, 64, 128), (2, 260, 390, 128, 64), (1, 64, 64, 64, 64)])
+@pytest.mark.parametrize("shape", [(2, 333, 333, 128, 128), (1, 700, 517, 64, 128), (2, 260, 390, 128, 64), (1, 64, 64, 64, 64),
+                                   (2, 600, 600, 256, 64), (1, 300, 700, 256, 128)])
 @pytest.mark.parametrize("ids", ["runs", "unsorted", "gapped"])
 def test_random_cases_bit_exact(si, shape, ids):
     """runs: packed documents with consecutive ids; unsorted: independent random ids;
@@ -92,7 +93,9 @@ def _spec_of(w):
 @pytest.mark.parametrize("name,bq,bk", [
     ("grouped_variate_4x17_f32", 128, 128),
     ("grouped_variate_4096g_bf16", 128, 128),
-    ("grouped_variate_4096g_bf16", 128, 64),
+    ("grouped_variate_4096g_bf16", 256, 64),
+    ("doc_causal_b4h16t8192_bf16", 256, 64),
+    ("swa1024_gqa32x8_softcap50_t16384_bf16", 256, 64),
     ("doc_causal_b4h16t8192_bf16", 128, 128),
     ("swa1024_gqa32x8_softcap50_t16384_bf16", 128, 128),
     ("dense_b1h32s24576_bf16", 128, 128),
@@ -110,7 +113,7 @@ def test_workload_block_masks(name, bq, bk):
         rows = [(b, qb) for b in range(Bm) for qb in range(nqb)]
     ref = ref_bm.block_mask(spec, w.B, w.Lq, w.Lkv, bq, bk, rows=rows)
     assert_same(got, ref, rows)
-    if name == "swa1024_gqa32x8_softcap50_t16384_bf16":
+    if name == "swa1024_gqa32x8_softcap50_t16384_bf16" and (bq, bk) == (128, 128):
         assert (int(got["full_kv_num_blocks"].sum()), int(got["kv_num_blocks"].sum())) == (868, 248)
     if name == "grouped_variate_4096g_bf16" and bk == 128:
         # Every row of the packed groups has only partial tiles (no group is tile-aligned).

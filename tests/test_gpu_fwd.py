@@ -42,7 +42,7 @@ def spec_of(w):
                 kv_doc=w.kv_doc, alibi_slopes=w.alibi_slopes, softcap=w.softcap)
 
 
-def run_gpu(w, kv_block=128, use_bm=True, lse=True):
+def run_gpu(w, kv_block=128, use_bm=True, lse=True, q_block=128):
     """Build the BlockMask and run the forward on the GPU; returns (out, lse, bm, tensors)."""
     import torch
     fa = _fa()
@@ -57,13 +57,16 @@ def run_gpu(w, kv_block=128, use_bm=True, lse=True):
     mk, sk = mask_kind(w), score_kind(w)
     bm = None
     if use_bm:
-        bm = fa.flexattn_block_mask_build(mk, w.B, w.Lq, w.Lkv, 128, kv_block, q_doc=qd, kv_doc=kd,
+        bm = fa.flexattn_block_mask_build(mk, w.B, w.Lq, w.Lkv, q_block, kv_block, q_doc=qd, kv_doc=kd,
                                           window=w.window or 0, prefix_len=w.prefix_len or 0, device=dev)
     out, l = fa.flexattn_fwd(q, k, v, bm, mk, sk, window=w.window or 0, prefix_len=w.prefix_len or 0,
                              softcap=w.softcap or 0.0, alibi_slopes=sl, q_doc=qd, kv_doc=kd, return_lse=lse)
     torch.cuda.synchronize()
     return out, l, bm
 
+
+# The BlockMask block sizes bench.py uses per dtype (q_block, kv_block).
+BENCH_BLOCKS = {"bf16": (128, 64), "f32": (128, 128)}
 
 CASES = [
     dict(),
@@ -89,11 +92,13 @@ def test_small_cases(ci, si, dtype):
     # Ragged lengths, Lq != Lkv only without self-attention-only structure, GQA 4:2.
     Lq, Lkv = (333, 333) if kw.get("doc") else (333, 401)
     w = random_case(10 * ci + si, dtype=dtype, B=2, Hq=4, Hkv=2, Lq=Lq, Lkv=Lkv, **kw)
-    for kvb in (128, 64):
-        out, lse, _ = run_gpu(w, kv_block=kvb)
-        qf, kf, vf = w.qkv_f32()
-        o_ref, l_ref = ref_attn.attention(qf, kf, vf, spec_of(w))
-        check_close(out.float().cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref, dtype, f"case {ci}/{si}/{dtype}/kv{kvb}")
+    qf, kf, vf = w.qkv_f32()
+    o_ref, l_ref = ref_attn.attention(qf, kf, vf, spec_of(w))
+    blocks = [(128, 128), (128, 64)] + ([(256, 64), (256, 128)] if dtype == "bf16" else [])
+    for qb, kvb in blocks:
+        out, lse, _ = run_gpu(w, kv_block=kvb, q_block=qb)
+        check_close(out.float().cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref, dtype,
+                    f"case {ci}/{si}/{dtype}/q{qb}/kv{kvb}")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -118,6 +123,15 @@ def test_fully_masked_rows_and_empty_rows(dtype):
     o_ref, l_ref = ref_attn.attention(qf, kf, vf, spec_of(w))
     o = out.float().cpu().numpy()
     l = lse.cpu().numpy()
+    if dtype == "bf16":  # the same with 256-query workgroups (a whole 256-query row empty)
+        w2 = random_case(503, dtype=dtype, B=1, Hq=2, Lq=600, Lkv=600, doc=True, n_docs=4, doc_sorted=False)
+        w2.q_doc = w2.q_doc.copy()
+        w2.q_doc[0, 256:512] = 77
+        out2, lse2, bm2 = run_gpu(w2, q_block=256, kv_block=64)
+        qf2, kf2, vf2 = w2.qkv_f32()
+        o_ref2, l_ref2 = ref_attn.attention(qf2, kf2, vf2, spec_of(w2))
+        assert int(bm2.kv_num_blocks[0, 0, 1]) == 0 and int(bm2.full_kv_num_blocks[0, 0, 1]) == 0
+        check_close(out2.float().cpu().numpy(), lse2.cpu().numpy(), o_ref2, l_ref2, dtype, "masked rows q256")
     assert np.all(o[0, :, 5] == 0) and np.all(np.isneginf(l[0, :, 5]))
     assert np.all(o[0, :, 256:] == 0) and np.all(np.isneginf(l[0, :, 256:]))
     assert int(bm.kv_num_blocks[0, 0, 2]) == 0 and int(bm.full_kv_num_blocks[0, 0, 2]) == 0
@@ -129,7 +143,7 @@ def test_gqa_ratios_and_strided_views():
     fa = _fa()
     for Hq, Hkv in [(8, 8), (8, 4), (8, 2), (8, 1)]:
         w = random_case(600 + Hq * 10 + Hkv, dtype="bf16", B=1, Hq=Hq, Hkv=Hkv, Lq=260, causal=True)
-        out, lse, _ = run_gpu(w)
+        out, lse, _ = run_gpu(w, q_block=256 if Hkv % 2 == 0 else 128, kv_block=64)
         qf, kf, vf = w.qkv_f32()
         o_ref, l_ref = ref_attn.attention(qf, kf, vf, spec_of(w))
         check_close(out.float().cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref, "bf16", f"gqa {Hq}/{Hkv}")
@@ -195,10 +209,13 @@ def _sample_rows(w, rng, n_heads=3, n_rows=96):
     "swa1024_gqa32x8_softcap50_t16384_bf16",
     "dense_b1h32s24576_bf16",
 ])
-def test_workloads_full_size(name):
-    print(f"workload {name}", flush=True)
+@pytest.mark.parametrize("blocks", ["bench", "128x128"])
+def test_workloads_full_size(name, blocks):
+    """blocks="bench": the launch configuration bench.py times (BENCH_BLOCKS); else 128x128."""
+    print(f"workload {name} blocks {blocks}", flush=True)
     w = make_workload(name)
-    out, lse, bm = run_gpu(w)
+    qb, kvb = (128, 128) if blocks != "bench" else BENCH_BLOCKS[w.dtype]
+    out, lse, bm = run_gpu(w, q_block=qb, kv_block=kvb)
     o = out.float().cpu().numpy()
     l = lse.cpu().numpy()
     del out, lse
