@@ -166,25 +166,31 @@ template <int N> __device__ __forceinline__ void wait_vmem() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Minimum / maximum over each 32-lane half (both halves hold the same values here), returned
-// wave-uniform. ds_swizzle in bit mode exchanges lanes l and l ^ m inside 32-lane groups with
-// the pattern as an immediate (pattern = m << 10 | 0x1f), so no lane-index registers are needed.
-template <int M> __device__ __forceinline__ int swz_xor(int x) { return __builtin_amdgcn_ds_swizzle(x, (M << 10) | 0x1f); }
+// Minimum / maximum over lanes 0..31 (both halves hold the same values where these are used),
+// returned wave-uniform. Data-parallel-primitive moves (DPP, a VALU operand modifier, no LDS
+// round trip) reduce each 16-lane row: quad_perm swaps of lanes l^1 and l^2, then the
+// half-row and row mirrors pair each 4- and 8-lane group with its partner; the two rows are
+// then combined in scalar registers.
+template <int CTRL> __device__ __forceinline__ int dpp(int x) {
+  return __builtin_amdgcn_update_dpp(x, x, CTRL, 0xf, 0xf, false);
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
 __device__ __forceinline__ int wave_min32(int x) {
-  x = min(x, swz_xor<16>(x));
-  x = min(x, swz_xor<8>(x));
-  x = min(x, swz_xor<4>(x));
-  x = min(x, swz_xor<2>(x));
-  x = min(x, swz_xor<1>(x));
-  return __builtin_amdgcn_readfirstlane(x);
+  x = min(x, dpp<kDppXor1>(x));
+  x = min(x, dpp<kDppXor2>(x));
+  x = min(x, dpp<kDppHalfMirror>(x));
+  x = min(x, dpp<kDppMirror>(x));
+  return min(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16));
 }
 __device__ __forceinline__ int wave_max32(int x) {
-  x = max(x, swz_xor<16>(x));
-  x = max(x, swz_xor<8>(x));
-  x = max(x, swz_xor<4>(x));
-  x = max(x, swz_xor<2>(x));
-  x = max(x, swz_xor<1>(x));
-  return __builtin_amdgcn_readfirstlane(x);
+  x = max(x, dpp<kDppXor1>(x));
+  x = max(x, dpp<kDppXor2>(x));
+  x = max(x, dpp<kDppHalfMirror>(x));
+  x = max(x, dpp<kDppMirror>(x));
+  return max(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16));
 }
 
 struct StepInfo {
@@ -290,7 +296,8 @@ __device__ __forceinline__ void compute_step(const FwdArgs& a, const Ctx& c, con
         // lq recovered from kx[0] (row lq times 256 plus a chunk offset below 256), which is live
         // here; c.lq itself would be kept in a spilled register.
         const int d = sD[min(nb * 32 + (kx[0] >> 8), k1 - kv0)];
-        dead = wave_max32(d) < c.qd_min || wave_min32(d) > c.qd_max;
+        const int dmax = wave_max32(d), dmin = wave_min32(d);
+        dead = (dmax < c.qd_min) | (dmin > c.qd_max);
       }
       if (!dead) live |= 1u << nb;
     }
@@ -428,7 +435,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(FwdArgs
 
   const WorkItem it = decode_work(a);
   Ctx c;
-  c.wave = threadIdx.x >> 6;
+  c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar registers
   c.lane = threadIdx.x & 63;
   c.hl = c.lane >> 5;
   c.lq = c.lane & 31;
