@@ -204,7 +204,6 @@ struct Ctx {
   int qw0, qw1, qi;
   bool q_in, doc;
   int qdoc, qd_min, qd_max;
-  int lo, hi;            // allowed key interval of this lane's query (index predicates + bounds)
   float slope;
   const __bf16* kp;
   const __bf16* vp;
@@ -260,7 +259,20 @@ __device__ __forceinline__ void issue_step(const FwdArgs& a, const Ctx& c, const
   }
 }
 
-template <int B, int SCORE, bool MASKED>
+// Allowed key interval [lo, hi) of query qi under the index predicates and the key count.
+__device__ __forceinline__ void key_interval(const FwdArgs& a, int qi, int& lo, int& hi) {
+  lo = INT_MIN / 2;
+  hi = a.Lkv;
+  if (a.flags & FA_MASK_CAUSAL) hi = min(hi, qi + 1);
+  if (a.flags & FA_MASK_PREFIX_LM) hi = min(hi, max(a.prefix_len, qi + 1));
+  if (a.flags & FA_MASK_WINDOW) lo = qi - a.window + 1;
+  hi = max(hi, lo);
+}
+
+// MASKED: evaluate the mask per score (partial tiles, ragged last step); DOC: the document
+// predicate is part of the mask (a compile-time choice, so that each score costs two compares
+// against inline constants, plus one id compare under DOC, and one select).
+template <int B, int SCORE, bool MASKED, bool DOC>
 __device__ __forceinline__ void compute_step(const FwdArgs& a, const Ctx& c, const bf16x8 (&qreg)[8], State& st,
                                              const int kv0) {
   const unsigned char* sK = kbuf<B>();
@@ -278,6 +290,11 @@ __device__ __forceinline__ void compute_step(const FwdArgs& a, const Ctx& c, con
   }
   int dx = 4 * c.hl;  // element offset of this lane's document ids in a step (same reason)
   asm volatile("" : "+v"(dx));
+  // This lane's query and its key interval, recomputed per step from the wave's first query
+  // (scalar) and the lane's row (kx[0] / 256): kept across the loop they would be spilled.
+  const int qi = c.qw0 + (kx[0] >> 8);
+  int lo = 0, hi = 0;
+  if constexpr (MASKED) key_interval(a, qi, lo, hi);
 
   // Live 32-key sub-blocks for this wave (wave-uniform).
   unsigned live = 3;
@@ -292,7 +309,7 @@ __device__ __forceinline__ void compute_step(const FwdArgs& a, const Ctx& c, con
       if (a.flags & FA_MASK_CAUSAL) dead = dead || c.qw1 < k0;
       if (a.flags & FA_MASK_WINDOW) dead = dead || c.qw0 - k1 >= a.window;
       if (a.flags & FA_MASK_PREFIX_LM) dead = dead || (k0 >= a.prefix_len && c.qw1 < k0);
-      if (c.doc && !dead) {
+      if (DOC && !dead) {
         // lq recovered from kx[0] (row lq times 256 plus a chunk offset below 256), which is live
         // here; c.lq itself would be kept in a spilled register.
         const int d = sD[min(nb * 32 + (kx[0] >> 8), k1 - kv0)];
@@ -333,25 +350,20 @@ __device__ __forceinline__ void compute_step(const FwdArgs& a, const Ctx& c, con
   for (int nb = 0; nb < 2; ++nb) {
     if (MASKED && !(live & (1u << nb))) continue;
     const int kbase = kv0 + nb * 32 + c.hl * 4;   // key of element i is kbase + (i/4)*8 + i%4
-    // kbase - lo, kept opaque so that the compiler does not hoist one loop-invariant register
-    // per element out of the step loop (it would otherwise spill).
-    int rel = kbase - c.lo;
-    asm volatile("" : "+v"(rel));
-    const unsigned span = (unsigned)(c.hi - c.lo);
+    // The allowed keys [lo, hi) relative to kbase: element offsets are the constants 0..27.
+    const int rlo = lo - kbase, rhi = hi - kbase;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       i32x4 kd4 = i32x4{};
-      if constexpr (MASKED) {
-        if (c.doc) kd4 = *(const i32x4*)(sD + dx + nb * 32 + g * 8);
-      }
+      if constexpr (MASKED && DOC) kd4 = *(const i32x4*)(sD + dx + nb * 32 + g * 8);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = g * 4 + e;
-        const int kv = kbase + g * 8 + e;
-        float x = SCORE == 0 ? sacc[nb][i] : score_log2<SCORE>(a, sacc[nb][i], c.qi, kv, c.slope);
+        const int off = g * 8 + e;
+        float x = SCORE == 0 ? sacc[nb][i] : score_log2<SCORE>(a, sacc[nb][i], qi, kbase + off, c.slope);
         if constexpr (MASKED) {
-          bool keep = (unsigned)(rel + g * 8 + e) < span;
-          if (c.doc) keep = keep && kd4[e] == c.qdoc;
+          bool keep = (rlo <= off) & (rhi > off);
+          if constexpr (DOC) keep = keep & (kd4[e] == c.qdoc);
           x = keep ? x : -INFINITY;
         }
         sacc[nb][i] = x;
@@ -465,36 +477,62 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(FwdArgs
     c.koff = r * (int)a.k_sl + ch * 8;
     c.voff = r * (int)a.v_sl + ch * 8;
   }
-  {
-    int lo = INT_MIN / 2, hi = a.Lkv;
-    if (a.flags & FA_MASK_CAUSAL) hi = min(hi, c.qi + 1);
-    if (a.flags & FA_MASK_PREFIX_LM) hi = min(hi, max(a.prefix_len, c.qi + 1));
-    if (a.flags & FA_MASK_WINDOW) lo = c.qi - a.window + 1;
-    c.lo = lo;
-    c.hi = max(hi, lo);
-  }
 
-  const TileList tl = tile_list(a, it);
+  int chunk_init;
+  // First-round loads, all issued before any of them is waited for (one memory round trip):
+  // this lane's Q row, its document id, the BlockMask counts and the first 64 entries of both
+  // index lists (the index rows always hold n_kvb entries, so no count is needed to read them).
+  // Addresses are clamped or redirected to valid memory instead of branching around the loads;
+  // the values are discarded afterwards where they do not apply.
+  // Q^T as the B operand: lane holds Q[qi][16*ks + 8*hl .. +8] for ks = 0..7.
+  const __bf16* qp = (const __bf16*)a.q + it.b * a.q_sb + it.hq * a.q_sh;
+  const int qi_c = min(c.qi, a.Lq - 1);
+  bf16x8 qreg[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) qreg[ks] = *(const bf16x8*)(qp + (int64_t)qi_c * a.q_sl + ks * 16 + c.hl * 8);
+  const int* qdoc_p = c.doc ? a.q_doc + (int64_t)it.b * a.Lq + qi_c : (const int*)qp;
+  const int qdoc_raw = *qdoc_p;
+  TileList tl;
+  {
+    const int bm = a.Bm == 1 ? 0 : it.b;
+    const int hm = a.Hm == 1 ? 0 : it.hq;
+    const int64_t row = ((int64_t)bm * a.Hm + hm) * a.nqb + it.qb;
+    // Without a BlockMask the list pointers are null, and with no key block (n_kvb = 0) the
+    // index rows are empty: the list reads then go to this head's first Q row (256 bytes, 64
+    // ints, always present when a workgroup runs) and are ignored.
+    const int* dummy = (const int*)qp;
+    const bool no_lists = a.all_full || a.nkvb == 0;
+    tl.full = no_lists ? dummy : a.full_idx + row * a.nkvb;
+    tl.part = no_lists ? dummy : a.kv_idx + row * a.nkvb;
+    const int fn = *(a.all_full ? dummy : a.full_num + row);
+    const int pn = *(a.all_full ? dummy : a.kv_num + row);
+    const int lc = max(min(c.lane, a.nkvb - 1), 0);  // in [0, 63] and inside the row
+    const int fch = tl.full[lc];
+    const int pch = tl.part[lc];
+    // Counts come from caller memory: clamp them so that a corrupt BlockMask cannot send the
+    // kernel outside the index arrays.
+    tl.nfull = a.all_full ? a.nkvb : min(max(fn, 0), a.nkvb);
+    tl.npart = a.all_full ? 0 : min(max(pn, 0), a.nkvb);
+    // Merge: entries of the full list, then of the partial list, with one cross-lane move.
+    const int pmv = __shfl(pch, (c.lane - tl.nfull) & 63, 64);
+    chunk_init = c.lane < tl.nfull ? fch : pmv;
+  }
+  if (!c.q_in) {
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qreg[ks] = bf16x8{};
+  }
+  c.qdoc = (c.doc && c.q_in) ? qdoc_raw : 0;
   const int ntiles = tl.nfull + tl.npart;
   const int nsteps = ntiles * HALVES;
 
-  // List entries, 64 per register: lane j holds the entry of tile chunk_base + j. Loaded first,
-  // so that waiting for them leaves the Q loads below in flight.
+  // List entries, 64 per register: lane j holds the entry of tile chunk_base + j.
   auto load_chunk = [&](int base) -> int {
     const int t = base + c.lane;
     if (a.all_full || t >= ntiles) return t;
     return t < tl.nfull ? tl.full[t] : tl.part[t - tl.nfull];
   };
   int chunk_base = 0;
-  int chunk = load_chunk(0);
-
-  // Q^T as the B operand: lane holds Q[qi][16*ks + 8*hl .. +8] for ks = 0..7.
-  const __bf16* qp = (const __bf16*)a.q + it.b * a.q_sb + it.hq * a.q_sh;
-  bf16x8 qreg[8];
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks)
-    qreg[ks] = c.q_in ? *(const bf16x8*)(qp + (int64_t)c.qi * a.q_sl + ks * 16 + c.hl * 8) : bf16x8{};
-  c.qdoc = (c.doc && c.q_in) ? a.q_doc[(int64_t)it.b * a.Lq + c.qi] : 0;
+  int chunk = chunk_init;
   c.slope = (SCORE & FA_SCORE_ALIBI) ? a.slopes[it.hq] : 0.f;
 
   // Step s -> StepInfo (steps past the end re-read row 0 and are not computed).
@@ -551,8 +589,9 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(FwdArgs
     const StepInfo cur = ring[B];
     ring[NB] = nxt;
     if (cur.ok) {
-      if (cur.masked) compute_step<B, SCORE, true>(a, c, qreg, st, cur.kv0);
-      else compute_step<B, SCORE, false>(a, c, qreg, st, cur.kv0);
+      if (!cur.masked) compute_step<B, SCORE, false, false>(a, c, qreg, st, cur.kv0);
+      else if (c.doc) compute_step<B, SCORE, true, true>(a, c, qreg, st, cur.kv0);
+      else compute_step<B, SCORE, true, false>(a, c, qreg, st, cur.kv0);
     }
   };
   for (int s = 0; s < nsteps; s += NBUF) {
