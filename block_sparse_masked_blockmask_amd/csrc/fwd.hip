@@ -209,11 +209,18 @@ struct Ctx {
   const __bf16* vp;
   const int* kvdoc;      // document ids of this batch, or a valid dummy address without DOC
   int koff, voff;        // element offset of this lane's 16-byte DMA chunk in its first segment
-  // Byte offsets within a K or V step buffer of this lane's operand reads (swizzle applied):
-  // kx[ks] for the K operand of k-step ks (row lq), vx[2*db + j] for the transposed V reads of
-  // channel block db at rows base (j = 0) and base + 8 (j = 1). Other rows add 256 * rows.
-  int kx[8], vx[8];
+  // Byte offsets within a K or V step buffer of this lane's first operand reads (swizzle
+  // applied): kx0 for the K operand of k-step 0 (row lq), vx0 for the transposed V read of
+  // channel block 0 at the lane's base row. The other reads follow by XOR (kx_at, vx_at).
+  int kx0, vx0;
 };
+
+// The swizzle's fields are disjoint bit ranges of the byte offset, so moving to another chunk
+// or row block is an XOR. K operand of k-step ks (chunk 2*ks + hl of row lq): the k-step sets
+// bits 5-7. Transposed V read of channel block db at base row + 8*j: db sets bits 6-7 of the
+// chunk field, and 8 more rows set bit 11 and flip chunk bit 1 (byte bit 5).
+__device__ __forceinline__ int kx_at(int kx0, int ks) { return kx0 ^ (32 * ks); }
+__device__ __forceinline__ int vx_at(int vx0, int db, int j) { return vx0 ^ (64 * db + 2080 * j); }
 
 struct State {
   f32x16 oacc[4];
@@ -225,22 +232,37 @@ struct State {
 // wave is therefore the same for every step: 2 * 16 / WAVES + 1.
 template <int WAVES> constexpr int step_ops() { return 2 * (16 / WAVES) + 1; }
 
-// Rows past the end are clamped to the last key: they hold finite data and are masked.
+// Transfer j (0 <= j < 2 * 16 / WAVES) of a step that ends inside the keys: segment j / 2 of K
+// (j even) or of V (j odd). Segment i*WAVES + wave holds rows 4*(i*WAVES + wave) + lane/16;
+// the chunk swizzle depends on the row modulo 16 only, and segments of one wave differ by
+// 4*WAVES rows (a multiple of 16), so they share the lane's chunk offset.
+template <int B, int WAVES>
+__device__ __forceinline__ void issue_seg(const FwdArgs& a, const Ctx& c, int kv0, int j) {
+  const int i = j >> 1;
+  const int seg = i * WAVES + c.wave;
+  if (j & 1)
+    dma16(c.vp + (int64_t)(kv0 + 4 * WAVES * i) * a.v_sl + c.voff, vbuf<B>() + seg * 1024);
+  else
+    dma16(c.kp + (int64_t)(kv0 + 4 * WAVES * i) * a.k_sl + c.koff, kbuf<B>() + seg * 1024);
+}
+// The step's document ids (one transfer; a valid dummy address without DOC).
+template <int B, int WAVES>
+__device__ __forceinline__ void issue_ids(const FwdArgs& a, const Ctx& c, int kv0) {
+  constexpr int IDS = kStep / WAVES;  // document ids per wave (lanes 0..IDS-1)
+  if (c.lane < IDS) {
+    const int* src = c.doc ? c.kvdoc + min(kv0 + c.wave * IDS + c.lane, a.Lkv - 1) : c.kvdoc;
+    dma4(src, dbuf<B>() + c.wave * IDS);
+  }
+}
+
+// All transfers of a step at once. Rows past the end are clamped to the last key: they hold
+// finite data and are masked.
 template <int B, int WAVES>
 __device__ __forceinline__ void issue_step(const FwdArgs& a, const Ctx& c, const StepInfo& si) {
   constexpr int SEGS = 16 / WAVES;  // segments per wave and tensor
-  const __bf16* kb = c.kp + (int64_t)si.kv0 * a.k_sl;
-  const __bf16* vb = c.vp + (int64_t)si.kv0 * a.v_sl;
   if (si.kv0 + kStep <= a.Lkv) {
-    // Segment i*WAVES + wave holds rows 4*(i*WAVES + wave) + lane/16; the chunk swizzle depends
-    // on the row modulo 16 only, and segments of one wave differ by 4*WAVES rows (a multiple
-    // of 16), so they share the lane's chunk offset.
 #pragma unroll
-    for (int i = 0; i < SEGS; ++i) {
-      const int seg = i * WAVES + c.wave;
-      dma16(kb + (int64_t)(4 * WAVES * i) * a.k_sl + c.koff, kbuf<B>() + seg * 1024);
-      dma16(vb + (int64_t)(4 * WAVES * i) * a.v_sl + c.voff, vbuf<B>() + seg * 1024);
-    }
+    for (int j = 0; j < 2 * SEGS; ++j) issue_seg<B, WAVES>(a, c, si.kv0, j);
   } else {
 #pragma unroll
     for (int i = 0; i < SEGS; ++i) {
@@ -252,11 +274,7 @@ __device__ __forceinline__ void issue_step(const FwdArgs& a, const Ctx& c, const
       dma16(c.vp + kv * a.v_sl + ch * 8, vbuf<B>() + seg * 1024);
     }
   }
-  constexpr int IDS = kStep / WAVES;  // document ids per wave (lanes 0..IDS-1)
-  if (c.lane < IDS) {
-    const int* src = c.doc ? c.kvdoc + min(si.kv0 + c.wave * IDS + c.lane, a.Lkv - 1) : c.kvdoc;
-    dma4(src, dbuf<B>() + c.wave * IDS);
-  }
+  issue_ids<B, WAVES>(a, c, si.kv0);
 }
 
 // Allowed key interval [lo, hi) of query qi under the index predicates and the key count.
@@ -272,27 +290,27 @@ __device__ __forceinline__ void key_interval(const FwdArgs& a, int qi, int& lo, 
 // MASKED: evaluate the mask per score (partial tiles, ragged last step); DOC: the document
 // predicate is part of the mask (a compile-time choice, so that each score costs two compares
 // against inline constants, plus one id compare under DOC, and one select).
-template <int B, int SCORE, bool MASKED, bool DOC>
+// ISSUE >= 0: this step also issues the transfers of the next step (which ends inside the keys,
+// kv0n) into buffer ISSUE, spread between its S products when both sub-blocks are live (a wave
+// is held while its transfers are accepted, and the memory pipeline accepts about 64 bytes per
+// cycle per CU, so issuing them back to back stalls every wave of the CU), else up front.
+template <int B, int SCORE, bool MASKED, bool DOC, int ISSUE, int WAVES>
 __device__ __forceinline__ void compute_step(const FwdArgs& a, const Ctx& c, const bf16x8 (&qreg)[8], State& st,
-                                             const int kv0) {
+                                             const int kv0, const int kv0n) {
+  constexpr int NSEG = 2 * (16 / WAVES);  // row transfers per wave and step
   const unsigned char* sK = kbuf<B>();
   const unsigned char* sV = vbuf<B>();
   const int* sD = dbuf<B>();
   // The offsets are re-defined here (no instruction is emitted) so that the compiler forms
   // buffer + offset inside the loop, where the buffer address folds into the instruction's
   // immediate offset, instead of keeping one hoisted register per buffer and offset.
-  int kx[8], vx[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    kx[i] = c.kx[i];
-    vx[i] = c.vx[i];
-    asm volatile("" : "+v"(kx[i]), "+v"(vx[i]));
-  }
+  int kx0 = c.kx0, vx0 = c.vx0;
+  asm volatile("" : "+v"(kx0), "+v"(vx0));
   int dx = 4 * c.hl;  // element offset of this lane's document ids in a step (same reason)
   asm volatile("" : "+v"(dx));
   // This lane's query and its key interval, recomputed per step from the wave's first query
-  // (scalar) and the lane's row (kx[0] / 256): kept across the loop they would be spilled.
-  const int qi = c.qw0 + (kx[0] >> 8);
+  // (scalar) and the lane's row (kx0 / 256): kept across the loop they would be spilled.
+  const int qi = c.qw0 + (kx0 >> 8);
   int lo = 0, hi = 0;
   if constexpr (MASKED) key_interval(a, qi, lo, hi);
 
@@ -310,28 +328,55 @@ __device__ __forceinline__ void compute_step(const FwdArgs& a, const Ctx& c, con
       if (a.flags & FA_MASK_WINDOW) dead = dead || c.qw0 - k1 >= a.window;
       if (a.flags & FA_MASK_PREFIX_LM) dead = dead || (k0 >= a.prefix_len && c.qw1 < k0);
       if (DOC && !dead) {
-        // lq recovered from kx[0] (row lq times 256 plus a chunk offset below 256), which is live
+        // lq recovered from kx0 (row lq times 256 plus a chunk offset below 256), which is live
         // here; c.lq itself would be kept in a spilled register.
-        const int d = sD[min(nb * 32 + (kx[0] >> 8), k1 - kv0)];
+        const int d = sD[min(nb * 32 + (kx0 >> 8), k1 - kv0)];
         const int dmax = wave_max32(d), dmin = wave_min32(d);
         dead = (dmax < c.qd_min) | (dmin > c.qd_max);
       }
       if (!dead) live |= 1u << nb;
     }
     live = __builtin_amdgcn_readfirstlane(live);
-    if (!live) return;
   }
 
   // S^T = K Q^T for the live 32-key sub-blocks.
   f32x16 sacc[2];
+  if (ISSUE >= 0 && live == 3u) {
+    // Both sub-blocks: the two product chains alternate, and one transfer of the next step
+    // follows each pair of products.
+    issue_ids<(ISSUE < 0 ? 0 : ISSUE), WAVES>(a, c, kv0n);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const bf16x8 kf = *(const bf16x8*)(sK + nb * 32 * 256 + kx_at(kx0, ks));
+        sacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[ks], ks ? sacc[nb] : f32x16{}, 0, 0, 0);
+      }
+      if (ks < NSEG) issue_seg<(ISSUE < 0 ? 0 : ISSUE), WAVES>(a, c, kv0n, ks);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (ks < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (ks < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (ks < NSEG) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+  } else {
+    if constexpr (ISSUE >= 0) {
+      StepInfo nx{kv0n, true, false};
+      issue_step<ISSUE, WAVES>(a, c, nx);
+    }
+    if (MASKED && !live) return;
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     if (MASKED && !(live & (1u << nb))) continue;
-    sacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(sK + nb * 32 * 256 + kx[0]), qreg[0],
+    sacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(sK + nb * 32 * 256 + kx0), qreg[0],
                                                        f32x16{}, 0, 0, 0);
 #pragma unroll
     for (int ks = 1; ks < 8; ++ks) {
-      const bf16x8 kf = *(const bf16x8*)(sK + nb * 32 * 256 + kx[ks]);
+      const bf16x8 kf = *(const bf16x8*)(sK + nb * 32 * 256 + kx_at(kx0, ks));
       sacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[ks], sacc[nb], 0, 0, 0);
     }
     // Schedule: 4 operand reads ahead, then one read per product (bounds live operands).
@@ -341,6 +386,7 @@ __device__ __forceinline__ void compute_step(const FwdArgs& a, const Ctx& c, con
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       if (k < 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
+  }
   }
 
   // Scores (log2 domain) and the mask. Without a score_mod the 1/sqrt(d) * log2(e) scale is
@@ -411,8 +457,8 @@ __device__ __forceinline__ void compute_step(const FwdArgs& a, const Ctx& c, con
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int rows = (nb * 32 + h * 16) * 256;  // the swizzle depends on the row modulo 16
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sV + rows + vx[2 * db]));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sV + rows + vx[2 * db + 1]));
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sV + rows + vx_at(vx0, db, 0)));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sV + rows + vx_at(vx0, db, 1)));
         // Whole-vector concatenation and bit cast (element-wise bf16 inserts of the i16 lanes
         // were observed to be folded into a broadcast of element 0).
         const i16x8 cat = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -461,15 +507,12 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(FwdArgs
   c.kp = (const __bf16*)a.k + it.b * a.k_sb + it.hkv * a.k_sh;
   c.vp = (const __bf16*)a.v + it.b * a.v_sb + it.hkv * a.v_sh;
   c.kvdoc = c.doc ? a.kv_doc + (int64_t)it.b * a.Lkv : (const int*)c.kp;
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks) c.kx[ks] = tile_off(c.lq, 2 * ks + c.hl);
-#pragma unroll
-  for (int db = 0; db < 4; ++db) {
+  c.kx0 = tile_off(c.lq, c.hl);
+  {
     // In each 16-lane group, source lane s points at key row base + s/4, channels d0 + 4*(s%4).
-    const int d = db * 32 + 16 * (c.g16 & 1) + 4 * (c.s16 & 3);
+    const int d = 16 * (c.g16 & 1) + 4 * (c.s16 & 3);
     const int r0 = (c.g16 >> 1) * 4 + (c.s16 >> 2);
-    c.vx[2 * db] = tile_off(r0, d >> 3) + (d & 7) * 2;
-    c.vx[2 * db + 1] = tile_off(r0 + 8, d >> 3) + (d & 7) * 2;
+    c.vx0 = tile_off(r0, d >> 3) + (d & 7) * 2;
   }
   {
     const int r = c.wave * 4 + (c.lane >> 4);  // row of this lane in its first segment
@@ -585,13 +628,20 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(FwdArgs
     wait_vmem<(NBUF - 2) * OPS>();
     __syncthreads();
     const StepInfo nxt = info(s + NBUF - 1);
-    issue_step<NB, WAVES>(a, c, nxt);
     const StepInfo cur = ring[B];
     ring[NB] = nxt;
-    if (cur.ok) {
-      if (!cur.masked) compute_step<B, SCORE, false, false>(a, c, qreg, st, cur.kv0);
-      else if (c.doc) compute_step<B, SCORE, true, true>(a, c, qreg, st, cur.kv0);
-      else compute_step<B, SCORE, true, false>(a, c, qreg, st, cur.kv0);
+    if (cur.ok && nxt.kv0 + kStep <= a.Lkv) {
+      // The step's own compute issues the next step's transfers.
+      if (!cur.masked) compute_step<B, SCORE, false, false, NB, WAVES>(a, c, qreg, st, cur.kv0, nxt.kv0);
+      else if (c.doc) compute_step<B, SCORE, true, true, NB, WAVES>(a, c, qreg, st, cur.kv0, nxt.kv0);
+      else compute_step<B, SCORE, true, false, NB, WAVES>(a, c, qreg, st, cur.kv0, nxt.kv0);
+    } else {
+      issue_step<NB, WAVES>(a, c, nxt);
+      if (cur.ok) {
+        if (!cur.masked) compute_step<B, SCORE, false, false, -1, WAVES>(a, c, qreg, st, cur.kv0, 0);
+        else if (c.doc) compute_step<B, SCORE, true, true, -1, WAVES>(a, c, qreg, st, cur.kv0, 0);
+        else compute_step<B, SCORE, true, false, -1, WAVES>(a, c, qreg, st, cur.kv0, 0);
+      }
     }
   };
   for (int s = 0; s < nsteps; s += NBUF) {
