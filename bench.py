@@ -240,13 +240,21 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    # Timed region: exactly K steps, bracketed by device synchronisation. It records no events:
+    # on this platform each timing event costs about 10 us of the step (measured), so the
+    # forward's own duration is taken in a second pass of K identical steps with HIP events
+    # around every forward launch, on the stream the kernels are launched on.
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(events[i])
+        step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
     fwd_ms = [a.elapsed_time(b) for a, b in events]
     fwd_avg_ms = float(np.mean(fwd_ms))
     ms_per_step = wall * 1e3 / args.steps

@@ -2,14 +2,18 @@
 // on the host before anything is enqueued, so a non-OK status never leaves partial writes.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
 #include <string>
 
+#include <vector>
+
 #include "flexattn.h"
 #include "launch.h"
+#include "tile_class.h"
 
 namespace {
 
@@ -50,6 +54,32 @@ fa_status check_mask(int mask_kind, const fa_params* p, int Lq, int Lkv) {
   return FA_OK;
 }
 
+// Checks of a BlockMask build request shared by the device and host builders.
+fa_status check_build(int mask_kind, const fa_params* p, int B, int q_len, int kv_len, const fa_block_mask* out) {
+  fa_status st = check_mask(mask_kind, p, q_len, kv_len);
+  if (st != FA_OK) return st;
+  if (out == nullptr) return fail(FA_ERR_INVALID_ARG, "out is NULL");
+  if (B <= 0 || B > 65535) return fail(FA_ERR_INVALID_ARG, "B must be in [1, 65535] (got %d)", B);
+  if (q_len < 0 || kv_len < 0) return fail(FA_ERR_INVALID_ARG, "negative sequence length");
+  if (out->q_len != q_len || out->kv_len != kv_len)
+    return fail(FA_ERR_INVALID_ARG, "out->q_len/kv_len (%d, %d) differ from q_len/kv_len (%d, %d)",
+                out->q_len, out->kv_len, q_len, kv_len);
+  if ((out->q_block != 64 && out->q_block != 128 && out->q_block != 256) ||
+      (out->kv_block != 64 && out->kv_block != 128))
+    return fail(FA_ERR_UNSUPPORTED, "block sizes must be q 64/128/256 and kv 64/128 (got %d x %d)", out->q_block,
+                out->kv_block);
+  if (out->n_qb != cdiv(q_len, out->q_block) || out->n_kvb != cdiv(kv_len, out->kv_block))
+    return fail(FA_ERR_INVALID_ARG, "n_qb/n_kvb (%d, %d) do not match ceil(len / block)", out->n_qb, out->n_kvb);
+  if (out->Hm != 1) return fail(FA_ERR_INVALID_ARG, "Hm must be 1: no mask flag depends on the head");
+  if ((mask_kind & FA_MASK_DOC) ? out->Bm != B : (out->Bm != 1 && out->Bm != B))
+    return fail(FA_ERR_INVALID_ARG, "Bm must be B with DOC, else 1 or B (got %d)", out->Bm);
+  if (out->n_qb > 0 && (!out->kv_num_blocks || !out->full_kv_num_blocks))
+    return fail(FA_ERR_INVALID_ARG, "BlockMask count arrays are NULL");
+  if (out->n_qb > 0 && out->n_kvb > 0 && (!out->kv_indices || !out->full_kv_indices))
+    return fail(FA_ERR_INVALID_ARG, "BlockMask index arrays are NULL");
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -76,27 +106,8 @@ size_t flexattn_block_mask_workspace_bytes(int mask_kind, int B, int q_len, int 
 fa_status flexattn_block_mask_build(int mask_kind, const fa_params* p, int B, int q_len, int kv_len,
                                     fa_block_mask* out, void* workspace, size_t workspace_bytes,
                                     hipStream_t stream) {
-  fa_status st = check_mask(mask_kind, p, q_len, kv_len);
+  fa_status st = check_build(mask_kind, p, B, q_len, kv_len, out);
   if (st != FA_OK) return st;
-  if (out == nullptr) return fail(FA_ERR_INVALID_ARG, "out is NULL");
-  if (B <= 0 || B > 65535) return fail(FA_ERR_INVALID_ARG, "B must be in [1, 65535] (got %d)", B);
-  if (q_len < 0 || kv_len < 0) return fail(FA_ERR_INVALID_ARG, "negative sequence length");
-  if (out->q_len != q_len || out->kv_len != kv_len)
-    return fail(FA_ERR_INVALID_ARG, "out->q_len/kv_len (%d, %d) differ from q_len/kv_len (%d, %d)",
-                out->q_len, out->kv_len, q_len, kv_len);
-  if ((out->q_block != 64 && out->q_block != 128 && out->q_block != 256) ||
-      (out->kv_block != 64 && out->kv_block != 128))
-    return fail(FA_ERR_UNSUPPORTED, "block sizes must be q 64/128/256 and kv 64/128 (got %d x %d)", out->q_block,
-                out->kv_block);
-  if (out->n_qb != cdiv(q_len, out->q_block) || out->n_kvb != cdiv(kv_len, out->kv_block))
-    return fail(FA_ERR_INVALID_ARG, "n_qb/n_kvb (%d, %d) do not match ceil(len / block)", out->n_qb, out->n_kvb);
-  if (out->Hm != 1) return fail(FA_ERR_INVALID_ARG, "Hm must be 1: no mask flag depends on the head");
-  if ((mask_kind & FA_MASK_DOC) ? out->Bm != B : (out->Bm != 1 && out->Bm != B))
-    return fail(FA_ERR_INVALID_ARG, "Bm must be B with DOC, else 1 or B (got %d)", out->Bm);
-  if (out->n_qb > 0 && (!out->kv_num_blocks || !out->full_kv_num_blocks))
-    return fail(FA_ERR_INVALID_ARG, "BlockMask count arrays are NULL");
-  if (out->n_qb > 0 && out->n_kvb > 0 && (!out->kv_indices || !out->full_kv_indices))
-    return fail(FA_ERR_INVALID_ARG, "BlockMask index arrays are NULL");
   const size_t need = flexattn_block_mask_workspace_bytes(mask_kind, B, q_len, kv_len, out->q_block, out->kv_block);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need))
     return fail(FA_ERR_INVALID_ARG, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
@@ -124,6 +135,73 @@ fa_status flexattn_block_mask_build(int mask_kind, const fa_params* p, int B, in
   a.full_idx = out->full_kv_indices;
   hipError_t e = fa::launch_block_mask(a, stream);
   if (e != hipSuccess) return fail(FA_ERR_DEVICE, "block mask launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+fa_status flexattn_block_mask_build_host(int mask_kind, const fa_params* p, int B, int q_len, int kv_len,
+                                         fa_block_mask* out) {
+  fa_status st = check_build(mask_kind, p, B, q_len, kv_len, out);
+  if (st != FA_OK) return st;
+  const int flags = mask_kind;
+  const int window = (mask_kind & FA_MASK_WINDOW) ? p->window : 0;
+  const int prefix_len = (mask_kind & FA_MASK_PREFIX_LM) ? p->prefix_len : 0;
+  const bool doc = (mask_kind & FA_MASK_DOC) != 0;
+  const int BQ = out->q_block, BK = out->kv_block, nqb = out->n_qb, nkvb = out->n_kvb;
+  // Per-block document-id summaries of one batch: [min, max, dense] (see tile_class.h).
+  auto summarise = [](const int32_t* ids, int L, int blk, int n, std::vector<int>& sum) {
+    sum.assign((size_t)3 * n, 0);
+    for (int x = 0; x < n; ++x) {
+      const int lo = x * blk, hi = std::min(L, lo + blk);
+      int mn = ids[lo], mx = ids[lo], dense = 1;
+      for (int i = lo + 1; i < hi; ++i) {
+        mn = std::min(mn, ids[i]);
+        mx = std::max(mx, ids[i]);
+        const int inc = ids[i] - ids[i - 1];
+        if (inc != 0 && inc != 1) dense = 0;
+      }
+      sum[3 * x] = mn;
+      sum[3 * x + 1] = mx;
+      sum[3 * x + 2] = dense;
+    }
+  };
+  std::vector<int> qs, ks;
+  for (int bm = 0; bm < out->Bm; ++bm) {
+    const int b = out->Bm == B ? bm : 0;  // without DOC no predicate depends on the batch
+    const int32_t* qd = doc ? p->q_doc + (size_t)b * q_len : nullptr;
+    const int32_t* kd = doc ? p->kv_doc + (size_t)b * kv_len : nullptr;
+    if (doc) {
+      summarise(qd, q_len, BQ, nqb, qs);
+      summarise(kd, kv_len, BK, nkvb, ks);
+    }
+    for (int qb = 0; qb < nqb; ++qb) {
+      const size_t row = (size_t)bm * nqb + qb;  // Hm = 1
+      int32_t* full = out->full_kv_indices + row * nkvb;
+      int32_t* part = out->kv_indices + row * nkvb;
+      const int q0 = qb * BQ, q1 = std::min(q_len, q0 + BQ);
+      int nf = 0, np = 0;
+      for (int kb = 0; kb < nkvb; ++kb) {
+        const int k0 = kb * BK, k1 = std::min(kv_len, k0 + BK);
+        int cls = fa::classify_closed(flags, window, prefix_len, q0, q1, k0, k1, doc ? qs[3 * qb] : 0,
+                                      doc ? qs[3 * qb + 1] : 0, doc ? qs[3 * qb + 2] : 0, doc ? ks[3 * kb] : 0,
+                                      doc ? ks[3 * kb + 1] : 0, doc ? ks[3 * kb + 2] : 0);
+        if (cls == 3) {  // every in-range pair, until one is allowed
+          cls = 0;
+          for (int i = q0; i < q1 && !cls; ++i)
+            for (int j = k0; j < k1; ++j)
+              if (fa::mask_pair_flags(flags, window, prefix_len, i, j, doc ? qd[i] : 0, doc ? kd[j] : 0)) {
+                cls = 1;
+                break;
+              }
+        }
+        if (cls == 2) full[nf++] = kb;
+        if (cls == 1) part[np++] = kb;
+      }
+      for (int j = nf; j < nkvb; ++j) full[j] = 0;
+      for (int j = np; j < nkvb; ++j) part[j] = 0;
+      out->full_kv_num_blocks[row] = nf;
+      out->kv_num_blocks[row] = np;
+    }
+  }
   return ok();
 }
 

@@ -17,6 +17,7 @@
 
 #include "device_common.h"
 #include "launch.h"
+#include "tile_class.h"
 
 namespace fa {
 
@@ -81,45 +82,6 @@ __global__ __launch_bounds__(256) void bm_summaries(BlockMaskArgs a) {
   }
 }
 
-// Class codes: 0 empty, 1 partial, 2 full, 3 undecided by closed forms.
-__device__ __forceinline__ int classify_closed(const BlockMaskArgs& a, int q0, int q1, int k0, int k1,
-                                               int qmin, int qmax, int qdense, int kmin, int kmax, int kdense) {
-  const int dmin = q0 - (k1 - 1), dmax = (q1 - 1) - k0;  // range of q - kv over the box
-  bool all = true, none = false;
-  if (a.flags & FA_MASK_CAUSAL) {
-    all = all && dmin >= 0;
-    none = none || dmax < 0;
-  }
-  if (a.flags & FA_MASK_WINDOW) {
-    all = all && dmax < a.window;
-    none = none || dmin >= a.window;
-  }
-  if (a.flags & FA_MASK_PREFIX_LM) {
-    all = all && ((k1 - 1 < a.prefix_len) || dmin >= 0);
-    none = none || (k0 >= a.prefix_len && dmax < 0);
-  }
-  const bool index_all = all;
-  if (a.flags & FA_MASK_DOC) {
-    all = all && (qmin == qmax && kmin == kmax && qmin == kmin);
-    none = none || (qmax < kmin || kmax < qmin);
-  }
-  if (all) return 2;
-  if (none) return 0;
-  if (!(a.flags & FA_MASK_DOC)) {
-    // Causal and window together allow exactly the pairs with q - kv in [0, window): the box's
-    // q - kv values form one integer interval, and each predicate alone was not all-false, so
-    // the interval meets [0, window) and some pair is allowed. Prefix-LM alone is one
-    // predicate that is not all-false.
-    if (!(a.flags & FA_MASK_PREFIX_LM)) return 1;
-    if (!(a.flags & FA_MASK_WINDOW)) return 1;
-    return 3;
-  }
-  // Document ids with every index predicate true on the whole box: the tile is non-empty iff
-  // the blocks share an id, which dense blocks with overlapping ranges do.
-  if (index_all && qdense && kdense) return 1;
-  return 3;
-}
-
 __global__ __launch_bounds__(256) void bm_classify(BlockMaskArgs a) {
   const int qb = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -169,7 +131,8 @@ __global__ __launch_bounds__(256) void bm_classify(BlockMaskArgs a) {
       cls[j] = -1;
       if (kb < a.nkvb) {
         const int k0 = kb * a.BK, k1 = min(a.Lkv, k0 + a.BK);
-        cls[j] = classify_closed(a, q0, q1, k0, k1, qmin, qmax, qdense, kmn[j], kmx[j], kdn[j]);
+        cls[j] = classify_closed(a.flags, a.window, a.prefix_len, q0, q1, k0, k1, qmin, qmax, qdense, kmn[j],
+                                 kmx[j], kdn[j]);
         if (cls[j] == 3) s_amb[atomicAdd(&s_namb, 1)] = tid * kPerThread + j;
       }
     }

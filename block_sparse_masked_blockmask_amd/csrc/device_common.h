@@ -4,6 +4,7 @@
 #include <stdint.h>
 
 #include "flexattn.h"
+#include "tile_class.h"
 
 namespace fa {
 
@@ -18,9 +19,8 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// mask_mod for one (query, key) pair: the AND of the enabled predicates on absolute
-// positions (FlexAttention guide: causal and window from the "Implementation" demo, the
-// document and prefix-LM masks from "Production Engineering"). Flags are wave-uniform.
+// mask_mod for one (query, key) pair (the predicate itself is mask_pair_flags in tile_class.h).
+// Flags are wave-uniform.
 struct MaskSpec {
   int flags;
   int window;
@@ -28,12 +28,7 @@ struct MaskSpec {
 };
 
 __device__ __forceinline__ bool mask_pair(const MaskSpec& m, int i, int j, int qdoc, int kvdoc) {
-  bool keep = true;
-  if (m.flags & FA_MASK_DOC) keep = keep && (qdoc == kvdoc);
-  if (m.flags & FA_MASK_CAUSAL) keep = keep && (i >= j);
-  if (m.flags & FA_MASK_WINDOW) keep = keep && (i - j < m.window);
-  if (m.flags & FA_MASK_PREFIX_LM) keep = keep && ((j < m.prefix_len) || (i >= j));
-  return keep;
+  return mask_pair_flags(m.flags, m.window, m.prefix_len, i, j, qdoc, kvdoc);
 }
 
 // Cross-half exchange inside a wave64: v_permlane32_swap swaps the upper half of the first

@@ -1,0 +1,70 @@
+// Tile classification shared by the device BlockMask builder and the host builder.
+//
+// FlexAttention guide, "Systems Mechanics", item 1: the mask predicate is evaluated over each
+// tile's bounding box; all-true tiles are full, all-false tiles are empty, the rest partial.
+// Here the box is the tile's in-range pairs. The closed forms below settle a tile from its
+// corners and from per-block document-id summaries; the tiles they cannot settle are evaluated
+// pair by pair with mask_pair.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "flexattn.h"
+
+namespace fa {
+
+// mask_mod for one (query, key) pair: the AND of the enabled predicates on absolute positions
+// (causal and window from the guide's "Implementation" demo, the document and prefix-LM masks
+// from "Production Engineering").
+__host__ __device__ inline bool mask_pair_flags(int flags, int window, int prefix_len, int i, int j, int qdoc,
+                                                int kvdoc) {
+  bool keep = true;
+  if (flags & FA_MASK_DOC) keep = keep && (qdoc == kvdoc);
+  if (flags & FA_MASK_CAUSAL) keep = keep && (i >= j);
+  if (flags & FA_MASK_WINDOW) keep = keep && (i - j < window);
+  if (flags & FA_MASK_PREFIX_LM) keep = keep && ((j < prefix_len) || (i >= j));
+  return keep;
+}
+
+// Class of the tile [q0, q1) x [k0, k1) (non-empty ranges): 0 empty, 1 partial, 2 full, 3 not
+// settled by closed forms. Under DOC, [qmin, qmax] and [kmin, kmax] are the id ranges of the
+// query and key blocks, and qdense / kdense flag blocks whose consecutive ids differ by 0 or 1
+// (every id of the range then occurs in the block).
+__host__ __device__ inline int classify_closed(int flags, int window, int prefix_len, int q0, int q1, int k0, int k1,
+                                               int qmin, int qmax, int qdense, int kmin, int kmax, int kdense) {
+  const int dmin = q0 - (k1 - 1), dmax = (q1 - 1) - k0;  // range of q - kv over the box
+  bool all = true, none = false;
+  if (flags & FA_MASK_CAUSAL) {
+    all = all && dmin >= 0;
+    none = none || dmax < 0;
+  }
+  if (flags & FA_MASK_WINDOW) {
+    all = all && dmax < window;
+    none = none || dmin >= window;
+  }
+  if (flags & FA_MASK_PREFIX_LM) {
+    all = all && ((k1 - 1 < prefix_len) || dmin >= 0);
+    none = none || (k0 >= prefix_len && dmax < 0);
+  }
+  const bool index_all = all;
+  if (flags & FA_MASK_DOC) {
+    all = all && (qmin == qmax && kmin == kmax && qmin == kmin);
+    none = none || (qmax < kmin || kmax < qmin);
+  }
+  if (all) return 2;
+  if (none) return 0;
+  if (!(flags & FA_MASK_DOC)) {
+    // Causal and window together allow exactly the pairs with q - kv in [0, window): the box's
+    // q - kv values form one integer interval, and each predicate alone was not all-false, so
+    // the interval meets [0, window) and some pair is allowed. Prefix-LM alone is one
+    // predicate that is not all-false.
+    if (!(flags & FA_MASK_PREFIX_LM)) return 1;
+    if (!(flags & FA_MASK_WINDOW)) return 1;
+    return 3;
+  }
+  // Document ids with every index predicate true on the whole box: the tile is non-empty iff
+  // the blocks share an id, which dense blocks with overlapping ranges do.
+  if (index_all && qdense && kdense) return 1;
+  return 3;
+}
+
+}  // namespace fa

@@ -67,6 +67,9 @@ def lib() -> ctypes.CDLL:
         L.flexattn_block_mask_build.argtypes = [c_int, POINTER(FaParams), c_int, c_int, c_int,
                                                 POINTER(FaBlockMask), c_void_p, c_size_t, c_void_p]
         L.flexattn_block_mask_build.restype = c_int
+        L.flexattn_block_mask_build_host.argtypes = [c_int, POINTER(FaParams), c_int, c_int, c_int,
+                                                     POINTER(FaBlockMask)]
+        L.flexattn_block_mask_build_host.restype = c_int
         L.flexattn_fwd.argtypes = [POINTER(FaTensor), POINTER(FaTensor), POINTER(FaTensor),
                                    POINTER(FaBlockMask), c_int, c_int, POINTER(FaParams),
                                    POINTER(FaTensor), c_void_p, c_void_p]
@@ -146,6 +149,14 @@ class BlockMask:
         self.kv_indices = torch.empty((Bm, Hm, self.n_qb, self.n_kvb), **z)
         self.full_kv_indices = torch.empty((Bm, Hm, self.n_qb, self.n_kvb), **z)
 
+    def to(self, device) -> "BlockMask":
+        """A copy of this BlockMask with its arrays on `device`."""
+        bm = BlockMask.__new__(BlockMask)
+        bm.__dict__.update(self.__dict__)
+        for k in ("kv_num_blocks", "full_kv_num_blocks", "kv_indices", "full_kv_indices"):
+            setattr(bm, k, getattr(self, k).to(device))
+        return bm
+
     def as_struct(self) -> FaBlockMask:
         return FaBlockMask(self.Bm, self.Hm, self.q_len, self.kv_len, self.q_block, self.kv_block,
                            self.n_qb, self.n_kvb, self.kv_num_blocks.data_ptr(), self.kv_indices.data_ptr(),
@@ -175,6 +186,26 @@ def flexattn_block_mask_build(mask_kind: int, B: int, q_len: int, kv_len: int, q
     _check(lib().flexattn_block_mask_build(mask_kind, ctypes.byref(p), B, q_len, kv_len, ctypes.byref(s),
                                            _ptr(workspace), workspace.numel() if workspace is not None else 0,
                                            _stream(stream)))
+    return out
+
+
+def flexattn_block_mask_build_host(mask_kind: int, B: int, q_len: int, kv_len: int, q_block: int = 128,
+                                   kv_block: int = 128, *, q_doc=None, kv_doc=None, window: int = 0,
+                                   prefix_len: int = 0) -> BlockMask:
+    """Build a BlockMask on the host: document ids and the returned arrays are CPU memory."""
+    def host_ids(x):
+        if x is None:
+            return None
+        t = x if isinstance(x, torch.Tensor) else torch.from_numpy(x)
+        if t.device.type != "cpu" or t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError("document ids must be contiguous int32 CPU arrays")
+        return t
+    qd, kd = host_ids(q_doc), host_ids(kv_doc)
+    Bm = B if (mask_kind & FA_MASK_DOC) else 1
+    out = BlockMask(Bm, 1, q_len, kv_len, q_block, kv_block, torch.device("cpu"))
+    p = _params(window=window, prefix_len=prefix_len, q_doc=qd, kv_doc=kd)
+    s = out.as_struct()
+    _check(lib().flexattn_block_mask_build_host(mask_kind, ctypes.byref(p), B, q_len, kv_len, ctypes.byref(s)))
     return out
 
 

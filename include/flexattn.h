@@ -120,6 +120,14 @@ fa_status flexattn_block_mask_build(int mask_kind, const fa_params* p, int B, in
                                     fa_block_mask* out, void* workspace, size_t workspace_bytes,
                                     hipStream_t stream);
 
+/* The same BlockMask built on the host, on the calling thread: p->q_doc / p->kv_doc (DOC) and the
+ * four arrays of `out` are host memory; no workspace, no stream. Validation, block sizes and
+ * results are those of flexattn_block_mask_build (exact classification; the two builders share
+ * their closed forms). For callers whose document ids live on the host, or that build a mask
+ * once and upload it. */
+fa_status flexattn_block_mask_build_host(int mask_kind, const fa_params* p, int B, int q_len, int kv_len,
+                                         fa_block_mask* out);
+
 /* Quantize bf16 q, k, v for the quantized forward (the int8-QK / fp8-PV attention form of
  * FlashRT-Structures PR #1, "LTX-2.5 attention forms"). All tensors are [B, H, L, 128] on the
  * device, D contiguous; q, k, v are FA_BF16 with scale = NULL; q8 and k8 are FA_I8 and v8 is
