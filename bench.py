@@ -33,10 +33,11 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2516.6
 FP32_PEAK_TFLOPS = 157.3
 INT8_FP8_PEAK_TOPS = 5033.2  # dense int8 / fp8 MFMA (2x bf16)
-CPU_SAMPLE_BLOCKS = 6   # query blocks (x all heads) of the oracle timed on the host
+CPU_SAMPLE_BLOCKS = 24   # query blocks (x all heads) of the oracle timed on the host
 KERNEL_SOURCES = ["block_sparse_masked_blockmask_amd/csrc/fwd.hip",
                   "block_sparse_masked_blockmask_amd/csrc/quant.hip",
-                  "block_sparse_masked_blockmask_amd/csrc/device_common.h"]
+                  "block_sparse_masked_blockmask_amd/csrc/device_common.h",
+                  "block_sparse_masked_blockmask_amd/csrc/tile_class.h"]
 
 
 def allowed_pairs(w) -> int:
@@ -149,6 +150,85 @@ def cpu_baseline(w, spec):
                       f"{w.Lkv} keys each, numpy fp64 dense rows; {dt:.1f} s"}
 
 
+def achievable_peaks(torch, dev):
+    """What this machine reaches outside the method: a 1 GiB device copy (HBM read + write bytes per
+    second) and an 8192^3 bf16 GEMM through the vendor BLAS (TFLOP/s); best of 5 after warm-up."""
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    b = torch.empty_like(a)
+    m = 8192
+    x = torch.randn(m, m, device=dev).bfloat16()
+    y = torch.randn(m, m, device=dev).bfloat16()
+
+    def best(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return min(ts)
+
+    t_copy = best(lambda: b.copy_(a))
+    t_gemm = best(lambda: torch.matmul(x, y))
+    res = {"hbm_copy_gbs": 2 * n / t_copy / 1e9, "bf16_gemm_tflops": 2.0 * m ** 3 / t_gemm / 1e12}
+    del a, b, x, y
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_sweep(args, fa, torch, dev):
+    """Group-count sweep of the grouped variate workload. Each sample is the mean of 100
+    back-to-back forward launches between two HIP events (the forwards run for microseconds);
+    the median of 5 samples is reported, after 2 warm-up samples."""
+    from workloads import SWEEP_GROUPS, grouped_sweep
+
+    def time_fwd(call):
+        samples = []
+        for rep in range(7):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(100):
+                call()
+            e1.record()
+            torch.cuda.synchronize()
+            if rep >= 2:
+                samples.append(e0.elapsed_time(e1) / 100 * 1e3)
+        return float(np.median(samples))
+
+    for dtype in ("f32", "bf16"):
+        for n in SWEEP_GROUPS:
+            w = grouped_sweep(n, dtype)
+            if dtype == "bf16":
+                q, k, v = (torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+                           for x in (w.q, w.k, w.v))
+            else:
+                q, k, v = (torch.from_numpy(np.ascontiguousarray(x)).to(dev) for x in (w.q, w.k, w.v))
+            qd = torch.from_numpy(w.q_doc).to(dev)
+            kv_block = 64 if dtype == "bf16" else 128
+            out = torch.empty_like(q)
+            lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+            sparse = fa.flexattn_block_mask_build(fa.FA_MASK_DOC, 1, w.Lq, w.Lkv, 128, kv_block, q_doc=qd, kv_doc=qd)
+            dense = fa.block_mask_all_partial(1, 1, w.Lq, w.Lkv, 128, kv_block, device=dev)
+            stream = torch.cuda.current_stream()
+            t = {}
+            for name, bm in (("sparse", sparse), ("all_live", dense)):
+                t[name] = time_fwd(lambda bm=bm: fa.flexattn_fwd(q, k, v, bm, fa.FA_MASK_DOC, q_doc=qd, kv_doc=qd,
+                                                                 out=out, lse=lse, stream=stream))
+            tiles = int(sparse.kv_num_blocks.sum() + sparse.full_kv_num_blocks.sum())
+            flops = 4.0 * w.D * w.Hq * 17 * 17 * n
+            print(json.dumps({"sweep": "grouped_variate", "groups": n, "variates_per_group": 17, "dtype": dtype,
+                              "L": w.Lq, "H": w.Hq, "D": w.D, "kv_block": kv_block,
+                              "tiles_sparse": tiles, "tiles_all_live": dense.n_qb * dense.n_kvb,
+                              "fwd_us_sparse": t["sparse"], "fwd_us_all_live": t["all_live"],
+                              "speedup_sparse": t["all_live"] / t["sparse"],
+                              "tflops_sparse": flops / (t["sparse"] * 1e-6) / 1e12}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -160,6 +240,10 @@ def main():
     ap.add_argument("--quantized", action="store_true",
                     help="int8-QK / fp8-PV form (unmasked workloads): step = quantize + quantized forward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the achievable-peak measurements")
+    ap.add_argument("--sweep", action="store_true",
+                    help="group-count sweep (8/32/64/128 groups x 17 variates, fp32 and bf16): block-sparse "
+                         "BlockMask against an all-live BlockMask through the same kernel, one JSON line each")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (HBM counter calibration for rocprofv3)")
     args = ap.parse_args()
@@ -182,6 +266,9 @@ def main():
 
     import block_sparse_masked_blockmask_amd as fa
     from workloads import make_workload
+    if args.sweep:
+        run_sweep(args, fa, torch, dev)
+        return
 
     t_gen = time.perf_counter()
     w = make_workload(args.workload)
@@ -295,6 +382,11 @@ def main():
         "roofline": roof,
         "input_gen_s": gen_s,
     }
+    if not args.no_peaks and not args.quantized and w.dtype == "bf16":
+        ach = achievable_peaks(torch, dev)
+        ref = ach["hbm_copy_gbs"] if roof["unit"] == "GB/s" else ach["bf16_gemm_tflops"]
+        ach["frac_of_achievable"] = roof["achieved"] / ref
+        rec["achievable"] = ach
     if not args.no_cpu_baseline:
         spec = dict(doc=w.doc, causal=w.causal, window=w.window, prefix_len=w.prefix_len, q_doc=w.q_doc,
                     kv_doc=w.kv_doc, alibi_slopes=w.alibi_slopes, softcap=w.softcap)

@@ -8,7 +8,7 @@ from .flexattn import (  # noqa: F401
     FA_MASK_CAUSAL, FA_MASK_DOC, FA_MASK_NONE, FA_MASK_PREFIX_LM, FA_MASK_WINDOW,
     FA_SCORE_ALIBI, FA_SCORE_NONE, FA_SCORE_SOFTCAP,
     FA_OK, FA_ERR_DEVICE, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED,
-    BlockMask, FlexAttnError, LIB_PATH,
+    BlockMask, FlexAttnError, LIB_PATH, block_mask_all_partial,
     flexattn_block_mask_build, flexattn_block_mask_build_host, flexattn_block_mask_count_bytes,
     flexattn_block_mask_index_bytes,
     flexattn_block_mask_workspace_bytes, flexattn_fwd, flexattn_last_error, flexattn_quantize_qkv,

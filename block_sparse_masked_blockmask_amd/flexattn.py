@@ -189,6 +189,20 @@ def flexattn_block_mask_build(mask_kind: int, B: int, q_len: int, kv_len: int, q
     return out
 
 
+def block_mask_all_partial(Bm: int, Hm: int, q_len: int, kv_len: int, q_block: int = 128, kv_block: int = 128,
+                           device=None) -> BlockMask:
+    """A BlockMask that lists every tile as partial: the kernel visits all tiles and evaluates the
+    mask on every score (the dense-iteration baseline for a block-sparse BlockMask; both give the
+    same result for the same mask)."""
+    bm = BlockMask(Bm, Hm, q_len, kv_len, q_block, kv_block, device)
+    bm.kv_num_blocks.fill_(bm.n_kvb)
+    bm.full_kv_num_blocks.zero_()
+    bm.kv_indices.copy_(torch.arange(bm.n_kvb, dtype=torch.int32, device=bm.kv_indices.device)
+                        .expand_as(bm.kv_indices))
+    bm.full_kv_indices.zero_()
+    return bm
+
+
 def flexattn_block_mask_build_host(mask_kind: int, B: int, q_len: int, kv_len: int, q_block: int = 128,
                                    kv_block: int = 128, *, q_doc=None, kv_doc=None, window: int = 0,
                                    prefix_len: int = 0) -> BlockMask:

@@ -23,7 +23,9 @@ from .synth import (  # noqa: F401
     Workload,
     bf16_bits_to_f32,
     f32_to_bf16_bits,
+    grouped_sweep,
     make_workload,
     random_case,
+    SWEEP_GROUPS,
     WORKLOADS,
 )

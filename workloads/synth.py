@@ -154,6 +154,19 @@ def _dense_long(with_tensors=True):
                     v_channel_scale=s)
 
 
+def grouped_sweep(n_groups: int, dtype: str) -> Workload:
+    """n_groups groups of 17 variates packed in order (TiRex2 shape: 1 target + 16 covariates),
+    B=1, H=4, D=128; the group-count sweep of the grouped variate workload."""
+    rng = np.random.default_rng(1000 + 2 * n_groups + (dtype == "bf16"))
+    doc = group_ids([17] * n_groups)[None, :]
+    L = doc.shape[1]
+    q, k, v = _qkv(rng, 1, 4, 4, L, L, 128, dtype)
+    return Workload(f"grouped_variate_{n_groups}x17_{dtype}", dtype, 1, 4, 4, L, L, 128, q, k, v,
+                    doc=True, q_doc=doc, kv_doc=doc)
+
+
+SWEEP_GROUPS = (8, 32, 64, 128)
+
 WORKLOADS = {
     "grouped_variate_4x17_f32": _tirex_small,
     "grouped_variate_4096g_bf16": _tirex_scale,
