@@ -100,7 +100,7 @@ size_t flexattn_block_mask_count_bytes(int Bm, int Hm, int q_len, int q_block) {
 
 size_t flexattn_block_mask_workspace_bytes(int mask_kind, int B, int q_len, int kv_len, int q_block, int kv_block) {
   if (!(mask_kind & FA_MASK_DOC) || B <= 0 || q_len < 0 || kv_len < 0 || q_block <= 0 || kv_block <= 0) return 0;
-  return (size_t)B * (cdiv(q_len, q_block) + cdiv(kv_len, kv_block)) * 3 * sizeof(int32_t);
+  return (size_t)B * (cdiv(q_len, q_block) + cdiv(kv_len, kv_block)) * 4 * sizeof(int32_t);
 }
 
 fa_status flexattn_block_mask_build(int mask_kind, const fa_params* p, int B, int q_len, int kv_len,
@@ -111,6 +111,7 @@ fa_status flexattn_block_mask_build(int mask_kind, const fa_params* p, int B, in
   const size_t need = flexattn_block_mask_workspace_bytes(mask_kind, B, q_len, kv_len, out->q_block, out->kv_block);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need))
     return fail(FA_ERR_INVALID_ARG, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+  if (need > 0 && !aligned16(workspace)) return fail(FA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   fa::BlockMaskArgs a{};
   a.flags = mask_kind;
   a.window = (mask_kind & FA_MASK_WINDOW) ? p->window : 0;
@@ -127,7 +128,7 @@ fa_status flexattn_block_mask_build(int mask_kind, const fa_params* p, int B, in
   a.kv_doc = (mask_kind & FA_MASK_DOC) ? p->kv_doc : nullptr;
   if (need > 0) {
     a.qsum = static_cast<int*>(workspace);
-    a.kvsum = a.qsum + (size_t)B * a.nqb * 3;
+    a.kvsum = a.qsum + (size_t)B * a.nqb * 4;
   }
   a.kv_num = out->kv_num_blocks;
   a.kv_idx = out->kv_indices;

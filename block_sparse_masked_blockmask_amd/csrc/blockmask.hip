@@ -3,16 +3,16 @@
 // FlexAttention guide, "Systems Mechanics", item 1: the mask predicate is evaluated over each
 // tile's bounding box; all-true tiles are full, all-false tiles are empty (never visited), the
 // rest are partial. Here the box is the tile's in-range pairs. Each (mask row, query block) row
-// is classified by one workgroup:
-//   1. closed forms decide most tiles exactly: the index predicates (causal, window, prefix-LM)
-//      are monotone in q - kv or kv, so their all-true / all-false conditions are corner tests;
-//      document ids use per-block summaries: [min, max] (equal single ids: full; disjoint:
-//      empty) and a "dense" flag (consecutive ids differ by 0 or 1, so every id in [min, max]
-//      occurs in the block; two dense blocks with overlapping ranges then share an id);
+// is classified by one workgroup, 2048 kv blocks per pass:
+//   1. closed forms (tile_class.h) decide most tiles exactly from corner tests and per-block
+//      document-id summaries [min, max, dense]; one kv block per thread and round, so the
+//      16-byte summaries are read with fully coalesced loads;
 //   2. tiles that the closed forms cannot settle are evaluated pair by pair by the whole
 //      workgroup (exact for any ids, sorted or not);
-//   3. each thread owns a run of consecutive kv blocks; one block-wide scan of the per-thread
-//      counts writes the full and partial lists in ascending order; their tails are zeroed.
+//   3. ordered compaction: wave w owns kv blocks [512 w, 512 w + 512) of the pass; ballots of
+//      the classes (kept in LDS) give each lane its rank, wave totals give each wave its base,
+//      so the full and partial lists are written in ascending order with coalesced stores.
+// The unused tails of both lists are zeroed.
 #include <hip/hip_runtime.h>
 
 #include "device_common.h"
@@ -23,8 +23,9 @@ namespace fa {
 
 namespace {
 
-constexpr int kPerThread = 8;                 // kv blocks owned by one thread per chunk
-constexpr int kChunk = 256 * kPerThread;      // kv blocks classified per pass of a workgroup
+constexpr int kChunk = 2048;  // kv blocks classified per pass of a workgroup
+constexpr int kRounds = kChunk / 256;      // rounds of one kv block per thread
+constexpr int kWaveRounds = kChunk / 4 / 64;  // rounds of one kv block per lane over a wave's quarter
 
 __device__ __forceinline__ int wave_reduce_min(int x) {
 #pragma unroll
@@ -39,7 +40,7 @@ __device__ __forceinline__ int wave_reduce_max(int x) {
 
 }  // namespace
 
-// One wave per (batch, block) of either side: [min id, max id, dense flag].
+// One wave per (batch, block) of either side: [min id, max id, dense flag, 0].
 __global__ __launch_bounds__(256) void bm_summaries(BlockMaskArgs a) {
   const int w = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int nq = a.B * a.nqb, nk = a.B * a.nkvb;
@@ -52,14 +53,14 @@ __global__ __launch_bounds__(256) void bm_summaries(BlockMaskArgs a) {
     ids = a.q_doc + (int64_t)b * a.Lq;
     lo = blk * a.BQ;
     hi = min(a.Lq, lo + a.BQ);
-    dst = a.qsum + 3 * w;
+    dst = a.qsum + 4 * w;
   } else {
     const int u = w - nq;
     const int b = u / a.nkvb, blk = u % a.nkvb;
     ids = a.kv_doc + (int64_t)b * a.Lkv;
     lo = blk * a.BK;
     hi = min(a.Lkv, lo + a.BK);
-    dst = a.kvsum + 3 * u;
+    dst = a.kvsum + 4 * u;
   }
   int mn = INT_MAX, mx = INT_MIN;
   bool step_ok = true;
@@ -75,11 +76,7 @@ __global__ __launch_bounds__(256) void bm_summaries(BlockMaskArgs a) {
   mn = wave_reduce_min(mn);
   mx = wave_reduce_max(mx);
   const bool dense = __ballot(!step_ok) == 0;
-  if (lane == 0) {
-    dst[0] = mn;
-    dst[1] = mx;
-    dst[2] = dense ? 1 : 0;
-  }
+  if (lane == 0) *(int4*)dst = make_int4(mn, mx, dense ? 1 : 0, 0);
 }
 
 __global__ __launch_bounds__(256) void bm_classify(BlockMaskArgs a) {
@@ -88,53 +85,39 @@ __global__ __launch_bounds__(256) void bm_classify(BlockMaskArgs a) {
   __shared__ int s_qdoc[256];
   __shared__ int s_kvdoc[128];
   __shared__ int s_amb[kChunk];
-  __shared__ unsigned char s_res[kChunk];
+  __shared__ unsigned char s_cls[kChunk];
   __shared__ int s_namb;
   __shared__ int s_wtot[4];
 
   const int q0 = qb * a.BQ, q1 = min(a.Lq, q0 + a.BQ);
   const bool doc = (a.flags & FA_MASK_DOC) != 0;
   const MaskSpec ms{a.flags, a.window, a.prefix_len};
-  int qmin = 0, qmax = 0, qdense = 0;
+  int4 qs = make_int4(0, 0, 0, 0);
   if (doc) {
-    const int* qs = a.qsum + 3 * (b * a.nqb + qb);
-    qmin = qs[0];
-    qmax = qs[1];
-    qdense = qs[2];
+    qs = *(const int4*)(a.qsum + 4 * (b * a.nqb + qb));
     if (tid < a.BQ) s_qdoc[tid] = (q0 + tid < q1) ? a.q_doc[(int64_t)b * a.Lq + q0 + tid] : 0;
   }
   const int64_t row = (int64_t)b * a.nqb + qb;  // Hm = 1
   int* full_idx = a.full_idx + row * a.nkvb;
   int* part_idx = a.kv_idx + row * a.nkvb;
-  int nfull = 0, npart = 0;
+  int nfull = 0, npart = 0;  // wave-uniform running totals
 
   for (int c0 = 0; c0 < a.nkvb; c0 += kChunk) {
-    // 1. closed forms for this thread's run of kv blocks (summaries loaded up front).
-    const int kb0 = c0 + tid * kPerThread;
-    int kmn[kPerThread], kmx[kPerThread], kdn[kPerThread];
-#pragma unroll
-    for (int j = 0; j < kPerThread; ++j) {
-      kmn[j] = kmx[j] = kdn[j] = 0;
-      if (doc && kb0 + j < a.nkvb) {
-        const int* ks = a.kvsum + 3 * (b * a.nkvb + kb0 + j);
-        kmn[j] = ks[0];
-        kmx[j] = ks[1];
-        kdn[j] = ks[2];
-      }
-    }
+    // 1. closed forms, one kv block per thread and round.
     if (tid == 0) s_namb = 0;
     __syncthreads();
-    int cls[kPerThread];
 #pragma unroll
-    for (int j = 0; j < kPerThread; ++j) {
-      const int kb = kb0 + j;
-      cls[j] = -1;
+    for (int r = 0; r < kRounds; ++r) {
+      const int loc = r * 256 + tid, kb = c0 + loc;
+      int cls = 0;
       if (kb < a.nkvb) {
         const int k0 = kb * a.BK, k1 = min(a.Lkv, k0 + a.BK);
-        cls[j] = classify_closed(a.flags, a.window, a.prefix_len, q0, q1, k0, k1, qmin, qmax, qdense, kmn[j],
-                                 kmx[j], kdn[j]);
-        if (cls[j] == 3) s_amb[atomicAdd(&s_namb, 1)] = tid * kPerThread + j;
+        int4 ks = make_int4(0, 0, 0, 0);
+        if (doc) ks = *(const int4*)(a.kvsum + 4 * (b * a.nkvb + kb));
+        cls = classify_closed(a.flags, a.window, a.prefix_len, q0, q1, k0, k1, qs.x, qs.y, qs.z, ks.x, ks.y, ks.z);
+        if (cls == 3) s_amb[atomicAdd(&s_namb, 1)] = loc;
       }
+      s_cls[loc] = (unsigned char)cls;
     }
     __syncthreads();
 
@@ -152,41 +135,42 @@ __global__ __launch_bounds__(256) void bm_classify(BlockMaskArgs a) {
         if (i < q1 && j < k1) any = any || mask_pair(ms, i, j, doc ? s_qdoc[ii] : 0, doc ? s_kvdoc[jj] : 0);
       }
       any = __syncthreads_or(any);
-      if (tid == 0) s_res[loc] = any ? 1 : 0;
+      if (tid == 0) s_cls[loc] = any ? 1 : 0;
       __syncthreads();
     }
 
-    // 3. ascending compaction: exclusive scan of (full, partial) counts packed in one int.
-    int packed = 0;
+    // 3. ordered compaction (full and partial counts of a wave packed in one int).
+    const int wb = wave * (kChunk / 4);
+    int wcount = 0;
 #pragma unroll
-    for (int j = 0; j < kPerThread; ++j) {
-      if (cls[j] == 3) cls[j] = s_res[tid * kPerThread + j];
-      packed += (cls[j] == 2 ? 1 : 0) + (cls[j] == 1 ? 0x10000 : 0);
+    for (int r = 0; r < kWaveRounds; ++r) {
+      const int c = s_cls[wb + r * 64 + lane];
+      wcount += __popcll(__ballot(c == 2)) + (__popcll(__ballot(c == 1)) << 16);
     }
-    int incl = packed;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int up = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += up;
-    }
-    if (lane == 63) s_wtot[wave] = incl;
+    if (lane == 0) s_wtot[wave] = wcount;
     __syncthreads();
     int base = 0, tot = 0;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      if (w < wave) base += s_wtot[w];
-      tot += s_wtot[w];
+      const int t = s_wtot[w];
+      if (w < wave) base += t;
+      tot += t;
     }
-    const int excl = base + incl - packed;
-    int pf = nfull + (excl & 0xffff), pp = npart + (excl >> 16);
+    int pf = nfull + (base & 0xffff), pp = npart + (base >> 16);
 #pragma unroll
-    for (int j = 0; j < kPerThread; ++j) {
-      if (cls[j] == 2) full_idx[pf++] = kb0 + j;
-      if (cls[j] == 1) part_idx[pp++] = kb0 + j;
+    for (int r = 0; r < kWaveRounds; ++r) {
+      const int loc = wb + r * 64 + lane;
+      const int c = s_cls[loc];
+      const uint64_t bf = __ballot(c == 2), bp = __ballot(c == 1);
+      const uint64_t below = (1ull << lane) - 1;
+      if (c == 2) full_idx[pf + __popcll(bf & below)] = c0 + loc;
+      if (c == 1) part_idx[pp + __popcll(bp & below)] = c0 + loc;
+      pf += __popcll(bf);
+      pp += __popcll(bp);
     }
     nfull += tot & 0xffff;
     npart += tot >> 16;
-    __syncthreads();  // s_namb, s_amb, s_res and s_wtot are reused by the next chunk
+    __syncthreads();  // s_namb, s_amb, s_cls and s_wtot are reused by the next pass
   }
   for (int j = nfull + tid; j < a.nkvb; j += 256) full_idx[j] = 0;
   for (int j = npart + tid; j < a.nkvb; j += 256) part_idx[j] = 0;

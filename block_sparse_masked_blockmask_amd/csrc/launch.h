@@ -11,8 +11,8 @@ struct BlockMaskArgs {
   int B, Lq, Lkv, BQ, BK, nqb, nkvb, Bm;
   const int* q_doc;
   const int* kv_doc;
-  int* qsum;    // [B][nqb][3] min id, max id, dense flag of each query block (DOC only)
-  int* kvsum;   // [B][nkvb][3]
+  int* qsum;    // [B][nqb][4] min id, max id, dense flag, 0 of each query block (DOC only)
+  int* kvsum;   // [B][nkvb][4]
   int* kv_num;
   int* kv_idx;
   int* full_num;

@@ -104,7 +104,7 @@ size_t flexattn_block_mask_index_bytes(int Bm, int Hm, int q_len, int kv_len, in
 size_t flexattn_block_mask_count_bytes(int Bm, int Hm, int q_len, int q_block);
 
 /* Device scratch needed by flexattn_block_mask_build (per-block document-id summaries when DOC
- * is set: 12 bytes per query block and per kv block and batch; else 0). */
+ * is set: 16 bytes per query block and per kv block and batch; else 0). */
 size_t flexattn_block_mask_workspace_bytes(int mask_kind, int B, int q_len, int kv_len,
                                            int q_block, int kv_block);
 
@@ -114,7 +114,8 @@ size_t flexattn_block_mask_workspace_bytes(int mask_kind, int B, int q_len, int 
  * kv_len, q_block, kv_block, n_qb, n_kvb) and its four array pointers; Bm must be B when DOC is
  * set (1 or B otherwise), Hm must be 1 (no flag depends on the head). q_block is 64, 128 or
  * 256 and kv_block is 64 or 128. Reads p->q_doc / p->kv_doc (DOC), p->window (WINDOW), p->prefix_len (PREFIX_LM).
- * `workspace` must hold flexattn_block_mask_workspace_bytes(...) bytes (may be NULL if 0).
+ * `workspace` must hold flexattn_block_mask_workspace_bytes(...) bytes, 16-byte aligned (may be
+ * NULL if 0).
  * Classification is exact: the lists equal exhaustive evaluation of every in-range pair. */
 fa_status flexattn_block_mask_build(int mask_kind, const fa_params* p, int B, int q_len, int kv_len,
                                     fa_block_mask* out, void* workspace, size_t workspace_bytes,

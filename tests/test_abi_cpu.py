@@ -43,7 +43,7 @@ def test_sizes():
     assert fa.flexattn_block_mask_index_bytes(2, 1, 300, 200, 128, 64) == 2 * 3 * 4 * 4
     assert fa.flexattn_block_mask_count_bytes(2, 1, 300, 128) == 2 * 3 * 4
     assert fa.flexattn_block_mask_workspace_bytes(fa.FA_MASK_CAUSAL, 2, 300, 200, 128, 64) == 0
-    assert fa.flexattn_block_mask_workspace_bytes(fa.FA_MASK_DOC, 2, 300, 200, 128, 64) == 2 * (3 + 4) * 12
+    assert fa.flexattn_block_mask_workspace_bytes(fa.FA_MASK_DOC, 2, 300, 200, 128, 64) == 2 * (3 + 4) * 16
     assert fa.flexattn_block_mask_index_bytes(0, 1, 10, 10, 128, 128) == 0
     assert fa.flexattn_version() >= 100
 
