@@ -339,142 +339,169 @@ __device__ __forceinline__ void compute_step(const FwdArgs& a, const Ctx& c, con
     live = __builtin_amdgcn_readfirstlane(live);
   }
 
-  // S^T = K Q^T for the live 32-key sub-blocks.
-  f32x16 sacc[2];
-  if (ISSUE >= 0 && live == 3u) {
-    // Both sub-blocks: the two product chains alternate, and one transfer of the next step
-    // follows each pair of products.
-    issue_ids<(ISSUE < 0 ? 0 : ISSUE), WAVES>(a, c, kv0n);
+  // Everything after the liveness test is straight-line code for a fixed live pattern L (bit nb:
+  // sub-block nb is live): a branch per sub-block inside the P.V loop made the compiler keep O
+  // in two register sets and copy the accumulators around each branch.
+  auto body = [&](auto live_c) {
+    constexpr unsigned L = decltype(live_c)::value;
+    // S^T = K Q^T for the live 32-key sub-blocks.
+    f32x16 sacc[2];
+    if constexpr (ISSUE >= 0 && L == 3u) {
+      // Both sub-blocks: the two product chains alternate, and one transfer of the next step
+      // follows each pair of products.
+      issue_ids<(ISSUE < 0 ? 0 : ISSUE), WAVES>(a, c, kv0n);
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
+      for (int ks = 0; ks < 8; ++ks) {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          const bf16x8 kf = *(const bf16x8*)(sK + nb * 32 * 256 + kx_at(kx0, ks));
+          sacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[ks], ks ? sacc[nb] : f32x16{}, 0, 0, 0);
+        }
+        if (ks < NSEG) issue_seg<(ISSUE < 0 ? 0 : ISSUE), WAVES>(a, c, kv0n, ks);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (ks < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (ks < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (ks < NSEG) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+    } else {
+      if constexpr (ISSUE >= 0) {
+        StepInfo nx{kv0n, true, false};
+        issue_step<ISSUE, WAVES>(a, c, nx);
+      }
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
-        const bf16x8 kf = *(const bf16x8*)(sK + nb * 32 * 256 + kx_at(kx0, ks));
-        sacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[ks], ks ? sacc[nb] : f32x16{}, 0, 0, 0);
-      }
-      if (ks < NSEG) issue_seg<(ISSUE < 0 ? 0 : ISSUE), WAVES>(a, c, kv0n, ks);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        if (!(L & (1u << nb))) continue;
+        sacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(sK + nb * 32 * 256 + kx0), qreg[0],
+                                                           f32x16{}, 0, 0, 0);
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (ks < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (ks < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      if (ks < NSEG) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    }
-  } else {
-    if constexpr (ISSUE >= 0) {
-      StepInfo nx{kv0n, true, false};
-      issue_step<ISSUE, WAVES>(a, c, nx);
-    }
-    if (MASKED && !live) return;
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    if (MASKED && !(live & (1u << nb))) continue;
-    sacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(sK + nb * 32 * 256 + kx0), qreg[0],
-                                                       f32x16{}, 0, 0, 0);
-#pragma unroll
-    for (int ks = 1; ks < 8; ++ks) {
-      const bf16x8 kf = *(const bf16x8*)(sK + nb * 32 * 256 + kx_at(kx0, ks));
-      sacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[ks], sacc[nb], 0, 0, 0);
-    }
-    // Schedule: 4 operand reads ahead, then one read per product (bounds live operands).
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (k < 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-  }
-  }
-
-  // Scores (log2 domain) and the mask. Without a score_mod the 1/sqrt(d) * log2(e) scale is
-  // folded into the exponent below, and the maximum is taken on the raw products.
-  float mx = -INFINITY;
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    if (MASKED && !(live & (1u << nb))) continue;
-    const int kbase = kv0 + nb * 32 + c.hl * 4;   // key of element i is kbase + (i/4)*8 + i%4
-    // The allowed keys [lo, hi) relative to kbase: element offsets are the constants 0..27.
-    const int rlo = lo - kbase, rhi = hi - kbase;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      i32x4 kd4 = i32x4{};
-      if constexpr (MASKED && DOC) kd4 = *(const i32x4*)(sD + dx + nb * 32 + g * 8);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = g * 4 + e;
-        const int off = g * 8 + e;
-        float x = SCORE == 0 ? sacc[nb][i] : score_log2<SCORE>(a, sacc[nb][i], qi, kbase + off, c.slope);
-        if constexpr (MASKED) {
-          bool keep = (rlo <= off) & (rhi > off);
-          if constexpr (DOC) keep = keep & (kd4[e] == c.qdoc);
-          x = keep ? x : -INFINITY;
+        for (int ks = 1; ks < 8; ++ks) {
+          const bf16x8 kf = *(const bf16x8*)(sK + nb * 32 * 256 + kx_at(kx0, ks));
+          sacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[ks], sacc[nb], 0, 0, 0);
         }
-        sacc[nb][i] = x;
-        mx = fmaxf(mx, x);
+        // Schedule: 4 operand reads ahead, then one read per product (bounds live operands).
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (k < 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
       }
     }
-  }
-  mx = half_swap_max(mx);
-  const float scale = SCORE == 0 ? a.scale_log2 : 1.0f;
-  const float m_cand = fmaxf(st.m_run, mx * scale);
-  const bool raise = m_cand > st.m_run + kRescaleSlack;
-  if (__builtin_amdgcn_readfirstlane(__ballot(raise) != 0)) {
-    // Rows that keep m (including rows still at -inf) must get alpha = 1 exactly; a raised row
-    // coming from -inf gets exp2(-inf) = 0.
-    const float m_new = raise ? m_cand : st.m_run;
-    const float alpha = raise ? fast_exp2(st.m_run - m_new) : 1.0f;
-    st.l_run *= alpha;
-#pragma unroll
-    for (int db = 0; db < 4; ++db) st.oacc[db] *= alpha;
-    st.m_run = m_new;
-  }
-  const float m_eff = st.m_run == -INFINITY ? 0.f : st.m_run;  // rows with no allowed key so far
 
-  // P = exp2(t - m); P^T goes straight into the B operand of O^T = V^T P^T as bf16.
-  bf16x8 pb[2][2];
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    if (MASKED && !(live & (1u << nb))) continue;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float p = fast_exp2(fmaf(sacc[nb][i], scale, -m_eff));
-      st.l_run += p;
-      pb[nb][i >> 3][i & 7] = (__bf16)p;
-    }
-  }
-
-  // O^T += V^T P^T. A operand (V^T: row = channel, k = key) by transposed LDS reads: in each
-  // 16-lane group, source lane s points at key row base + s/4 and channels d0 + 4*(s%4); lane i
-  // of the group then receives V[base + j][d0 + i], j = 0..3.
-#pragma unroll
-  for (int db = 0; db < 4; ++db) {
+    // Scores (log2 domain) and the mask. Without a score_mod the 1/sqrt(d) * log2(e) scale is
+    // folded into the exponent below, and the maximum is taken on the raw products.
+    float mx = -INFINITY;
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      if (MASKED && !(live & (1u << nb))) continue;
+      if (!(L & (1u << nb))) continue;
+      const int kbase = kv0 + nb * 32 + c.hl * 4;   // key of element i is kbase + (i/4)*8 + i%4
+      // The allowed keys [lo, hi) relative to kbase: element offsets are the constants 0..27.
+      const int rlo = lo - kbase, rhi = hi - kbase;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int rows = (nb * 32 + h * 16) * 256;  // the swizzle depends on the row modulo 16
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sV + rows + vx_at(vx0, db, 0)));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sV + rows + vx_at(vx0, db, 1)));
-        // Whole-vector concatenation and bit cast (element-wise bf16 inserts of the i16 lanes
-        // were observed to be folded into a broadcast of element 0).
-        const i16x8 cat = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        st.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, cat), pb[nb][h],
-                                                              st.oacc[db], 0, 0, 0);
+      for (int g = 0; g < 4; ++g) {
+        i32x4 kd4 = i32x4{};
+        if constexpr (MASKED && DOC) kd4 = *(const i32x4*)(sD + dx + nb * 32 + g * 8);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = g * 4 + e;
+          const int off = g * 8 + e;
+          float x = SCORE == 0 ? sacc[nb][i] : score_log2<SCORE>(a, sacc[nb][i], qi, kbase + off, c.slope);
+          if constexpr (MASKED) {
+            bool keep = (rlo <= off) & (rhi > off);
+            if constexpr (DOC) keep = keep & (kd4[e] == c.qdoc);
+            x = keep ? x : -INFINITY;
+          }
+          sacc[nb][i] = x;
+          mx = fmaxf(mx, x);
+        }
       }
     }
-    if constexpr (!MASKED) {
-      // Schedule: 4 transposed reads ahead, then two reads per product.
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+    mx = half_swap_max(mx);
+    const float scale = SCORE == 0 ? a.scale_log2 : 1.0f;
+    const float m_cand = fmaxf(st.m_run, mx * scale);
+    const bool raise = m_cand > st.m_run + kRescaleSlack;
+
+    // The exponentials and P.V products follow in two copies, one per outcome of the rescale
+    // test: with one copy after a conditional rescale, the compiler kept O in two register sets
+    // and copied all 64 accumulators on every step.
+    auto finish = [&]() {
+      const float m_eff = st.m_run == -INFINITY ? 0.f : st.m_run;  // rows with no allowed key so far
+      // P = exp2(t - m); P^T goes straight into the B operand of O^T = V^T P^T as bf16.
+      bf16x8 pb[2][2];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-        if (k < 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+      for (int nb = 0; nb < 2; ++nb) {
+        if (!(L & (1u << nb))) continue;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = fast_exp2(fmaf(sacc[nb][i], scale, -m_eff));
+          st.l_run += p;
+          pb[nb][i >> 3][i & 7] = (__bf16)p;
+        }
       }
+      // O^T += V^T P^T. A operand (V^T: row = channel, k = key) by transposed LDS reads: in each
+      // 16-lane group, source lane s points at key row base + s/4 and channels d0 + 4*(s%4);
+      // lane i of the group then receives V[base + j][d0 + i], j = 0..3.
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          if (!(L & (1u << nb))) continue;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int rows = (nb * 32 + h * 16) * 256;  // the swizzle depends on the row modulo 16
+            const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sV + rows + vx_at(vx0, db, 0)));
+            const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sV + rows + vx_at(vx0, db, 1)));
+            // Whole-vector concatenation and bit cast (element-wise bf16 inserts of the i16 lanes
+            // were observed to be folded into a broadcast of element 0).
+            const i16x8 cat = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+            st.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, cat), pb[nb][h],
+                                                                  st.oacc[db], 0, 0, 0);
+          }
+        }
+        if constexpr (L == 3u) {
+          // Schedule: 4 transposed reads ahead, then two reads per product.
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+            if (k < 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+          }
+        }
+      }
+    };
+    if (__builtin_amdgcn_readfirstlane(__ballot(raise) != 0)) {
+      // Rows that keep m (including rows still at -inf) must get alpha = 1 exactly; a raised row
+      // coming from -inf gets exp2(-inf) = 0.
+      const float m_new = raise ? m_cand : st.m_run;
+      const float alpha = raise ? fast_exp2(st.m_run - m_new) : 1.0f;
+      st.l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) st.oacc[db] *= alpha;
+      st.m_run = m_new;
+      finish();
+    } else {
+      finish();
     }
+  };
+
+  if constexpr (!MASKED) {
+    body(std::integral_constant<unsigned, 3u>{});
+  } else {
+    if (live == 0u) {
+      if constexpr (ISSUE >= 0) {
+        StepInfo nx{kv0n, true, false};
+        issue_step<ISSUE, WAVES>(a, c, nx);
+      }
+      return;
+    }
+    if (live == 3u) body(std::integral_constant<unsigned, 3u>{});
+    else if (live == 1u) body(std::integral_constant<unsigned, 1u>{});
+    else body(std::integral_constant<unsigned, 2u>{});
   }
 }
 
