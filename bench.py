@@ -181,6 +181,48 @@ def achievable_peaks(torch, dev):
     return res
 
 
+def run_decode(args, fa, torch, dev):
+    """Decoding shape through flexattn_fwd (one workgroup per (batch, query head)) and
+    flexattn_fwd_splitkv. Each sample is the mean of 20 back-to-back calls between two HIP
+    events; median of 5 after 2 warm-up samples. Bytes: Q, K, V read once, O and lse written."""
+    from workloads import decode_workload
+    w = decode_workload()
+    bf = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v = bf(w.q), bf(w.k), bf(w.v)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    flops = 4.0 * w.D * w.Lq * w.Lkv * w.Hq * w.B
+    abytes = (q.numel() + k.numel() + v.numel() + out.numel()) * 2 + lse.numel() * 4
+
+    def time_call(call):
+        samples = []
+        for rep in range(7):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(20):
+                call()
+            e1.record()
+            torch.cuda.synchronize()
+            if rep >= 2:
+                samples.append(e0.elapsed_time(e1) / 20 * 1e3)
+        return float(np.median(samples))
+
+    for n in (1, 2, 4, 8, 16, 32):
+        ws = None
+        if n > 1:
+            ws = torch.empty(fa.flexattn_fwd_splitkv_workspace_bytes(w.B, w.Hq, w.Lq, n), dtype=torch.uint8, device=dev)
+        call = (lambda: fa.flexattn_fwd(q, k, v, None, out=out, lse=lse, stream=stream)) if n == 1 else \
+               (lambda ws=ws, n=n: fa.flexattn_fwd_splitkv(q, k, v, None, n_splits=n, workspace=ws, out=out, lse=lse,
+                                                         stream=stream))
+        us = time_call(call)
+        print(json.dumps({"decode": w.name, "entry": "flexattn_fwd" if n == 1 else "flexattn_fwd_splitkv",
+                          "n_splits": n, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Lq": w.Lq, "Lkv": w.Lkv,
+                          "us": us, "tflops": flops / (us * 1e-6) / 1e12,
+                          "gbs": abytes / (us * 1e-6) / 1e9, "hbm_frac": abytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}),
+              flush=True)
+
+
 def run_sweep(args, fa, torch, dev):
     """Group-count sweep of the grouped variate workload. Each sample is the mean of 100
     back-to-back forward launches between two HIP events (the forwards run for microseconds);
@@ -244,6 +286,9 @@ def main():
     ap.add_argument("--sweep", action="store_true",
                     help="group-count sweep (8/32/64/128 groups x 17 variates, fp32 and bf16): block-sparse "
                          "BlockMask against an all-live BlockMask through the same kernel, one JSON line each")
+    ap.add_argument("--decode", action="store_true",
+                    help="decoding shape (B=8, GQA 32/8, 16 queries x 32768 keys): flexattn_fwd and "
+                         "flexattn_fwd_splitkv over split counts, one JSON line each")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (HBM counter calibration for rocprofv3)")
     args = ap.parse_args()
@@ -268,6 +313,9 @@ def main():
     from workloads import make_workload
     if args.sweep:
         run_sweep(args, fa, torch, dev)
+        return
+    if args.decode:
+        run_decode(args, fa, torch, dev)
         return
 
     t_gen = time.perf_counter()

@@ -11,7 +11,8 @@ from .flexattn import (  # noqa: F401
     BlockMask, FlexAttnError, LIB_PATH, block_mask_all_partial,
     flexattn_block_mask_build, flexattn_block_mask_build_host, flexattn_block_mask_count_bytes,
     flexattn_block_mask_index_bytes,
-    flexattn_block_mask_workspace_bytes, flexattn_fwd, flexattn_last_error, flexattn_quantize_qkv,
+    flexattn_block_mask_workspace_bytes, flexattn_fwd, flexattn_fwd_splitkv, flexattn_fwd_splitkv_workspace_bytes,
+    flexattn_last_error, flexattn_quantize_qkv,
     flexattn_version,
     lib, tensor_desc,
 )

@@ -224,11 +224,20 @@ static fa_status fwd_quantized(const fa_tensor* q, const fa_tensor* k, const fa_
                                int mask_kind, int score_kind, const fa_params* p, fa_tensor* out, float* lse,
                                hipStream_t stream);
 
-fa_status flexattn_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_block_mask* bm,
-                       int mask_kind, int score_kind, const fa_params* p, fa_tensor* out, float* lse,
-                       hipStream_t stream) {
-  if (!q || !k || !v || !out) return fail(FA_ERR_INVALID_ARG, "q, k, v and out must not be NULL");
-  if (q->dtype == FA_I8) return fwd_quantized(q, k, v, bm, mask_kind, score_kind, p, out, lse, stream);
+size_t flexattn_fwd_splitkv_workspace_bytes(int B, int Hq, int Lq, int n_splits) {
+  if (B < 0 || Hq < 0 || Lq < 0 || n_splits < 1) return 0;
+  return (size_t)n_splits * B * Hq * Lq * (128 + 1) * sizeof(float);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The forward with nsplit contiguous ranges of each work item's tile list (nsplit = 1: the
+// plain forward; nsplit > 1: partial results in the workspace, then the merge).
+fa_status fwd_impl(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_block_mask* bm,
+                   int mask_kind, int score_kind, const fa_params* p, fa_tensor* out, float* lse, int nsplit,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
   const int dt = q->dtype;
   if (k->dtype != dt || v->dtype != dt || out->dtype != dt)
     return fail(FA_ERR_INVALID_ARG, "q, k, v and out must share one dtype");
@@ -261,7 +270,7 @@ fa_status flexattn_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* 
   if (bm == nullptr) {
     if (mask_kind != FA_MASK_NONE) return fail(FA_ERR_INVALID_ARG, "a BlockMask is required unless mask_kind is NONE");
     // 256-query workgroups (bf16) once they still give at least one per CU.
-    if (dt == FA_BF16 && (int64_t)B * q->H * cdiv(Lq, 256) >= 256) q_block = 256;
+    if (dt == FA_BF16 && nsplit == 1 && (int64_t)B * q->H * cdiv(Lq, 256) >= 256) q_block = 256;
     a.all_full = 1;
     a.Bm = a.Hm = 1;
     a.nqb = cdiv(Lq, q_block);
@@ -291,7 +300,15 @@ fa_status flexattn_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* 
     a.full_num = bm->full_kv_num_blocks;
     a.full_idx = bm->full_kv_indices;
   }
-  const int64_t total = (int64_t)B * q->H * a.nqb;
+  if (nsplit > 1) {
+    if (dt != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "split-KV serves bf16 tensors");
+    if (q_block != 128) return fail(FA_ERR_UNSUPPORTED, "split-KV needs q_block 128 (got %d)", q_block);
+    const size_t need = flexattn_fwd_splitkv_workspace_bytes(B, q->H, Lq, nsplit);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+      return fail(FA_ERR_INVALID_ARG, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+    if (need > 0 && !aligned16(workspace)) return fail(FA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  }
+  const int64_t total = (int64_t)B * q->H * a.nqb * nsplit;
   if (total > 0x7fffffff) return fail(FA_ERR_UNSUPPORTED, "grid too large (%lld workgroups)", (long long)total);
 
   a.q = q->data; a.k = k->data; a.v = v->data; a.o = out->data; a.lse = lse;
@@ -312,9 +329,51 @@ fa_status flexattn_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* 
   a.inv_softcap = (score_kind & FA_SCORE_SOFTCAP) ? 1.0f / p->softcap : 0.f;
   a.slopes = (score_kind & FA_SCORE_ALIBI) ? p->alibi_slopes : nullptr;
   a.total_wg = (int)total;
+  a.nsplit = nsplit;
+  if (nsplit > 1) {
+    a.part_o = static_cast<float*>(workspace);
+    a.part_lse = a.part_o + (size_t)nsplit * B * q->H * Lq * 128;
+  }
   hipError_t e = fa::launch_fwd(a, dt == FA_BF16 ? 1 : 0, q_block, kv_block, score_kind, stream);
   if (e != hipSuccess) return fail(FA_ERR_DEVICE, "forward launch failed: %s", hipGetErrorString(e));
+  if (nsplit > 1) {
+    fa::MergeArgs m{};
+    m.part_o = a.part_o;
+    m.part_lse = a.part_lse;
+    m.o = static_cast<__bf16*>(out->data);
+    m.lse = lse;
+    m.o_sb = out->stride_b;
+    m.o_sh = out->stride_h;
+    m.o_sl = out->stride_l;
+    m.B = B;
+    m.Hq = q->H;
+    m.Lq = Lq;
+    m.nsplit = nsplit;
+    e = fa::launch_splitkv_merge(m, stream);
+    if (e != hipSuccess) return fail(FA_ERR_DEVICE, "split-KV merge launch failed: %s", hipGetErrorString(e));
+  }
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status flexattn_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_block_mask* bm,
+                       int mask_kind, int score_kind, const fa_params* p, fa_tensor* out, float* lse,
+                       hipStream_t stream) {
+  if (!q || !k || !v || !out) return fail(FA_ERR_INVALID_ARG, "q, k, v and out must not be NULL");
+  if (q->dtype == FA_I8) return fwd_quantized(q, k, v, bm, mask_kind, score_kind, p, out, lse, stream);
+  return fwd_impl(q, k, v, bm, mask_kind, score_kind, p, out, lse, 1, nullptr, 0, stream);
+}
+
+fa_status flexattn_fwd_splitkv(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_block_mask* bm,
+                               int mask_kind, int score_kind, const fa_params* p, fa_tensor* out, float* lse,
+                               int n_splits, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!q || !k || !v || !out) return fail(FA_ERR_INVALID_ARG, "q, k, v and out must not be NULL");
+  if (n_splits < 1 || n_splits > 256) return fail(FA_ERR_INVALID_ARG, "n_splits must be in [1, 256] (got %d)", n_splits);
+  if (q->dtype == FA_I8) return fail(FA_ERR_UNSUPPORTED, "split-KV does not serve the quantized form");
+  return fwd_impl(q, k, v, bm, mask_kind, score_kind, p, out, lse, n_splits, workspace, workspace_bytes, stream);
 }
 
 static fa_status check_q_tensor(const fa_tensor* t, const char* name, int dtype, int elem_align) {

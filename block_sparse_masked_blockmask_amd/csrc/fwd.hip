@@ -33,14 +33,21 @@ constexpr int kD = 128;
 constexpr int kBQ = 128;
 
 struct WorkItem {
-  int b, hq, hkv, qb;
+  int b, hq, hkv, qb, split;
 };
 
+template <bool SPLIT = false>
 __device__ __forceinline__ WorkItem decode_work(const FwdArgs& a) {
   int w = xcd_remap(blockIdx.x, a.total_wg);
-  // Order: query heads of one kv head fastest (they read the same K/V tiles), then query
-  // blocks from the last (most tiles under causal masks) to the first, then kv head, batch.
+  // Order: splits of one work item fastest (they read the same Q rows), then query heads of
+  // one kv head (they read the same K/V tiles), then query blocks from the last (most tiles
+  // under causal masks) to the first, then kv head, batch.
   WorkItem it;
+  it.split = 0;
+  if constexpr (SPLIT) {
+    it.split = w % a.nsplit;
+    w /= a.nsplit;
+  }
   const int g = w % a.group;
   w /= a.group;
   const int qbr = w % a.nqb;
@@ -294,7 +301,7 @@ __device__ __forceinline__ void key_interval(const FwdArgs& a, int qi, int& lo, 
 // kv0n) into buffer ISSUE, spread between its S products when both sub-blocks are live (a wave
 // is held while its transfers are accepted, and the memory pipeline accepts about 64 bytes per
 // cycle per CU, so issuing them back to back stalls every wave of the CU), else up front.
-template <int B, int SCORE, bool MASKED, bool DOC, int ISSUE, int WAVES>
+template <int B, int SCORE, bool MASKED, bool DOC, int ISSUE, int WAVES, bool SPLIT>
 __device__ __forceinline__ void compute_step(const FwdArgs& a, const Ctx& c, const bf16x8 (&qreg)[8], State& st,
                                              const int kv0, const int kv0n) {
   constexpr int NSEG = 2 * (16 / WAVES);  // row transfers per wave and step
@@ -490,6 +497,15 @@ __device__ __forceinline__ void compute_step(const FwdArgs& a, const Ctx& c, con
   };
 
   if constexpr (!MASKED) {
+    if (SPLIT && c.qw0 >= a.Lq) {
+      // A wave past the last query (few query rows, as in decoding) only does its share of the
+      // transfers; its products would be discarded. (Masked steps find this in the liveness test.)
+      if constexpr (ISSUE >= 0) {
+        StepInfo nx{kv0n, true, false};
+        issue_step<ISSUE, WAVES>(a, c, nx);
+      }
+      return;
+    }
     body(std::integral_constant<unsigned, 3u>{});
   } else {
     if (live == 0u) {
@@ -512,13 +528,15 @@ struct StepPlan {
 
 }  // namespace
 
-template <int TB, int SCORE, int WAVES, int NBUF>
+// SPLIT: the split-KV form (a range of each tile list, partial results; waves without a query
+// skip the products). A separate instantiation, so that the plain forward carries none of it.
+template <int TB, int SCORE, int WAVES, int NBUF, bool SPLIT>
 __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(FwdArgs a) {
   constexpr int HALVES = TB / kStep;
   constexpr int BQ = 32 * WAVES;
   constexpr int OPS = step_ops<WAVES>();
 
-  const WorkItem it = decode_work(a);
+  const WorkItem it = decode_work<SPLIT>(a);
   Ctx c;
   c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar registers
   c.lane = threadIdx.x & 63;
@@ -593,7 +611,13 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(FwdArgs
   }
   c.qdoc = (c.doc && c.q_in) ? qdoc_raw : 0;
   const int ntiles = tl.nfull + tl.npart;
-  const int nsteps = ntiles * HALVES;
+  // Split-KV: this workgroup takes list entries [t_begin, t_end).
+  int t_begin = 0, t_end = ntiles;
+  if constexpr (SPLIT) {
+    t_begin = (int)((int64_t)it.split * ntiles / a.nsplit);
+    t_end = (int)((int64_t)(it.split + 1) * ntiles / a.nsplit);
+  }
+  const int nsteps = (t_end - t_begin) * HALVES;
 
   // List entries, 64 per register: lane j holds the entry of tile chunk_base + j.
   auto load_chunk = [&](int base) -> int {
@@ -609,7 +633,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(FwdArgs
   auto info = [&](int s) {
     StepInfo si{0, false, false};
     if (s >= nsteps) return si;
-    const int t = s / HALVES;
+    const int t = t_begin + s / HALVES;
     if (t >= chunk_base + 64) {  // next 64 list entries (once per 64 tiles)
       chunk_base = t & ~63;
       chunk = load_chunk(chunk_base);
@@ -659,15 +683,15 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(FwdArgs
     ring[NB] = nxt;
     if (cur.ok && nxt.kv0 + kStep <= a.Lkv) {
       // The step's own compute issues the next step's transfers.
-      if (!cur.masked) compute_step<B, SCORE, false, false, NB, WAVES>(a, c, qreg, st, cur.kv0, nxt.kv0);
-      else if (c.doc) compute_step<B, SCORE, true, true, NB, WAVES>(a, c, qreg, st, cur.kv0, nxt.kv0);
-      else compute_step<B, SCORE, true, false, NB, WAVES>(a, c, qreg, st, cur.kv0, nxt.kv0);
+      if (!cur.masked) compute_step<B, SCORE, false, false, NB, WAVES, SPLIT>(a, c, qreg, st, cur.kv0, nxt.kv0);
+      else if (c.doc) compute_step<B, SCORE, true, true, NB, WAVES, SPLIT>(a, c, qreg, st, cur.kv0, nxt.kv0);
+      else compute_step<B, SCORE, true, false, NB, WAVES, SPLIT>(a, c, qreg, st, cur.kv0, nxt.kv0);
     } else {
       issue_step<NB, WAVES>(a, c, nxt);
       if (cur.ok) {
-        if (!cur.masked) compute_step<B, SCORE, false, false, -1, WAVES>(a, c, qreg, st, cur.kv0, 0);
-        else if (c.doc) compute_step<B, SCORE, true, true, -1, WAVES>(a, c, qreg, st, cur.kv0, 0);
-        else compute_step<B, SCORE, true, false, -1, WAVES>(a, c, qreg, st, cur.kv0, 0);
+        if (!cur.masked) compute_step<B, SCORE, false, false, -1, WAVES, SPLIT>(a, c, qreg, st, cur.kv0, 0);
+        else if (c.doc) compute_step<B, SCORE, true, true, -1, WAVES, SPLIT>(a, c, qreg, st, cur.kv0, 0);
+        else compute_step<B, SCORE, true, false, -1, WAVES, SPLIT>(a, c, qreg, st, cur.kv0, 0);
       }
     }
   };
@@ -684,6 +708,25 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(FwdArgs
   // Epilogue: combine the two halves' row sums, normalise, store O (bf16) and the natural-log lse.
   const float l_tot = half_swap_sum(st.l_run);
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+  if constexpr (SPLIT) {
+    // Split-KV partial result: normalised O in fp32 and the lse of this range of tiles.
+    if (c.q_in) {
+      const int64_t prow = (((int64_t)it.split * a.B + it.b) * a.Hq + it.hq) * a.Lq + c.qi;
+      float* po = a.part_o + prow * 128;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          f32x4 o4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o4[e] = st.oacc[db][gq * 4 + e] * inv;
+          *(f32x4*)(po + db * 32 + gq * 8 + c.hl * 4) = o4;
+        }
+      }
+      if (c.hl == 0) a.part_lse[prow] = l_tot > 0.f ? (st.m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+    }
+    return;
+  }
   if (c.q_in) {
     __bf16* op = (__bf16*)a.o + it.b * a.o_sb + it.hq * a.o_sh + (int64_t)c.qi * a.o_sl;
 #pragma unroll
@@ -856,9 +899,11 @@ template <int BK, int SCORE>
 static hipError_t launch_t(const FwdArgs& a, int dtype, int q_block, hipStream_t stream) {
   if (dtype == 1) {
     if (q_block == 256)
-      hipLaunchKernelGGL((fwd_bf16_kernel<BK, SCORE, 8, 4>), dim3(a.total_wg), dim3(512), 0, stream, a);
+      hipLaunchKernelGGL((fwd_bf16_kernel<BK, SCORE, 8, 4, false>), dim3(a.total_wg), dim3(512), 0, stream, a);
+    else if (a.nsplit > 1)
+      hipLaunchKernelGGL((fwd_bf16_kernel<BK, SCORE, 4, 2, true>), dim3(a.total_wg), dim3(256), 0, stream, a);
     else
-      hipLaunchKernelGGL((fwd_bf16_kernel<BK, SCORE, 4, 2>), dim3(a.total_wg), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((fwd_bf16_kernel<BK, SCORE, 4, 2, false>), dim3(a.total_wg), dim3(256), 0, stream, a);
   } else {
     hipLaunchKernelGGL((fwd_f32_kernel<BK, SCORE>), dim3(a.total_wg), dim3(256), 0, stream, a);
   }
@@ -873,6 +918,46 @@ static hipError_t launch_bk(const FwdArgs& a, int dtype, int q_block, int score,
     case FA_SCORE_SOFTCAP: return launch_t<BK, FA_SCORE_SOFTCAP>(a, dtype, q_block, stream);
     default: return launch_t<BK, FA_SCORE_ALIBI | FA_SCORE_SOFTCAP>(a, dtype, q_block, stream);
   }
+}
+
+// Split-KV merge: one wave per query row; lane l owns channels 2l and 2l + 1. With the ranges'
+// lse_s (natural log) and normalised outputs O_s: lse = log sum_s exp(lse_s) and
+// O = sum_s exp(lse_s - lse) O_s. A row whose every range is empty keeps O = 0, lse = -inf.
+__global__ __launch_bounds__(256) void splitkv_merge_kernel(MergeArgs m) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int64_t nrows = (int64_t)m.B * m.Hq * m.Lq;
+  if (row >= nrows) return;
+  const int64_t stride = nrows;  // between splits
+  float mx = -INFINITY;
+  for (int sp = 0; sp < m.nsplit; ++sp) mx = fmaxf(mx, m.part_lse[sp * stride + row]);
+  float o0 = 0.f, o1 = 0.f, wsum = 0.f;
+  if (mx != -INFINITY) {
+    for (int sp = 0; sp < m.nsplit; ++sp) {
+      const float ls = m.part_lse[sp * stride + row];
+      const float w = ls == -INFINITY ? 0.f : expf(ls - mx);
+      const float2 v = *(const float2*)(m.part_o + (sp * stride + row) * 128 + 2 * lane);
+      o0 = fmaf(w, v.x, o0);
+      o1 = fmaf(w, v.y, o1);
+      wsum += w;
+    }
+    o0 /= wsum;
+    o1 /= wsum;
+  }
+  const int qi = (int)(row % m.Lq);
+  const int64_t bh = row / m.Lq;
+  const int hq = (int)(bh % m.Hq), b = (int)(bh / m.Hq);
+  __bf16* op = m.o + b * m.o_sb + hq * m.o_sh + (int64_t)qi * m.o_sl + 2 * lane;
+  op[0] = (__bf16)o0;
+  op[1] = (__bf16)o1;
+  if (lane == 0 && m.lse) m.lse[row] = mx == -INFINITY ? -INFINITY : mx + logf(wsum);
+}
+
+hipError_t launch_splitkv_merge(const MergeArgs& m, hipStream_t stream) {
+  const int64_t nrows = (int64_t)m.B * m.Hq * m.Lq;
+  if (nrows == 0) return hipSuccess;
+  hipLaunchKernelGGL(splitkv_merge_kernel, dim3((unsigned)((nrows + 3) / 4)), dim3(256), 0, stream, m);
+  return hipGetLastError();
 }
 
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int q_block, int kv_block, int score, hipStream_t stream) {

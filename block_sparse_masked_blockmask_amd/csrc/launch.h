@@ -43,6 +43,22 @@ struct FwdArgs {
   float sm_scale, scale_log2, softcap, inv_softcap;
   const float* slopes;
   int total_wg;
+  // Split-KV: nsplit > 1 cuts each work item's tile list into nsplit contiguous ranges, one
+  // workgroup each; they write normalised partial outputs and their lse to part_o
+  // [nsplit][B][Hq][Lq][128] (fp32) and part_lse [nsplit][B][Hq][Lq] instead of o and lse.
+  int nsplit;
+  float* part_o;
+  float* part_lse;
+};
+
+// Merge of split-KV partial results into o (bf16) and lse.
+struct MergeArgs {
+  const float* part_o;
+  const float* part_lse;
+  __bf16* o;
+  float* lse;
+  int64_t o_sb, o_sh, o_sl;
+  int B, Hq, Lq, nsplit;
 };
 
 // Quantized form: bf16 sources and int8 / E4M3 outputs (element strides; int8 elements are bytes).
@@ -83,5 +99,6 @@ hipError_t launch_fwd_quant(const QuantFwdArgs& a, hipStream_t stream);
 // dtype 0 = f32, 1 = bf16; q_block 128 (f32, bf16) or 256 (bf16); kv_block in {64, 128};
 // score bits FA_SCORE_*.
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int q_block, int kv_block, int score, hipStream_t stream);
+hipError_t launch_splitkv_merge(const MergeArgs& m, hipStream_t stream);
 
 }  // namespace fa

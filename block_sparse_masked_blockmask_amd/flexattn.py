@@ -74,6 +74,12 @@ def lib() -> ctypes.CDLL:
                                    POINTER(FaBlockMask), c_int, c_int, POINTER(FaParams),
                                    POINTER(FaTensor), c_void_p, c_void_p]
         L.flexattn_fwd.restype = c_int
+        L.flexattn_fwd_splitkv_workspace_bytes.argtypes = [c_int] * 4
+        L.flexattn_fwd_splitkv_workspace_bytes.restype = c_size_t
+        L.flexattn_fwd_splitkv.argtypes = [POINTER(FaTensor), POINTER(FaTensor), POINTER(FaTensor),
+                                           POINTER(FaBlockMask), c_int, c_int, POINTER(FaParams),
+                                           POINTER(FaTensor), c_void_p, c_int, c_void_p, c_size_t, c_void_p]
+        L.flexattn_fwd_splitkv.restype = c_int
         L.flexattn_quantize_qkv.argtypes = [POINTER(FaTensor)] * 6 + [c_void_p]
         L.flexattn_quantize_qkv.restype = c_int
         L.flexattn_last_error.argtypes = []
@@ -246,6 +252,38 @@ def flexattn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_mask: 
     bm = ctypes.byref(block_mask.as_struct()) if block_mask is not None else None
     _check(lib().flexattn_fwd(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), bm, mask_kind, score_kind,
                               ctypes.byref(p), ctypes.byref(to), _ptr(lse), _stream(stream)))
+    return out, lse
+
+
+def flexattn_fwd_splitkv_workspace_bytes(B: int, Hq: int, Lq: int, n_splits: int) -> int:
+    return lib().flexattn_fwd_splitkv_workspace_bytes(B, Hq, Lq, n_splits)
+
+
+def flexattn_fwd_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_mask: Optional[BlockMask] = None,
+                         mask_kind: int = FA_MASK_NONE, score_kind: int = FA_SCORE_NONE, *, n_splits: int,
+                         workspace: Optional[torch.Tensor] = None, window: int = 0, prefix_len: int = 0,
+                         softcap: float = 0.0, alibi_slopes=None, q_doc=None, kv_doc=None, sm_scale: float = 0.0,
+                         out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                         return_lse: bool = True, stream=None):
+    """Split-KV forward (flexattn_fwd_splitkv); returns (out, lse). The workspace is allocated
+    when not given (flexattn_fwd_splitkv_workspace_bytes bytes)."""
+    if out is None:
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != tuple(q.shape[:3])):
+        raise ValueError("lse must be a contiguous float32 [B, Hq, Lq] tensor")
+    ws_bytes = flexattn_fwd_splitkv_workspace_bytes(q.shape[0], q.shape[1], q.shape[2], n_splits) if n_splits > 1 else 0
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    tq, tk, tv, to = tensor_desc(q), tensor_desc(k), tensor_desc(v), tensor_desc(out)
+    p = _params(window=window, prefix_len=prefix_len, softcap=softcap, alibi_slopes=alibi_slopes,
+                q_doc=q_doc, kv_doc=kv_doc, sm_scale=sm_scale)
+    bm = ctypes.byref(block_mask.as_struct()) if block_mask is not None else None
+    _check(lib().flexattn_fwd_splitkv(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), bm, mask_kind,
+                                      score_kind, ctypes.byref(p), ctypes.byref(to), _ptr(lse), n_splits,
+                                      _ptr(workspace), workspace.numel() if workspace is not None else 0,
+                                      _stream(stream)))
     return out, lse
 
 

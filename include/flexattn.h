@@ -166,6 +166,22 @@ fa_status flexattn_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* 
                        const fa_block_mask* bm, int mask_kind, int score_kind, const fa_params* p,
                        fa_tensor* out, float* lse, hipStream_t stream);
 
+/* Split-KV forward (the decoding form: few queries against many keys, FlexAttention wiki,
+ * "flex_decoding"): the same result as flexattn_fwd, computed by cutting each work item's
+ * (batch, query head, 128-query block) BlockMask tile list into n_splits contiguous ranges that
+ * run as separate workgroups, so that a handful of query rows still fills the GPU. Each range
+ * writes its normalised output and natural-log lse to `workspace`; a second kernel combines
+ * them per row with weights exp(lse_s - lse), lse = log sum_s exp(lse_s).
+ *   - bf16 only (FA_ERR_UNSUPPORTED otherwise, and for the quantized form or q_block 256);
+ *   - n_splits in [1, 256] (1 is flexattn_fwd and needs no workspace);
+ *   - workspace: device, 16-byte aligned, flexattn_fwd_splitkv_workspace_bytes(B, Hq, Lq,
+ *     n_splits) bytes (fp32 partial outputs [n_splits][B][Hq][Lq][128], then their lse); its
+ *     contents after the call are unspecified. Everything else as flexattn_fwd. */
+size_t flexattn_fwd_splitkv_workspace_bytes(int B, int Hq, int Lq, int n_splits);
+fa_status flexattn_fwd_splitkv(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_block_mask* bm,
+                               int mask_kind, int score_kind, const fa_params* p, fa_tensor* out, float* lse,
+                               int n_splits, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Reason for the last non-OK status returned on this thread ("" if none). */
 const char* flexattn_last_error(void);
 

@@ -167,3 +167,31 @@ def test_quantize_validation():
     assert call(d64, q, q, q8, q8, v8) == fa.FA_ERR_UNSUPPORTED
     short = FaTensor(256, fa.FA_I8, 1, 2, 99, 128, 2 * 100 * 128, 100 * 128, 128, 512)
     assert call(q, q, q, short, q8, v8) == fa.FA_ERR_INVALID_ARG and "shapes" in fa.flexattn_last_error()
+
+
+@pytest.mark.parametrize("case,status,needle", [
+    ("splits0", fa.FA_ERR_INVALID_ARG, "n_splits"),
+    ("splits_big", fa.FA_ERR_INVALID_ARG, "n_splits"),
+    ("f32", fa.FA_ERR_UNSUPPORTED, "bf16"),
+    ("no_ws", fa.FA_ERR_INVALID_ARG, "workspace needs"),
+    ("ws_misaligned", fa.FA_ERR_INVALID_ARG, "16-byte aligned"),
+    ("i8", fa.FA_ERR_UNSUPPORTED, "quantized"),
+])
+def test_splitkv_validation(case, status, needle):
+    """flexattn_fwd_splitkv refuses before enqueuing anything (no GPU needed)."""
+    lib = fa.lib()
+    dt = {"f32": fa.FA_F32, "i8": fa.FA_I8}.get(case, fa.FA_BF16)
+    q, k, v, o = _t(dtype=dt), _t(dtype=dt), _t(dtype=dt), _t(dtype=dt)
+    p = FaParams(0.0, 0, 0, 0.0, None, None, None)
+    n = {"splits0": 0, "splits_big": 257}.get(case, 4)
+    need = lib.flexattn_fwd_splitkv_workspace_bytes(1, 2, 100, 4)
+    assert need == 4 * 2 * 100 * 129 * 4
+    ws, wsb = 4096, need
+    if case == "no_ws":
+        ws, wsb = None, 0
+    if case == "ws_misaligned":
+        ws = 4100
+    st = lib.flexattn_fwd_splitkv(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), None, 0, 0, ctypes.byref(p),
+                                  ctypes.byref(o), None, n, ws, wsb, None)
+    assert st == status, (st, fa.flexattn_last_error())
+    assert needle in fa.flexattn_last_error(), fa.flexattn_last_error()

@@ -22,6 +22,7 @@ order: structure, Q, K, V, then the V channel scales.
 from .synth import (  # noqa: F401
     Workload,
     bf16_bits_to_f32,
+    decode_workload,
     f32_to_bf16_bits,
     grouped_sweep,
     make_workload,

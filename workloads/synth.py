@@ -167,6 +167,15 @@ def grouped_sweep(n_groups: int, dtype: str) -> Workload:
 
 SWEEP_GROUPS = (8, 32, 64, 128)
 
+
+def decode_workload() -> Workload:
+    """Decoding shape: 16 new queries per sequence against 32768 cached keys, B=8, GQA 32/8,
+    D=128, bf16, no mask (the split-KV form's workload)."""
+    rng = np.random.default_rng(6)
+    B, Hq, Hkv, Lq, Lkv = 8, 32, 8, 16, 32768
+    q, k, v = _qkv(rng, B, Hq, Hkv, Lq, Lkv, 128, "bf16")
+    return Workload("decode_b8h32x8_q16_kv32768_bf16", "bf16", B, Hq, Hkv, Lq, Lkv, 128, q, k, v)
+
 WORKLOADS = {
     "grouped_variate_4x17_f32": _tirex_small,
     "grouped_variate_4096g_bf16": _tirex_scale,
