@@ -308,7 +308,12 @@ fa_status fwd_impl(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, c
       return fail(FA_ERR_INVALID_ARG, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
     if (need > 0 && !aligned16(workspace)) return fail(FA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   }
-  const int64_t total = (int64_t)B * q->H * a.nqb * nsplit;
+  // Split-KV with grouped query heads: when all queries of all heads of a kv group fit one
+  // 128-row workgroup (and the BlockMask does not depend on the head), one workgroup per kv head
+  // computes them all and each K/V tile is read once for the group.
+  const int group = q->H / k->H;
+  a.pack = (nsplit > 1 && group > 1 && (int64_t)group * Lq <= 128 && (bm == nullptr || bm->Hm == 1)) ? 1 : 0;
+  const int64_t total = (int64_t)B * (a.pack ? k->H : q->H) * a.nqb * nsplit;
   if (total > 0x7fffffff) return fail(FA_ERR_UNSUPPORTED, "grid too large (%lld workgroups)", (long long)total);
 
   a.q = q->data; a.k = k->data; a.v = v->data; a.o = out->data; a.lse = lse;

@@ -36,7 +36,9 @@ struct WorkItem {
   int b, hq, hkv, qb, split;
 };
 
-template <bool SPLIT = false>
+// MODE 0: plain forward; 1: split-KV; 2: split-KV with the query heads of one kv head packed
+// into one workgroup (rows = (head, query) pairs, all queries of all heads of the group).
+template <int MODE = 0>
 __device__ __forceinline__ WorkItem decode_work(const FwdArgs& a) {
   int w = xcd_remap(blockIdx.x, a.total_wg);
   // Order: splits of one work item fastest (they read the same Q rows), then query heads of
@@ -44,12 +46,15 @@ __device__ __forceinline__ WorkItem decode_work(const FwdArgs& a) {
   // under causal masks) to the first, then kv head, batch.
   WorkItem it;
   it.split = 0;
-  if constexpr (SPLIT) {
+  if constexpr (MODE > 0) {
     it.split = w % a.nsplit;
     w /= a.nsplit;
   }
-  const int g = w % a.group;
-  w /= a.group;
+  int g = 0;
+  if constexpr (MODE != 2) {
+    g = w % a.group;
+    w /= a.group;
+  }
   const int qbr = w % a.nqb;
   w /= a.nqb;
   it.hkv = w % a.Hkv;
@@ -209,6 +214,7 @@ struct StepInfo {
 struct Ctx {
   int wave, lane, hl, lq, g16, s16;
   int qw0, qw1, qi;
+  int hq;                // query head of this lane's row
   bool q_in, doc;
   int qdoc, qd_min, qd_max;
   float slope;
@@ -301,7 +307,7 @@ __device__ __forceinline__ void key_interval(const FwdArgs& a, int qi, int& lo, 
 // kv0n) into buffer ISSUE, spread between its S products when both sub-blocks are live (a wave
 // is held while its transfers are accepted, and the memory pipeline accepts about 64 bytes per
 // cycle per CU, so issuing them back to back stalls every wave of the CU), else up front.
-template <int B, int SCORE, bool MASKED, bool DOC, int ISSUE, int WAVES, bool SPLIT>
+template <int B, int SCORE, bool MASKED, bool DOC, int ISSUE, int WAVES, int MODE>
 __device__ __forceinline__ void compute_step(const FwdArgs& a, const Ctx& c, const bf16x8 (&qreg)[8], State& st,
                                              const int kv0, const int kv0n) {
   constexpr int NSEG = 2 * (16 / WAVES);  // row transfers per wave and step
@@ -317,7 +323,7 @@ __device__ __forceinline__ void compute_step(const FwdArgs& a, const Ctx& c, con
   asm volatile("" : "+v"(dx));
   // This lane's query and its key interval, recomputed per step from the wave's first query
   // (scalar) and the lane's row (kx0 / 256): kept across the loop they would be spilled.
-  const int qi = c.qw0 + (kx0 >> 8);
+  const int qi = MODE == 2 ? c.qi : c.qw0 + (kx0 >> 8);
   int lo = 0, hi = 0;
   if constexpr (MASKED) key_interval(a, qi, lo, hi);
 
@@ -497,7 +503,7 @@ __device__ __forceinline__ void compute_step(const FwdArgs& a, const Ctx& c, con
   };
 
   if constexpr (!MASKED) {
-    if (SPLIT && c.qw0 >= a.Lq) {
+    if (MODE > 0 && c.qw0 >= a.Lq) {
       // A wave past the last query (few query rows, as in decoding) only does its share of the
       // transfers; its products would be discarded. (Masked steps find this in the liveness test.)
       if constexpr (ISSUE >= 0) {
@@ -528,15 +534,16 @@ struct StepPlan {
 
 }  // namespace
 
-// SPLIT: the split-KV form (a range of each tile list, partial results; waves without a query
-// skip the products). A separate instantiation, so that the plain forward carries none of it.
-template <int TB, int SCORE, int WAVES, int NBUF, bool SPLIT>
+// MODE > 0: the split-KV form (a range of each tile list, partial results; waves without a
+// query skip the products); MODE 2 also packs the query heads of one kv head (see decode_work).
+// Separate instantiations, so that the plain forward carries none of it.
+template <int TB, int SCORE, int WAVES, int NBUF, int MODE>
 __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(FwdArgs a) {
   constexpr int HALVES = TB / kStep;
   constexpr int BQ = 32 * WAVES;
   constexpr int OPS = step_ops<WAVES>();
 
-  const WorkItem it = decode_work<SPLIT>(a);
+  const WorkItem it = decode_work<MODE>(a);
   Ctx c;
   c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar registers
   c.lane = threadIdx.x & 63;
@@ -544,10 +551,22 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(FwdArgs
   c.lq = c.lane & 31;
   c.g16 = c.lane >> 4;
   c.s16 = c.lane & 15;
-  c.qw0 = it.qb * BQ + c.wave * 32;
-  c.qw1 = min(c.qw0 + 31, a.Lq - 1);
-  c.qi = c.qw0 + c.lq;
-  c.q_in = c.qi < a.Lq;
+  if constexpr (MODE == 2) {
+    // Row r = 32 * wave + lq holds query r % Lq of head r / Lq of the group (group * Lq <= 128).
+    const int r = c.wave * 32 + c.lq;
+    const int g = r / a.Lq;
+    c.qi = r - g * a.Lq;
+    c.q_in = g < a.group;
+    c.hq = it.hkv * a.group + min(g, a.group - 1);
+    c.qw0 = wave_min32(c.q_in ? c.qi : INT_MAX);  // INT_MAX: the wave holds no row
+    c.qw1 = wave_max32(c.q_in ? c.qi : INT_MIN);
+  } else {
+    c.qw0 = it.qb * BQ + c.wave * 32;
+    c.qw1 = min(c.qw0 + 31, a.Lq - 1);
+    c.qi = c.qw0 + c.lq;
+    c.q_in = c.qi < a.Lq;
+    c.hq = it.hq;
+  }
   c.doc = (a.flags & FA_MASK_DOC) != 0;
   c.kp = (const __bf16*)a.k + it.b * a.k_sb + it.hkv * a.k_sh;
   c.vp = (const __bf16*)a.v + it.b * a.v_sb + it.hkv * a.v_sh;
@@ -573,7 +592,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(FwdArgs
   // Addresses are clamped or redirected to valid memory instead of branching around the loads;
   // the values are discarded afterwards where they do not apply.
   // Q^T as the B operand: lane holds Q[qi][16*ks + 8*hl .. +8] for ks = 0..7.
-  const __bf16* qp = (const __bf16*)a.q + it.b * a.q_sb + it.hq * a.q_sh;
+  const __bf16* qp = (const __bf16*)a.q + it.b * a.q_sb + c.hq * a.q_sh;
   const int qi_c = min(c.qi, a.Lq - 1);
   bf16x8 qreg[8];
 #pragma unroll
@@ -588,7 +607,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(FwdArgs
     // Without a BlockMask the list pointers are null, and with no key block (n_kvb = 0) the
     // index rows are empty: the list reads then go to this head's first Q row (256 bytes, 64
     // ints, always present when a workgroup runs) and are ignored.
-    const int* dummy = (const int*)qp;
+    const int* dummy = (const int*)((const __bf16*)a.q + it.b * a.q_sb + it.hq * a.q_sh);
     const bool no_lists = a.all_full || a.nkvb == 0;
     tl.full = no_lists ? dummy : a.full_idx + row * a.nkvb;
     tl.part = no_lists ? dummy : a.kv_idx + row * a.nkvb;
@@ -613,7 +632,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(FwdArgs
   const int ntiles = tl.nfull + tl.npart;
   // Split-KV: this workgroup takes list entries [t_begin, t_end).
   int t_begin = 0, t_end = ntiles;
-  if constexpr (SPLIT) {
+  if constexpr (MODE > 0) {
     t_begin = (int)((int64_t)it.split * ntiles / a.nsplit);
     t_end = (int)((int64_t)(it.split + 1) * ntiles / a.nsplit);
   }
@@ -627,7 +646,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(FwdArgs
   };
   int chunk_base = 0;
   int chunk = chunk_init;
-  c.slope = (SCORE & FA_SCORE_ALIBI) ? a.slopes[it.hq] : 0.f;
+  c.slope = (SCORE & FA_SCORE_ALIBI) ? a.slopes[c.hq] : 0.f;
 
   // Step s -> StepInfo (steps past the end re-read row 0 and are not computed).
   auto info = [&](int s) {
@@ -683,15 +702,15 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(FwdArgs
     ring[NB] = nxt;
     if (cur.ok && nxt.kv0 + kStep <= a.Lkv) {
       // The step's own compute issues the next step's transfers.
-      if (!cur.masked) compute_step<B, SCORE, false, false, NB, WAVES, SPLIT>(a, c, qreg, st, cur.kv0, nxt.kv0);
-      else if (c.doc) compute_step<B, SCORE, true, true, NB, WAVES, SPLIT>(a, c, qreg, st, cur.kv0, nxt.kv0);
-      else compute_step<B, SCORE, true, false, NB, WAVES, SPLIT>(a, c, qreg, st, cur.kv0, nxt.kv0);
+      if (!cur.masked) compute_step<B, SCORE, false, false, NB, WAVES, MODE>(a, c, qreg, st, cur.kv0, nxt.kv0);
+      else if (c.doc) compute_step<B, SCORE, true, true, NB, WAVES, MODE>(a, c, qreg, st, cur.kv0, nxt.kv0);
+      else compute_step<B, SCORE, true, false, NB, WAVES, MODE>(a, c, qreg, st, cur.kv0, nxt.kv0);
     } else {
       issue_step<NB, WAVES>(a, c, nxt);
       if (cur.ok) {
-        if (!cur.masked) compute_step<B, SCORE, false, false, -1, WAVES, SPLIT>(a, c, qreg, st, cur.kv0, 0);
-        else if (c.doc) compute_step<B, SCORE, true, true, -1, WAVES, SPLIT>(a, c, qreg, st, cur.kv0, 0);
-        else compute_step<B, SCORE, true, false, -1, WAVES, SPLIT>(a, c, qreg, st, cur.kv0, 0);
+        if (!cur.masked) compute_step<B, SCORE, false, false, -1, WAVES, MODE>(a, c, qreg, st, cur.kv0, 0);
+        else if (c.doc) compute_step<B, SCORE, true, true, -1, WAVES, MODE>(a, c, qreg, st, cur.kv0, 0);
+        else compute_step<B, SCORE, true, false, -1, WAVES, MODE>(a, c, qreg, st, cur.kv0, 0);
       }
     }
   };
@@ -708,10 +727,10 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(FwdArgs
   // Epilogue: combine the two halves' row sums, normalise, store O (bf16) and the natural-log lse.
   const float l_tot = half_swap_sum(st.l_run);
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-  if constexpr (SPLIT) {
+  if constexpr (MODE > 0) {
     // Split-KV partial result: normalised O in fp32 and the lse of this range of tiles.
     if (c.q_in) {
-      const int64_t prow = (((int64_t)it.split * a.B + it.b) * a.Hq + it.hq) * a.Lq + c.qi;
+      const int64_t prow = (((int64_t)it.split * a.B + it.b) * a.Hq + c.hq) * a.Lq + c.qi;
       float* po = a.part_o + prow * 128;
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
@@ -899,11 +918,13 @@ template <int BK, int SCORE>
 static hipError_t launch_t(const FwdArgs& a, int dtype, int q_block, hipStream_t stream) {
   if (dtype == 1) {
     if (q_block == 256)
-      hipLaunchKernelGGL((fwd_bf16_kernel<BK, SCORE, 8, 4, false>), dim3(a.total_wg), dim3(512), 0, stream, a);
+      hipLaunchKernelGGL((fwd_bf16_kernel<BK, SCORE, 8, 4, 0>), dim3(a.total_wg), dim3(512), 0, stream, a);
+    else if (a.nsplit > 1 && a.pack)
+      hipLaunchKernelGGL((fwd_bf16_kernel<BK, SCORE, 4, 2, 2>), dim3(a.total_wg), dim3(256), 0, stream, a);
     else if (a.nsplit > 1)
-      hipLaunchKernelGGL((fwd_bf16_kernel<BK, SCORE, 4, 2, true>), dim3(a.total_wg), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((fwd_bf16_kernel<BK, SCORE, 4, 2, 1>), dim3(a.total_wg), dim3(256), 0, stream, a);
     else
-      hipLaunchKernelGGL((fwd_bf16_kernel<BK, SCORE, 4, 2, false>), dim3(a.total_wg), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((fwd_bf16_kernel<BK, SCORE, 4, 2, 0>), dim3(a.total_wg), dim3(256), 0, stream, a);
   } else {
     hipLaunchKernelGGL((fwd_f32_kernel<BK, SCORE>), dim3(a.total_wg), dim3(256), 0, stream, a);
   }

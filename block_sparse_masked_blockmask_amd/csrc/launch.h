@@ -49,6 +49,7 @@ struct FwdArgs {
   int nsplit;
   float* part_o;
   float* part_lse;
+  int pack;  // with nsplit > 1: one workgroup per kv head holds all (query head, query) rows
 };
 
 // Merge of split-KV partial results into o (bf16) and lse.

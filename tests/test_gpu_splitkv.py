@@ -1,5 +1,6 @@
 """GPU: the split-KV forward (decoding form) matches the fp64 oracle for every split count,
-including more splits than tiles (empty ranges), GQA, masks and score mods."""
+including more splits than tiles (empty ranges), GQA (also with the query heads of a kv head
+packed into one workgroup), masks and score mods."""
 import numpy as np
 import pytest
 
@@ -16,6 +17,10 @@ CASES = [
     (13, dict(B=1, Hq=4, Hkv=2, Lq=16, Lkv=1500, window=600, softcap=30.0, alibi=True), "window+softcap+alibi"),
     (14, dict(B=1, Hq=2, Lq=300, Lkv=900, causal=True), "causal, several query blocks"),
     (15, dict(B=1, Hq=2, Lq=5, Lkv=500), "few tiles"),
+    # grouped query heads packed into one workgroup per kv head (group * Lq <= 128)
+    (16, dict(B=1, Hq=6, Hkv=2, Lq=7, Lkv=1200, doc=True, n_docs=2), "packed GQA, doc"),
+    (17, dict(B=2, Hq=8, Hkv=2, Lq=16, Lkv=900, causal=True, softcap=20.0), "packed GQA, causal+softcap"),
+    (18, dict(B=1, Hq=16, Hkv=2, Lq=16, Lkv=700, alibi=True), "packed GQA, 8 heads x 16 queries"),
 ]
 
 
