@@ -23,6 +23,11 @@ PyTorch 2.5"; sage2 form = FlashRT-Structures PR #1 "LTX-2.5 attention forms"):
                 floating point specification (OFP8, E4M3).
   brute.py      pure-Python loops on tiny inputs; an independent restatement used
                 only to pin attention.py.
+  backward.py   dQ, dK, dV and the ALiBi-slope gradient of attention.py's output —
+                guide "Systems Mechanics", item 2 (automatic differentiation of the
+                score_mod, gradients into learnable slopes); the derivative written
+                out by hand. blockmask.transposed_block_mask gives the per-kv-block
+                q-block lists a backward walks.
 
 Parity status: every function here is pinned by tests under tests/ marked
 "not gpu" (library routines, closed forms, invariants, brute force), except the

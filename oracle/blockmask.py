@@ -74,3 +74,35 @@ def block_mask(spec, B, Lq, Lkv, BQ=128, BK=128, rows=None):
 def tile_counts(bm_dict):
     """(full, partial) tile totals over all rows."""
     return int(bm_dict["full_kv_num_blocks"].sum()), int(bm_dict["kv_num_blocks"].sum())
+
+
+def transposed_block_mask(spec, B, Lq, Lkv, BQ=128, BK=128):
+    """The column view of the same tile classes, for a backward that walks kv blocks.
+
+    For each mask row bm and kv block kb: the q blocks whose (qb, kb) tile is
+    partial (q_indices) or full (full_q_indices), ascending, with their counts;
+    unused entries 0. Shapes: q_num_blocks / full_q_num_blocks [Bm][Hm][nKVB],
+    q_indices / full_q_indices [Bm][Hm][nKVB][nQB]. (The pages give no layout;
+    the field names follow FlexAttention's BlockMask, whose backward needs this
+    view of the tiles.)
+    """
+    Bm, Hm, nqb, nkvb = dims(spec, B, Lq, Lkv, BQ, BK)
+    cls = np.zeros((Bm, nqb, nkvb), np.int32)
+    for bm in range(Bm):
+        for qb in range(nqb):
+            cls[bm, qb] = _row_classes(spec, bm, qb, Lq, Lkv, BQ, BK)
+    out = {
+        "q_num_blocks": np.zeros((Bm, Hm, nkvb), np.int32),
+        "q_indices": np.zeros((Bm, Hm, nkvb, nqb), np.int32),
+        "full_q_num_blocks": np.zeros((Bm, Hm, nkvb), np.int32),
+        "full_q_indices": np.zeros((Bm, Hm, nkvb, nqb), np.int32),
+    }
+    for bm in range(Bm):
+        for kb in range(nkvb):
+            part = np.flatnonzero(cls[bm, :, kb] == 1)
+            full = np.flatnonzero(cls[bm, :, kb] == 2)
+            out["q_num_blocks"][bm, 0, kb] = len(part)
+            out["q_indices"][bm, 0, kb, :len(part)] = part
+            out["full_q_num_blocks"][bm, 0, kb] = len(full)
+            out["full_q_indices"][bm, 0, kb, :len(full)] = full
+    return out
