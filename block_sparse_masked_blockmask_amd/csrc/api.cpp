@@ -471,4 +471,155 @@ static fa_status fwd_quantized(const fa_tensor* q, const fa_tensor* k, const fa_
 }
 
 
+
+size_t flexattn_bwd_workspace_bytes(int B, int Hq, int Lq) {
+  if (B < 0 || Hq < 0 || Lq < 0) return 0;
+  const size_t rows = (size_t)B * Hq * Lq;
+  const size_t rows4 = (rows + 3) / 4 * 4;  // keeps each part 16-byte aligned
+  return (2 * rows4 + (size_t)B * Hq * cdiv(Lq, 128)) * sizeof(float);
+}
+
+fa_status flexattn_block_mask_transpose(const fa_block_mask* bm, fa_block_mask_transposed* out, hipStream_t stream) {
+  if (bm == nullptr || out == nullptr) return fail(FA_ERR_INVALID_ARG, "bm and out must not be NULL");
+  if (out->Bm != bm->Bm || out->Hm != bm->Hm || out->q_len != bm->q_len || out->kv_len != bm->kv_len ||
+      out->q_block != bm->q_block || out->kv_block != bm->kv_block || out->n_qb != bm->n_qb || out->n_kvb != bm->n_kvb)
+    return fail(FA_ERR_INVALID_ARG, "out's dimensions must equal the BlockMask's");
+  if (bm->Bm <= 0 || bm->Hm <= 0 || bm->q_block <= 0 || bm->kv_block <= 0 || bm->q_len < 0 || bm->kv_len < 0 ||
+      bm->n_qb != cdiv(bm->q_len, bm->q_block) || bm->n_kvb != cdiv(bm->kv_len, bm->kv_block))
+    return fail(FA_ERR_INVALID_ARG, "BlockMask dimensions are inconsistent");
+  if ((int64_t)bm->Bm * bm->Hm * bm->n_kvb > ((int64_t)1 << 31) - 4)
+    return fail(FA_ERR_UNSUPPORTED, "too many BlockMask columns");
+  if (bm->n_qb > 0 && bm->n_kvb > 0 &&
+      (!bm->kv_num_blocks || !bm->full_kv_num_blocks || !bm->kv_indices || !bm->full_kv_indices))
+    return fail(FA_ERR_INVALID_ARG, "BlockMask arrays are NULL");
+  if (bm->n_kvb > 0 && (!out->q_num_blocks || !out->full_q_num_blocks || (bm->n_qb > 0 && (!out->q_indices || !out->full_q_indices))))
+    return fail(FA_ERR_INVALID_ARG, "transposed BlockMask arrays are NULL");
+  fa::TransposeArgs t{};
+  t.Bm = bm->Bm;
+  t.Hm = bm->Hm;
+  t.nqb = bm->n_qb;
+  t.nkvb = bm->n_kvb;
+  t.kv_num = bm->kv_num_blocks;
+  t.kv_idx = bm->kv_indices;
+  t.full_num = bm->full_kv_num_blocks;
+  t.full_idx = bm->full_kv_indices;
+  t.q_num = out->q_num_blocks;
+  t.q_idx = out->q_indices;
+  t.fullq_num = out->full_q_num_blocks;
+  t.fullq_idx = out->full_q_indices;
+  hipError_t e = fa::launch_block_mask_transpose(t, stream);
+  if (e != hipSuccess) return fail(FA_ERR_DEVICE, "transpose launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+fa_status flexattn_bwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* out,
+                       const fa_tensor* dout, const float* lse, const fa_block_mask* bm,
+                       const fa_block_mask_transposed* bmt, int mask_kind, int score_kind, const fa_params* p,
+                       fa_tensor* dq, fa_tensor* dk, fa_tensor* dv, float* dslopes, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  if (!q || !k || !v || !out || !dout || !dq || !dk || !dv)
+    return fail(FA_ERR_INVALID_ARG, "q, k, v, out, dout, dq, dk and dv must not be NULL");
+  const fa_tensor* all[8] = {q, k, v, out, dout, dq, dk, dv};
+  const char* names[8] = {"q", "k", "v", "out", "dout", "dq", "dk", "dv"};
+  for (int i = 0; i < 8; ++i) {
+    if (all[i]->dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "the backward serves bf16 tensors (%s)", names[i]);
+    fa_status st = check_tensor(all[i], names[i], 8);
+    if (st != FA_OK) return st;
+    if (all[i]->D != 128) return fail(FA_ERR_UNSUPPORTED, "head dim must be 128 (%s has %d)", names[i], all[i]->D);
+    if (all[i]->B != q->B) return fail(FA_ERR_INVALID_ARG, "batch sizes differ (%s)", names[i]);
+  }
+  if (k->H != v->H || k->L != v->L || dk->H != k->H || dk->L != k->L || dv->H != k->H || dv->L != k->L)
+    return fail(FA_ERR_INVALID_ARG, "k, v, dk and dv must share one shape");
+  if (out->H != q->H || out->L != q->L || dout->H != q->H || dout->L != q->L || dq->H != q->H || dq->L != q->L)
+    return fail(FA_ERR_INVALID_ARG, "q, out, dout and dq must share one shape");
+  if (q->H % k->H != 0) return fail(FA_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", q->H, k->H);
+  const int B = q->B, Hq = q->H, Lq = q->L, Lkv = k->L;
+  if (lse == nullptr && (int64_t)B * Hq * Lq > 0) return fail(FA_ERR_INVALID_ARG, "lse is NULL");
+  if (reinterpret_cast<uintptr_t>(lse) & 3u) return fail(FA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  fa_status st;
+  if ((st = check_mask(mask_kind, p, Lq, Lkv)) != FA_OK) return st;
+  if (score_kind & ~kValidScore) return fail(FA_ERR_INVALID_ARG, "unknown score_kind bits 0x%x", score_kind);
+  if (score_kind != FA_SCORE_NONE && p == nullptr) return fail(FA_ERR_INVALID_ARG, "params is NULL");
+  if ((score_kind & FA_SCORE_ALIBI) && p->alibi_slopes == nullptr)
+    return fail(FA_ERR_INVALID_ARG, "ALIBI needs alibi_slopes");
+  if ((score_kind & FA_SCORE_SOFTCAP) && !(p->softcap > 0.f)) return fail(FA_ERR_INVALID_ARG, "SOFTCAP needs softcap > 0");
+  if (dslopes != nullptr && !(score_kind & FA_SCORE_ALIBI))
+    return fail(FA_ERR_INVALID_ARG, "dslopes is only written with ALIBI; pass NULL");
+  if (reinterpret_cast<uintptr_t>(dslopes) & 3u) return fail(FA_ERR_INVALID_ARG, "dslopes must be 4-byte aligned");
+  const int nqb = cdiv(Lq, 128), nkvb = cdiv(Lkv, 128);
+  if ((int64_t)B * Hq * nqb > 0x7fffffff || (int64_t)B * k->H * nkvb > 0x7fffffff || Hq > 65535)
+    return fail(FA_ERR_UNSUPPORTED, "grid too large");
+
+  fa::BwdArgs a{};
+  if (bm == nullptr || bmt == nullptr) {
+    if (bm != nullptr || bmt != nullptr)
+      return fail(FA_ERR_INVALID_ARG, "pass both the BlockMask and its transpose, or neither");
+    if (mask_kind != FA_MASK_NONE) return fail(FA_ERR_INVALID_ARG, "a BlockMask is required unless mask_kind is NONE");
+    a.all_full = 1;
+    a.Bm = a.Hm = 1;
+  } else {
+    if (bm->q_len != Lq || bm->kv_len != Lkv)
+      return fail(FA_ERR_INVALID_ARG, "BlockMask was built for lengths (%d, %d), not (%d, %d)", bm->q_len, bm->kv_len, Lq, Lkv);
+    if (bm->q_block != 128 || bm->kv_block != 128)
+      return fail(FA_ERR_UNSUPPORTED, "the backward needs 128 x 128 BlockMask tiles (got %d x %d)", bm->q_block, bm->kv_block);
+    if (bm->n_qb != nqb || bm->n_kvb != nkvb)
+      return fail(FA_ERR_INVALID_ARG, "BlockMask n_qb/n_kvb do not match its lengths and block sizes");
+    if (bm->Bm != 1 && bm->Bm != B) return fail(FA_ERR_INVALID_ARG, "BlockMask Bm must be 1 or B");
+    if (bm->Hm != 1 && bm->Hm != Hq) return fail(FA_ERR_INVALID_ARG, "BlockMask Hm must be 1 or Hq");
+    if (bmt->Bm != bm->Bm || bmt->Hm != bm->Hm || bmt->q_len != Lq || bmt->kv_len != Lkv || bmt->q_block != 128 ||
+        bmt->kv_block != 128 || bmt->n_qb != nqb || bmt->n_kvb != nkvb)
+      return fail(FA_ERR_INVALID_ARG, "the transposed BlockMask's dimensions differ from the BlockMask's");
+    if (nqb > 0 && nkvb > 0 &&
+        (!bm->kv_num_blocks || !bm->full_kv_num_blocks || !bm->kv_indices || !bm->full_kv_indices ||
+         !bmt->q_num_blocks || !bmt->full_q_num_blocks || !bmt->q_indices || !bmt->full_q_indices))
+      return fail(FA_ERR_INVALID_ARG, "BlockMask arrays are NULL");
+    a.all_full = 0;
+    a.Bm = bm->Bm;
+    a.Hm = bm->Hm;
+    a.kv_num = bm->kv_num_blocks;
+    a.kv_idx = bm->kv_indices;
+    a.full_num = bm->full_kv_num_blocks;
+    a.full_idx = bm->full_kv_indices;
+    a.q_num = bmt->q_num_blocks;
+    a.q_idx = bmt->q_indices;
+    a.fullq_num = bmt->full_q_num_blocks;
+    a.fullq_idx = bmt->full_q_indices;
+  }
+  const size_t need = flexattn_bwd_workspace_bytes(B, Hq, Lq);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(FA_ERR_INVALID_ARG, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+  if (!aligned16(workspace)) return fail(FA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+
+  a.q = q->data; a.k = k->data; a.v = v->data; a.o = out->data; a.dout = dout->data; a.lse = lse;
+  a.dq = dq->data; a.dk = dk->data; a.dv = dv->data; a.dslopes = dslopes;
+  a.q_sb = q->stride_b; a.q_sh = q->stride_h; a.q_sl = q->stride_l;
+  a.k_sb = k->stride_b; a.k_sh = k->stride_h; a.k_sl = k->stride_l;
+  a.v_sb = v->stride_b; a.v_sh = v->stride_h; a.v_sl = v->stride_l;
+  a.o_sb = out->stride_b; a.o_sh = out->stride_h; a.o_sl = out->stride_l;
+  a.do_sb = dout->stride_b; a.do_sh = dout->stride_h; a.do_sl = dout->stride_l;
+  a.dq_sb = dq->stride_b; a.dq_sh = dq->stride_h; a.dq_sl = dq->stride_l;
+  a.dk_sb = dk->stride_b; a.dk_sh = dk->stride_h; a.dk_sl = dk->stride_l;
+  a.dv_sb = dv->stride_b; a.dv_sh = dv->stride_h; a.dv_sl = dv->stride_l;
+  a.B = B; a.Hq = Hq; a.Hkv = k->H; a.Lq = Lq; a.Lkv = Lkv; a.group = Hq / k->H;
+  a.nqb = nqb;
+  a.nkvb = nkvb;
+  a.flags = mask_kind;
+  a.window = (mask_kind & FA_MASK_WINDOW) ? p->window : 0;
+  a.prefix_len = (mask_kind & FA_MASK_PREFIX_LM) ? p->prefix_len : 0;
+  a.q_doc = (mask_kind & FA_MASK_DOC) ? p->q_doc : nullptr;
+  a.kv_doc = (mask_kind & FA_MASK_DOC) ? p->kv_doc : nullptr;
+  a.sm_scale = (p && p->sm_scale > 0.f) ? p->sm_scale : 1.0f / std::sqrt((float)q->D);
+  a.softcap = (score_kind & FA_SCORE_SOFTCAP) ? p->softcap : 0.f;
+  a.inv_softcap = (score_kind & FA_SCORE_SOFTCAP) ? 1.0f / p->softcap : 0.f;
+  a.slopes = (score_kind & FA_SCORE_ALIBI) ? p->alibi_slopes : nullptr;
+  const size_t rows = (size_t)B * Hq * Lq, rows4 = (rows + 3) / 4 * 4;
+  float* ws = static_cast<float*>(workspace);
+  a.lse2 = ws;
+  a.delta = ws ? ws + rows4 : nullptr;
+  a.slope_part = (dslopes != nullptr && ws) ? ws + 2 * rows4 : nullptr;  // read only when rows > 0
+  hipError_t e = fa::launch_bwd(a, score_kind, stream);
+  if (e != hipSuccess) return fail(FA_ERR_DEVICE, "backward launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 }  // extern "C"

@@ -1,0 +1,572 @@
+// Block-sparse masked attention backward for gfx950 (CDNA4), bf16, head dim 128.
+//
+// Method (FlexAttention guide, "Systems Mechanics", item 2): the backward of the fused forward
+// gives dQ, dK and dV, differentiates the score_mod, and lets gradients reach learnable score_mod
+// parameters (ALiBi slopes). It walks the same BlockMask tiles as the forward: full tiles without
+// the mask, partial tiles with it, empty tiles never.
+//
+// With r = q.k (raw product), s = r * sm_scale, a = s - slope |i - j| (ALiBi), f = C tanh(a / C)
+// (soft-cap, else f = a), P = exp(f - lse) on allowed pairs and 0 elsewhere:
+//   dV = P^T dO,  dP = dO V^T,  dF = P (dP - delta), delta_i = dO_i . O_i,
+//   dA = dF (1 - (f / C)^2)  (soft-cap; dA = dF without),  dslope_h = -sum dA |i - j|,
+//   dQ = sm_scale dA K,  dK = sm_scale dA^T Q.
+// P is recomputed from the forward's lse, so nothing of size Lq x Lkv is stored.
+//
+// Kernels:
+//   bwd_prep_kernel     delta = rowsum(dO * O) and lse2 = lse * log2(e) (+inf for a row with no
+//                       allowed key, so its probabilities are exactly 0);
+//   bwd_dq_kernel       one workgroup of 4 waves per (b, query head, 128-query block), walking the
+//                       row's BlockMask tiles in steps of 64 keys. Orientation of the forward:
+//                       each wave computes S^T = K Q^T and dP^T = V dO^T with Q^T and dO^T held
+//                       in registers as B operands (a lane owns one query), then
+//                       dQ^T += K^T dA^T with dA^T straight from the accumulators as the B
+//                       operand and K^T read from LDS with ds_read_b64_tr_b16. Also sums the
+//                       ALiBi-slope gradient of its rows;
+//   bwd_dkdv_kernel     one workgroup of 4 waves per (b, kv head, 128-key block), walking the
+//                       column's q blocks (the transposed BlockMask) for every query head of the
+//                       group, in steps of 64 queries. Mirrored orientation: S = Q K^T and
+//                       dP = dO V^T with K^T and V^T held in registers (a lane owns one key),
+//                       then dV^T += dO^T P and dK^T += Q^T dA, both A operands read transposed
+//                       from LDS. GQA sums over the group inside the workgroup (no atomics);
+//   bwd_slope_kernel    sums the per-block slope partials into dslopes[h] (deterministic).
+//
+// Accumulator layout (32x32 MFMA): element i of lane l holds row 8*(i/4) + 4*(l/32) + i%4 and
+// column l%32. Tiles in LDS are [64 rows][128 bf16] with 16-byte chunks XOR-swizzled by row
+// (tile_off), which serves both the row reads of A operands and the transposed reads.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace fa {
+
+namespace {
+
+constexpr int kRows = 64;                  // rows per LDS tile and per step
+constexpr int kTileBytes = kRows * 256;    // [64][128] bf16
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
+
+// Transposed-read base offset of this lane (see the forward kernel): in each 16-lane group,
+// source lane s points at row (g/2)*4 + s/4 and channels 16*(g%2) + 4*(s%4); lane i of the
+// group then receives X[row0 + j][d0 + i], j = 0..3.
+__device__ __forceinline__ int tr_base(int lane) {
+  const int g16 = lane >> 4, s16 = lane & 15;
+  const int d = 16 * (g16 & 1) + 4 * (s16 & 3);
+  const int r0 = (g16 >> 1) * 4 + (s16 >> 2);
+  return tile_off(r0, d >> 3) + (d & 7) * 2;
+}
+
+// A operand of X^T (row = channel in block db, k = 16 tile rows from row0, in the order of the
+// accumulator rows i = 8h .. 8h+7 of a 32x32 tile) from a swizzled [rows][128] tile.
+__device__ __forceinline__ bf16x8 read_xt(const unsigned char* tile, int row0, int db, int tb) {
+  const unsigned char* base = tile + row0 * 256;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(base + (tb ^ (64 * db))));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(base + (tb ^ (64 * db + 2080))));
+  const i16x8 cat = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, cat);
+}
+
+// A operand of X (row = tile row r, k = channels 16 ks + 8 hl .. +8).
+__device__ __forceinline__ bf16x8 read_x(const unsigned char* tile, int r, int ks, int hl) {
+  return *(const bf16x8*)(tile + tile_off(r, 2 * ks + hl));
+}
+
+// Score and its derivative factor for one pair: returns f (natural units) and sets dfac =
+// d f / d a (1 - tanh^2 under soft-cap, else 1).
+template <int SCORE>
+__device__ __forceinline__ float score_f(const BwdArgs& a, float r, int qi, int kv, float slope, float& dfac) {
+  float s = r * a.sm_scale;
+  if constexpr (SCORE & FA_SCORE_ALIBI) s = fmaf(-slope, fabsf((float)(qi - kv)), s);
+  dfac = 1.0f;
+  if constexpr (SCORE & FA_SCORE_SOFTCAP) {
+    const float th = fast_tanh(s * a.inv_softcap);
+    dfac = 1.0f - th * th;
+    s = a.softcap * th;
+  }
+  return s;
+}
+
+// Stage rows [r0, r0 + 64) of two [L][128] bf16 tensors into registers (4 chunks of 16 bytes
+// per thread and tensor); rows at or past L read row L - 1 and are zeroed when stored.
+struct Stage {
+  i32x4 x[4], y[4];
+};
+
+__device__ __forceinline__ void stage_load(Stage& st, const __bf16* xp, int64_t xsl, const __bf16* yp, int64_t ysl,
+                                           int r0, int L, int tid) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int id = tid + 256 * u;
+    const int r = min(r0 + (id >> 4), L - 1);
+    const int ch = id & 15;
+    st.x[u] = *(const i32x4*)(xp + (int64_t)r * xsl + ch * 8);
+    st.y[u] = *(const i32x4*)(yp + (int64_t)r * ysl + ch * 8);
+  }
+}
+
+__device__ __forceinline__ void stage_store(const Stage& st, unsigned char* sx, unsigned char* sy, int r0, int L,
+                                            int tid) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int id = tid + 256 * u;
+    const int r = id >> 4, ch = id & 15;
+    const bool in = r0 + r < L;
+    *(i32x4*)(sx + tile_off(r, ch)) = in ? st.x[u] : i32x4{0, 0, 0, 0};
+    *(i32x4*)(sy + tile_off(r, ch)) = in ? st.y[u] : i32x4{0, 0, 0, 0};
+  }
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+}  // namespace
+
+// delta = rowsum(dO * O) in fp32 and lse2 = lse * log2(e) (+inf where lse = -inf); 16 threads
+// per row, 16 rows per workgroup.
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
+  const int64_t rows = (int64_t)a.B * a.Hq * a.Lq;
+  const int64_t r = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int c = threadIdx.x & 15;
+  float acc = 0.f;
+  if (r < rows) {
+    const int qi = (int)(r % a.Lq);
+    const int64_t t = r / a.Lq;
+    const int hq = (int)(t % a.Hq), b = (int)(t / a.Hq);
+    const bf16x8 o = *(const bf16x8*)((const __bf16*)a.o + b * a.o_sb + hq * a.o_sh + (int64_t)qi * a.o_sl + c * 8);
+    const bf16x8 d = *(const bf16x8*)((const __bf16*)a.dout + b * a.do_sb + hq * a.do_sh + (int64_t)qi * a.do_sl + c * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = fmaf((float)o[e], (float)d[e], acc);
+  }
+#pragma unroll
+  for (int off = 8; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if (c == 0 && r < rows) {
+    a.delta[r] = acc;
+    const float l = a.lse[r];
+    a.lse2[r] = l == -INFINITY ? INFINITY : l * kLog2e;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// dQ (and the slope-gradient partials): one workgroup per (b, hq, 128-query block).
+// ---------------------------------------------------------------------------------------------
+template <int SCORE>
+__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(1024))) unsigned char sK[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char sV[kTileBytes];
+  __shared__ int sDoc[kRows];
+  __shared__ float sRed[4];
+
+  int w = blockIdx.x;
+  const int qb = w % a.nqb;
+  w /= a.nqb;
+  const int hq = w % a.Hq, b = w / a.Hq;
+  const int hkv = hq / a.group;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hl = lane >> 5, lq = lane & 31;
+  const int qi = qb * 128 + wave * 32 + lq;
+  const bool q_in = qi < a.Lq;
+  const int qc = min(qi, a.Lq - 1);
+  const bool doc = (a.flags & FA_MASK_DOC) != 0;
+
+  // Q^T and dO^T as B operands: lane holds X[qi][16 ks + 8 hl .. +8].
+  const __bf16* qp = (const __bf16*)a.q + b * a.q_sb + hq * a.q_sh + (int64_t)qc * a.q_sl;
+  const __bf16* dop = (const __bf16*)a.dout + b * a.do_sb + hq * a.do_sh + (int64_t)qc * a.do_sl;
+  bf16x8 qreg[8], doreg[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    qreg[ks] = *(const bf16x8*)(qp + ks * 16 + hl * 8);
+    doreg[ks] = *(const bf16x8*)(dop + ks * 16 + hl * 8);
+  }
+  const int64_t row = ((int64_t)b * a.Hq + hq) * a.Lq + qc;
+  const float lse2 = q_in ? a.lse2[row] : INFINITY;
+  const float delta = q_in ? a.delta[row] : 0.f;
+  const int qdoc = doc ? a.q_doc[(int64_t)b * a.Lq + qc] : 0;
+  const float slope = (SCORE & FA_SCORE_ALIBI) ? a.slopes[hq] : 0.f;
+  const MaskSpec ms{a.flags, a.window, a.prefix_len};
+  const int tb = tr_base(lane);
+
+  const __bf16* kp = (const __bf16*)a.k + b * a.k_sb + hkv * a.k_sh;
+  const __bf16* vp = (const __bf16*)a.v + b * a.v_sb + hkv * a.v_sh;
+
+  int nfull, npart;
+  const int* full = nullptr;
+  const int* part = nullptr;
+  if (a.all_full) {
+    nfull = (a.Lkv + 127) / 128;
+    npart = 0;
+  } else {
+    const int bm = a.Bm == 1 ? 0 : b, hm = a.Hm == 1 ? 0 : hq;
+    const int64_t r = ((int64_t)bm * a.Hm + hm) * a.nqb + qb;
+    nfull = a.full_num[r];
+    npart = a.kv_num[r];
+    full = a.full_idx + r * a.nkvb;
+    part = a.kv_idx + r * a.nkvb;
+  }
+  const int nsteps = 2 * (nfull + npart);
+  auto step_kv0 = [&](int s, bool& masked) {
+    const int t = s >> 1;
+    const bool partial = t >= nfull;
+    const int kb = partial ? part[t - nfull] : (a.all_full ? t : full[t]);
+    const int kv0 = kb * 128 + (s & 1) * kRows;
+    masked = partial || kv0 + kRows > a.Lkv;
+    return kv0;
+  };
+
+  f32x16 dqacc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) dqacc[db] = f32x16{};
+  float slope_acc = 0.f;
+
+  Stage st;
+  int dstage = 0;
+  bool m_next = false;
+  int kv_next = nsteps > 0 ? step_kv0(0, m_next) : 0;
+  if (nsteps > 0 && kv_next < a.Lkv) {
+    stage_load(st, kp, a.k_sl, vp, a.v_sl, kv_next, a.Lkv, tid);
+    if (doc && tid < kRows) dstage = a.kv_doc[(int64_t)b * a.Lkv + min(kv_next + tid, a.Lkv - 1)];
+  }
+  for (int s = 0; s < nsteps; ++s) {
+    const int kv0 = kv_next;
+    const bool masked = m_next;
+    if (kv0 >= a.Lkv) {  // second half of a ragged last tile: no keys (uniform over the workgroup)
+      if (s + 1 < nsteps) {
+        kv_next = step_kv0(s + 1, m_next);
+        if (kv_next < a.Lkv) {
+          stage_load(st, kp, a.k_sl, vp, a.v_sl, kv_next, a.Lkv, tid);
+          if (doc && tid < kRows) dstage = a.kv_doc[(int64_t)b * a.Lkv + min(kv_next + tid, a.Lkv - 1)];
+        }
+      }
+      continue;
+    }
+    __syncthreads();  // the previous step's reads of sK / sV are done
+    stage_store(st, sK, sV, kv0, a.Lkv, tid);
+    if (doc && tid < kRows) sDoc[tid] = dstage;
+    __syncthreads();
+    if (s + 1 < nsteps) {
+      kv_next = step_kv0(s + 1, m_next);
+      if (kv_next < a.Lkv) {
+        stage_load(st, kp, a.k_sl, vp, a.v_sl, kv_next, a.Lkv, tid);
+        if (doc && tid < kRows) dstage = a.kv_doc[(int64_t)b * a.Lkv + min(kv_next + tid, a.Lkv - 1)];
+      }
+    }
+
+    f32x16 sacc[2], dpacc[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      sacc[nb] = f32x16{};
+      dpacc[nb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        sacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_x(sK, nb * 32 + lq, ks, hl), qreg[ks], sacc[nb], 0, 0, 0);
+        dpacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_x(sV, nb * 32 + lq, ks, hl), doreg[ks], dpacc[nb], 0, 0, 0);
+      }
+    }
+    bf16x8 dsb[2][2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int kr = nb * 32 + 8 * (i >> 2) + 4 * hl + (i & 3);
+        const int kv = kv0 + kr;
+        float dfac;
+        const float f = score_f<SCORE>(a, sacc[nb][i], qi, kv, slope, dfac);
+        float p = fast_exp2(fmaf(f, kLog2e, -lse2));
+        if (masked) {
+          const bool keep = kv < a.Lkv && mask_pair(ms, qi, kv, qdoc, doc ? sDoc[kr] : 0);
+          p = keep ? p : 0.f;
+        }
+        float da = p * (dpacc[nb][i] - delta);
+        if constexpr (SCORE & FA_SCORE_SOFTCAP) da *= dfac;
+        if constexpr (SCORE & FA_SCORE_ALIBI) slope_acc = fmaf(-da, fabsf((float)(qi - kv)), slope_acc);
+        dsb[nb][i >> 3][i & 7] = (__bf16)da;
+      }
+    }
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_xt(sK, nb * 32 + h * 16, db, tb), dsb[nb][h],
+                                                              dqacc[db], 0, 0, 0);
+      }
+    }
+  }
+
+  // dQ[qi][channel]: lane holds channels 32 db + 8 gq + 4 hl + 0..3 of its query.
+  if (q_in) {
+    __bf16* op = (__bf16*)a.dq + b * a.dq_sb + hq * a.dq_sh + (int64_t)qi * a.dq_sl;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        bf16x4 o4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(dqacc[db][gq * 4 + e] * a.sm_scale);
+        *(bf16x4*)(op + db * 32 + gq * 8 + hl * 4) = o4;
+      }
+    }
+  }
+  if constexpr (SCORE & FA_SCORE_ALIBI) {
+    if (a.dslopes) {
+      const float ws = wave_sum(slope_acc);
+      if (lane == 0) sRed[wave] = ws;
+      __syncthreads();
+      if (tid == 0) a.slope_part[((int64_t)b * a.Hq + hq) * a.nqb + qb] = (sRed[0] + sRed[1]) + (sRed[2] + sRed[3]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// dK and dV: one workgroup per (b, hkv, 128-key block), summing over the query heads of the
+// group.
+// ---------------------------------------------------------------------------------------------
+template <int SCORE>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(1024))) unsigned char sQ[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char sO[kTileBytes];
+  __shared__ __attribute__((aligned(16))) float sL[kRows];
+  __shared__ __attribute__((aligned(16))) float sDl[kRows];
+  __shared__ __attribute__((aligned(16))) int sDoc[kRows];
+
+  int w = blockIdx.x;
+  const int kb = w % a.nkvb;
+  w /= a.nkvb;
+  const int hkv = w % a.Hkv, b = w / a.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hl = lane >> 5, lq = lane & 31;
+  const int kj = kb * 128 + wave * 32 + lq;
+  const bool k_in = kj < a.Lkv;
+  const int kc = min(kj, a.Lkv - 1);
+  const bool doc = (a.flags & FA_MASK_DOC) != 0;
+
+  // K^T and V^T as B operands: lane holds X[kj][16 ks + 8 hl .. +8].
+  const __bf16* kp = (const __bf16*)a.k + b * a.k_sb + hkv * a.k_sh + (int64_t)kc * a.k_sl;
+  const __bf16* vp = (const __bf16*)a.v + b * a.v_sb + hkv * a.v_sh + (int64_t)kc * a.v_sl;
+  bf16x8 kreg[8], vreg[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    kreg[ks] = *(const bf16x8*)(kp + ks * 16 + hl * 8);
+    vreg[ks] = *(const bf16x8*)(vp + ks * 16 + hl * 8);
+  }
+  const int kdoc = doc ? a.kv_doc[(int64_t)b * a.Lkv + kc] : 0;
+  const MaskSpec ms{a.flags, a.window, a.prefix_len};
+  const int tb = tr_base(lane);
+
+  f32x16 dkacc[4], dvacc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    dkacc[db] = f32x16{};
+    dvacc[db] = f32x16{};
+  }
+
+  for (int g = 0; g < a.group; ++g) {
+    const int hq = hkv * a.group + g;
+    const float slope = (SCORE & FA_SCORE_ALIBI) ? a.slopes[hq] : 0.f;
+    const __bf16* qp = (const __bf16*)a.q + b * a.q_sb + hq * a.q_sh;
+    const __bf16* dop = (const __bf16*)a.dout + b * a.do_sb + hq * a.do_sh;
+    const int64_t rowbase = ((int64_t)b * a.Hq + hq) * a.Lq;
+
+    int nfull, npart;
+    const int* full = nullptr;
+    const int* part = nullptr;
+    if (a.all_full) {
+      nfull = (a.Lq + 127) / 128;
+      npart = 0;
+    } else {
+      const int bm = a.Bm == 1 ? 0 : b, hm = a.Hm == 1 ? 0 : hq;
+      const int64_t r = ((int64_t)bm * a.Hm + hm) * a.nkvb + kb;
+      nfull = a.fullq_num[r];
+      npart = a.q_num[r];
+      full = a.fullq_idx + r * a.nqb;
+      part = a.q_idx + r * a.nqb;
+    }
+    const int nsteps = 2 * (nfull + npart);
+    for (int s = 0; s < nsteps; ++s) {
+      const int t = s >> 1;
+      const bool masked = t >= nfull;
+      const int qbk = masked ? part[t - nfull] : (a.all_full ? t : full[t]);
+      const int q0 = qbk * 128 + (s & 1) * kRows;
+      if (q0 >= a.Lq) continue;  // uniform over the workgroup
+
+      Stage st;
+      stage_load(st, qp, a.q_sl, dop, a.do_sl, q0, a.Lq, tid);
+      float lv = INFINITY, dv = 0.f;
+      int dd = 0;
+      if (tid < kRows) {
+        const int qr = q0 + tid;
+        if (qr < a.Lq) {
+          lv = a.lse2[rowbase + qr];
+          dv = a.delta[rowbase + qr];
+          if (doc) dd = a.q_doc[(int64_t)b * a.Lq + qr];
+        }
+      }
+      __syncthreads();  // the previous step's reads are done
+      stage_store(st, sQ, sO, q0, a.Lq, tid);
+      if (tid < kRows) {
+        sL[tid] = lv;
+        sDl[tid] = dv;
+        sDoc[tid] = dd;
+      }
+      __syncthreads();
+
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        f32x16 sacc = f32x16{}, dpacc = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_x(sQ, sub * 32 + lq, ks, hl), kreg[ks], sacc, 0, 0, 0);
+          dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_x(sO, sub * 32 + lq, ks, hl), vreg[ks], dpacc, 0, 0, 0);
+        }
+        bf16x8 pb[2], dsb[2];
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int r4 = sub * 32 + 8 * gq + 4 * hl;
+          const f32x4 l4 = *(const f32x4*)(sL + r4);
+          const f32x4 d4 = *(const f32x4*)(sDl + r4);
+          const i32x4 c4 = *(const i32x4*)(sDoc + r4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * gq + e;
+            const int qi = q0 + r4 + e;
+            float dfac;
+            const float f = score_f<SCORE>(a, sacc[i], qi, kj, slope, dfac);
+            float p = fast_exp2(fmaf(f, kLog2e, -l4[e]));
+            if (masked) p = mask_pair(ms, qi, kj, c4[e], kdoc) ? p : 0.f;
+            float da = p * (dpacc[i] - d4[e]);
+            if constexpr (SCORE & FA_SCORE_SOFTCAP) da *= dfac;
+            pb[i >> 3][i & 7] = (__bf16)p;
+            dsb[i >> 3][i & 7] = (__bf16)da;
+          }
+        }
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_xt(sO, sub * 32 + h * 16, db, tb), pb[h],
+                                                                dvacc[db], 0, 0, 0);
+            dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_xt(sQ, sub * 32 + h * 16, db, tb), dsb[h],
+                                                                dkacc[db], 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+
+  if (k_in) {
+    __bf16* kop = (__bf16*)a.dk + b * a.dk_sb + hkv * a.dk_sh + (int64_t)kj * a.dk_sl;
+    __bf16* vop = (__bf16*)a.dv + b * a.dv_sb + hkv * a.dv_sh + (int64_t)kj * a.dv_sl;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        bf16x4 k4, v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          k4[e] = (__bf16)(dkacc[db][gq * 4 + e] * a.sm_scale);
+          v4[e] = (__bf16)dvacc[db][gq * 4 + e];
+        }
+        *(bf16x4*)(kop + db * 32 + gq * 8 + hl * 4) = k4;
+        *(bf16x4*)(vop + db * 32 + gq * 8 + hl * 4) = v4;
+      }
+    }
+  }
+}
+
+// dslopes[h] = sum over batches and query blocks of the partial sums (one workgroup per head).
+__global__ __launch_bounds__(256) void bwd_slope_kernel(BwdArgs a) {
+  __shared__ float sRed[4];
+  const int hq = blockIdx.x;
+  float acc = 0.f;
+  const int n = a.B * a.nqb;
+  for (int i = threadIdx.x; i < n; i += 256) {
+    const int b = i / a.nqb, qb = i % a.nqb;
+    acc += a.slope_part[((int64_t)b * a.Hq + hq) * a.nqb + qb];
+  }
+  acc = wave_sum(acc);
+  if ((threadIdx.x & 63) == 0) sRed[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) a.dslopes[hq] = (sRed[0] + sRed[1]) + (sRed[2] + sRed[3]);
+}
+
+// Column lists of a BlockMask: one wave per (mask row, kv block). Lane l tests q blocks
+// c + l; membership in the ascending row lists is a binary search; ballots keep the output
+// ascending.
+__global__ __launch_bounds__(256) void bm_transpose_kernel(TransposeArgs t) {
+  const int lane = threadIdx.x & 63;
+  const int64_t col = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (col >= (int64_t)t.Bm * t.Hm * t.nkvb) return;  // whole waves
+  const int kb = (int)(col % t.nkvb);
+  const int64_t mrow = col / t.nkvb;  // bm * Hm + hm
+  auto find = [&](const int* lst, int n, int key) {
+    int lo = 0, hi = n;  // first index with lst[i] >= key
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (lst[mid] < key) lo = mid + 1; else hi = mid;
+    }
+    return lo < n && lst[lo] == key;
+  };
+  int* qi_out = t.q_idx + col * t.nqb;
+  int* fq_out = t.fullq_idx + col * t.nqb;
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  int np = 0, nf = 0;
+  for (int c = 0; c < t.nqb; c += 64) {
+    const int qb = c + lane;
+    int cls = 0;
+    if (qb < t.nqb) {
+      const int64_t r = mrow * t.nqb + qb;
+      if (find(t.kv_idx + r * t.nkvb, t.kv_num[r], kb)) cls = 1;
+      else if (find(t.full_idx + r * t.nkvb, t.full_num[r], kb)) cls = 2;
+    }
+    const unsigned long long mp = __ballot(cls == 1), mf = __ballot(cls == 2);
+    if (cls == 1) qi_out[np + __popcll(mp & lt)] = qb;
+    if (cls == 2) fq_out[nf + __popcll(mf & lt)] = qb;
+    np += __popcll(mp);
+    nf += __popcll(mf);
+  }
+  for (int e = np + lane; e < t.nqb; e += 64) qi_out[e] = 0;
+  for (int e = nf + lane; e < t.nqb; e += 64) fq_out[e] = 0;
+  if (lane == 0) {
+    t.q_num[col] = np;
+    t.fullq_num[col] = nf;
+  }
+}
+
+template <int SCORE>
+static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
+  // With no query rows, only dk / dv (zeros) and dslopes (zeros) are written.
+  const int64_t rows = (int64_t)a.B * a.Hq * a.Lq;
+  if (rows > 0) hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream, a);
+  const int64_t nq = (int64_t)a.B * a.Hq * a.nqb;
+  if (nq > 0) hipLaunchKernelGGL((bwd_dq_kernel<SCORE>), dim3((unsigned)nq), dim3(256), 0, stream, a);
+  const int64_t nk = (int64_t)a.B * a.Hkv * a.nkvb;
+  if (nk > 0) hipLaunchKernelGGL((bwd_dkdv_kernel<SCORE>), dim3((unsigned)nk), dim3(256), 0, stream, a);
+  if ((SCORE & FA_SCORE_ALIBI) && a.dslopes)
+    hipLaunchKernelGGL(bwd_slope_kernel, dim3(a.Hq), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd(const BwdArgs& a, int score, hipStream_t stream) {
+  switch (score) {
+    case 0: return launch_bwd_t<0>(a, stream);
+    case FA_SCORE_ALIBI: return launch_bwd_t<FA_SCORE_ALIBI>(a, stream);
+    case FA_SCORE_SOFTCAP: return launch_bwd_t<FA_SCORE_SOFTCAP>(a, stream);
+    default: return launch_bwd_t<FA_SCORE_ALIBI | FA_SCORE_SOFTCAP>(a, stream);
+  }
+}
+
+hipError_t launch_block_mask_transpose(const TransposeArgs& t, hipStream_t stream) {
+  const int64_t cols = (int64_t)t.Bm * t.Hm * t.nkvb;
+  if (cols == 0) return hipSuccess;
+  hipLaunchKernelGGL(bm_transpose_kernel, dim3((unsigned)((cols + 3) / 4)), dim3(256), 0, stream, t);
+  return hipGetLastError();
+}
+
+}  // namespace fa

@@ -62,6 +62,64 @@ struct MergeArgs {
   int B, Hq, Lq, nsplit;
 };
 
+// Backward (bf16, head dim 128). Gradients dq [B][Hq][Lq][128], dk and dv [B][Hkv][Lkv][128]
+// (bf16, element strides); the workspace holds per-row lse2 = lse * log2(e) (+inf for rows with
+// no allowed key, so that their probabilities come out 0) and delta = dout . out, and the
+// per-(b, hq, 128-query block) partial sums of the ALiBi-slope gradient.
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dslopes;
+  int64_t q_sb, q_sh, q_sl;
+  int64_t k_sb, k_sh, k_sl;
+  int64_t v_sb, v_sh, v_sl;
+  int64_t o_sb, o_sh, o_sl;
+  int64_t do_sb, do_sh, do_sl;
+  int64_t dq_sb, dq_sh, dq_sl;
+  int64_t dk_sb, dk_sh, dk_sl;
+  int64_t dv_sb, dv_sh, dv_sl;
+  int B, Hq, Hkv, Lq, Lkv, group;
+  // Row lists (per 128-query block) for dq, column lists (per 128-key block) for dk/dv;
+  // all_full = 1: no BlockMask, every tile is full.
+  const int* kv_num;
+  const int* kv_idx;
+  const int* full_num;
+  const int* full_idx;
+  const int* q_num;
+  const int* q_idx;
+  const int* fullq_num;
+  const int* fullq_idx;
+  int Bm, Hm, nqb, nkvb, all_full;
+  int flags, window, prefix_len;
+  const int* q_doc;
+  const int* kv_doc;
+  float sm_scale, softcap, inv_softcap;
+  const float* slopes;
+  float* lse2;        // [B][Hq][Lq]
+  float* delta;       // [B][Hq][Lq]
+  float* slope_part;  // [B][Hq][nqb], or null when no slope gradient is asked for
+};
+
+// Column view of a BlockMask (q-block lists per kv block).
+struct TransposeArgs {
+  int Bm, Hm, nqb, nkvb;
+  const int* kv_num;
+  const int* kv_idx;
+  const int* full_num;
+  const int* full_idx;
+  int* q_num;
+  int* q_idx;
+  int* fullq_num;
+  int* fullq_idx;
+};
+
 // Quantized form: bf16 sources and int8 / E4M3 outputs (element strides; int8 elements are bytes).
 struct QuantTensor {
   const unsigned short* data;  // bf16 bit patterns
@@ -101,5 +159,8 @@ hipError_t launch_fwd_quant(const QuantFwdArgs& a, hipStream_t stream);
 // score bits FA_SCORE_*.
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int q_block, int kv_block, int score, hipStream_t stream);
 hipError_t launch_splitkv_merge(const MergeArgs& m, hipStream_t stream);
+// Backward: delta/lse2 preparation, dq (+ slope partials), dk/dv, slope reduction.
+hipError_t launch_bwd(const BwdArgs& a, int score, hipStream_t stream);
+hipError_t launch_block_mask_transpose(const TransposeArgs& t, hipStream_t stream);
 
 }  // namespace fa

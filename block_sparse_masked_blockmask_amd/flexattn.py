@@ -41,6 +41,13 @@ class FaBlockMask(ctypes.Structure):
                 ("full_kv_num_blocks", c_void_p), ("full_kv_indices", c_void_p)]
 
 
+class FaBlockMaskTransposed(ctypes.Structure):
+    _fields_ = [("Bm", c_int32), ("Hm", c_int32), ("q_len", c_int32), ("kv_len", c_int32),
+                ("q_block", c_int32), ("kv_block", c_int32), ("n_qb", c_int32), ("n_kvb", c_int32),
+                ("q_num_blocks", c_void_p), ("q_indices", c_void_p),
+                ("full_q_num_blocks", c_void_p), ("full_q_indices", c_void_p)]
+
+
 class FlexAttnError(RuntimeError):
     def __init__(self, status: int, reason: str):
         super().__init__(f"flexattn status {status}: {reason}")
@@ -81,6 +88,14 @@ def lib() -> ctypes.CDLL:
                                            POINTER(FaTensor), c_void_p, c_int, c_void_p, c_size_t, c_void_p]
         L.flexattn_fwd_splitkv.restype = c_int
         L.flexattn_quantize_qkv.argtypes = [POINTER(FaTensor)] * 6 + [c_void_p]
+        L.flexattn_block_mask_transpose.argtypes = [POINTER(FaBlockMask), POINTER(FaBlockMaskTransposed), c_void_p]
+        L.flexattn_block_mask_transpose.restype = c_int
+        L.flexattn_bwd_workspace_bytes.argtypes = [c_int] * 3
+        L.flexattn_bwd_workspace_bytes.restype = c_size_t
+        L.flexattn_bwd.argtypes = [POINTER(FaTensor)] * 5 + [c_void_p, POINTER(FaBlockMask),
+                                   POINTER(FaBlockMaskTransposed), c_int, c_int, POINTER(FaParams)] + \
+                                  [POINTER(FaTensor)] * 3 + [c_void_p, c_void_p, c_size_t, c_void_p]
+        L.flexattn_bwd.restype = c_int
         L.flexattn_quantize_qkv.restype = c_int
         L.flexattn_last_error.argtypes = []
         L.flexattn_last_error.restype = ctypes.c_char_p
@@ -122,9 +137,11 @@ def tensor_desc(t: torch.Tensor, scale: Optional[torch.Tensor] = None) -> FaTens
     """Descriptor of a [B, H, L, D] tensor whose last dimension is contiguous."""
     if t.dim() != 4:
         raise ValueError("attention tensors are [B, H, L, D]")
+    B, H, L, D = t.shape
+    if t.numel() == 0:  # no element is addressed: describe it with the dense layout
+        return FaTensor(t.data_ptr(), _DTYPES[t.dtype], B, H, L, D, H * L * D, L * D, D, _ptr(scale))
     if t.stride(3) != 1:
         raise ValueError("the D dimension must be contiguous")
-    B, H, L, D = t.shape
     return FaTensor(t.data_ptr(), _DTYPES[t.dtype], B, H, L, D, t.stride(0), t.stride(1), t.stride(2),
                     _ptr(scale))
 
@@ -306,3 +323,67 @@ def flexattn_quantize_qkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, 
              tensor_desc(out["k8"], out["k_scale"]), tensor_desc(out["v8"], out["v_scale"])]
     _check(lib().flexattn_quantize_qkv(*[ctypes.byref(d) for d in descs], _stream(stream)))
     return out
+
+
+class BlockMaskTransposed:
+    """Device column view of a BlockMask (q-block lists per kv block; caller-owned memory)."""
+
+    def __init__(self, bm: BlockMask):
+        self.Bm, self.Hm, self.q_len, self.kv_len = bm.Bm, bm.Hm, bm.q_len, bm.kv_len
+        self.q_block, self.kv_block, self.n_qb, self.n_kvb = bm.q_block, bm.kv_block, bm.n_qb, bm.n_kvb
+        z = dict(dtype=torch.int32, device=bm.kv_num_blocks.device)
+        self.q_num_blocks = torch.empty((self.Bm, self.Hm, self.n_kvb), **z)
+        self.full_q_num_blocks = torch.empty((self.Bm, self.Hm, self.n_kvb), **z)
+        self.q_indices = torch.empty((self.Bm, self.Hm, self.n_kvb, self.n_qb), **z)
+        self.full_q_indices = torch.empty((self.Bm, self.Hm, self.n_kvb, self.n_qb), **z)
+
+    def as_struct(self) -> FaBlockMaskTransposed:
+        return FaBlockMaskTransposed(self.Bm, self.Hm, self.q_len, self.kv_len, self.q_block, self.kv_block,
+                                     self.n_qb, self.n_kvb, self.q_num_blocks.data_ptr(), self.q_indices.data_ptr(),
+                                     self.full_q_num_blocks.data_ptr(), self.full_q_indices.data_ptr())
+
+
+def flexattn_block_mask_transpose(block_mask: BlockMask, *, out: Optional[BlockMaskTransposed] = None,
+                                  stream=None) -> BlockMaskTransposed:
+    """Column view of a device BlockMask (flexattn_block_mask_transpose)."""
+    if out is None:
+        out = BlockMaskTransposed(block_mask)
+    s, t = block_mask.as_struct(), out.as_struct()
+    _check(lib().flexattn_block_mask_transpose(ctypes.byref(s), ctypes.byref(t), _stream(stream)))
+    return out
+
+
+def flexattn_bwd_workspace_bytes(B: int, Hq: int, Lq: int) -> int:
+    return lib().flexattn_bwd_workspace_bytes(B, Hq, Lq)
+
+
+def flexattn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, dout: torch.Tensor,
+                 lse: torch.Tensor, block_mask: Optional[BlockMask] = None,
+                 block_mask_t: Optional[BlockMaskTransposed] = None, mask_kind: int = FA_MASK_NONE,
+                 score_kind: int = FA_SCORE_NONE, *, window: int = 0, prefix_len: int = 0, softcap: float = 0.0,
+                 alibi_slopes=None, q_doc=None, kv_doc=None, sm_scale: float = 0.0, slope_grad: bool = False,
+                 dq=None, dk=None, dv=None, dslopes=None, workspace: Optional[torch.Tensor] = None, stream=None):
+    """Backward pass (flexattn_bwd); returns (dq, dk, dv, dslopes). The transposed BlockMask is built
+    when a BlockMask is given without one; dslopes is computed when slope_grad is set (ALiBi)."""
+    if block_mask is not None and block_mask_t is None:
+        block_mask_t = flexattn_block_mask_transpose(block_mask, stream=stream)
+    dq = torch.empty(q.shape, dtype=q.dtype, device=q.device) if dq is None else dq
+    dk = torch.empty(k.shape, dtype=k.dtype, device=k.device) if dk is None else dk
+    dv = torch.empty(v.shape, dtype=v.dtype, device=v.device) if dv is None else dv
+    if slope_grad and dslopes is None:
+        dslopes = torch.empty(q.shape[1], dtype=torch.float32, device=q.device)
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != tuple(q.shape[:3]):
+        raise ValueError("lse must be a contiguous float32 [B, Hq, Lq] tensor")
+    ws_bytes = flexattn_bwd_workspace_bytes(q.shape[0], q.shape[1], q.shape[2])
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    descs = [tensor_desc(t) for t in (q, k, v, out, dout, dq, dk, dv)]
+    p = _params(window=window, prefix_len=prefix_len, softcap=softcap, alibi_slopes=alibi_slopes,
+                q_doc=q_doc, kv_doc=kv_doc, sm_scale=sm_scale)
+    bm = ctypes.byref(block_mask.as_struct()) if block_mask is not None else None
+    bmt = ctypes.byref(block_mask_t.as_struct()) if block_mask_t is not None else None
+    _check(lib().flexattn_bwd(*[ctypes.byref(d) for d in descs[:5]], _ptr(lse), bm, bmt, mask_kind, score_kind,
+                              ctypes.byref(p), *[ctypes.byref(d) for d in descs[5:]], _ptr(dslopes),
+                              _ptr(workspace), workspace.numel() if workspace is not None else 0,
+                              _stream(stream)))
+    return dq, dk, dv, dslopes

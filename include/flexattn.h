@@ -1,5 +1,6 @@
 /*
- * flexattn.h — C ABI of the block-sparse masked attention forward for MI355X (gfx950).
+ * flexattn.h — C ABI of the block-sparse masked attention forward (and its backward) for MI355X
+ * (gfx950).
  *
  * The operation (FlexAttention guide, "The Core Design Principles"):
  *     out_i = sum_j softmax_j( score_mod(q_i . k_j * sm_scale) restricted to mask_mod(i, j) ) v_j
@@ -181,6 +182,58 @@ size_t flexattn_fwd_splitkv_workspace_bytes(int B, int Hq, int Lq, int n_splits)
 fa_status flexattn_fwd_splitkv(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_block_mask* bm,
                                int mask_kind, int score_kind, const fa_params* p, fa_tensor* out, float* lse,
                                int n_splits, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Column view of a BlockMask, for a backward that walks kv blocks (field names as in
+ * FlexAttention's BlockMask; the pages give no layout). For each mask row (bm, hm) and kv block
+ * kb, the q blocks whose (qb, kb) tile is partial (q_indices) or full (full_q_indices), each
+ * list ascending with its length in the matching *_num_blocks entry and the unused tail 0.
+ * Shapes (int32, device):
+ *   q_num_blocks, full_q_num_blocks : [Bm][Hm][n_kvb]   (flexattn_block_mask_count_bytes(Bm, Hm,
+ *                                                          kv_len, kv_block) bytes each)
+ *   q_indices, full_q_indices       : [Bm][Hm][n_kvb][n_qb]  (flexattn_block_mask_index_bytes) */
+typedef struct {
+  int32_t Bm, Hm, q_len, kv_len, q_block, kv_block, n_qb, n_kvb;
+  int32_t* q_num_blocks;
+  int32_t* q_indices;
+  int32_t* full_q_num_blocks;
+  int32_t* full_q_indices;
+} fa_block_mask_transposed;
+
+/* Transpose a BlockMask into its column view on the device (the same tiles and classes, listed
+ * per kv block). `out` carries the dimensions of `bm` (all eight must be equal) and four
+ * caller-owned arrays; every entry of them is written. */
+fa_status flexattn_block_mask_transpose(const fa_block_mask* bm, fa_block_mask_transposed* out, hipStream_t stream);
+
+/* Device scratch of flexattn_bwd: per query row lse * log2(e) and delta = dout . out (float32
+ * [B][Hq][Lq] each, padded to 16 bytes), then the slope-gradient partials (float32
+ * [B][Hq][ceil(Lq / 128)]). */
+size_t flexattn_bwd_workspace_bytes(int B, int Hq, int Lq);
+
+/* Backward pass of flexattn_fwd (FlexAttention guide, "Systems Mechanics", item 2: the backward
+ * gives dQ, dK, dV, differentiates the score_mod, and passes gradients to learnable score_mod
+ * parameters such as ALiBi slopes). With f the modified score of an allowed pair and
+ * P = exp(f - lse):
+ *   dv = P^T dout;  dA = P (dout v^T - rowsum(dout * out)) * (1 - (f / softcap)^2 under SOFTCAP);
+ *   dq = sm_scale dA k;  dk = sm_scale dA^T q;  dslopes[h] = -sum over (b, i, j) of dA |i - j|.
+ * GQA: dk and dv of a kv head sum over its query heads.
+ *   - all tensors FA_BF16 with D = 128: q, out, dout, dq [B][Hq][Lq]; k, v, dk, dv [B][Hkv][Lkv];
+ *     element strides as in flexattn_fwd; gradients written in bf16 (fp32 accumulation);
+ *   - out and lse are those of flexattn_fwd on the same inputs (lse natural log, float32
+ *     [B][Hq][Lq] contiguous; -inf rows get zero gradients);
+ *   - bm and bmt: the forward's BlockMask and its transpose (flexattn_block_mask_transpose), both
+ *     with 128 x 128 tiles (other tile sizes are FA_ERR_UNSUPPORTED), or both NULL with mask_kind
+ *     NONE. As in the forward the BlockMask decides which tiles are visited and mask_kind is
+ *     evaluated on partial tiles;
+ *   - dslopes: float32 [Hq] device, overwritten with the slope gradient summed over batches; NULL
+ *     skips it; only allowed with ALIBI;
+ *   - workspace: flexattn_bwd_workspace_bytes(B, Hq, Lq) bytes, 16-byte aligned; contents after
+ *     the call unspecified.
+ * dq, dk and dv are overwritten (not accumulated into). Everything else as flexattn_fwd. */
+fa_status flexattn_bwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* out,
+                       const fa_tensor* dout, const float* lse, const fa_block_mask* bm,
+                       const fa_block_mask_transposed* bmt, int mask_kind, int score_kind, const fa_params* p,
+                       fa_tensor* dq, fa_tensor* dk, fa_tensor* dv, float* dslopes, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream);
 
 /* Reason for the last non-OK status returned on this thread ("" if none). */
 const char* flexattn_last_error(void);

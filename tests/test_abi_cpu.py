@@ -195,3 +195,81 @@ def test_splitkv_validation(case, status, needle):
                                   ctypes.byref(o), None, n, ws, wsb, None)
     assert st == status, (st, fa.flexattn_last_error())
     assert needle in fa.flexattn_last_error(), fa.flexattn_last_error()
+
+
+def test_bwd_sizes_and_struct():
+    from block_sparse_masked_blockmask_amd.flexattn import FaBlockMaskTransposed
+    assert ctypes.sizeof(FaBlockMaskTransposed) == 4 * 8 + 8 * 4
+    rows4 = (2 * 3 * 130 + 3) // 4 * 4
+    assert fa.flexattn_bwd_workspace_bytes(2, 3, 130) == (2 * rows4 + 2 * 3 * 2) * 4
+    assert fa.flexattn_bwd_workspace_bytes(0, 3, 130) == 0
+
+
+def _bm(Bm=1, Hm=1, Lq=100, Lkv=100, bq=128, bk=128, ptr=4096):
+    nq, nk = -(-Lq // bq), -(-Lkv // bk)
+    return FaBlockMask(Bm, Hm, Lq, Lkv, bq, bk, nq, nk, ptr, ptr, ptr, ptr)
+
+
+def _bmt(Bm=1, Hm=1, Lq=100, Lkv=100, bq=128, bk=128, ptr=4096):
+    from block_sparse_masked_blockmask_amd.flexattn import FaBlockMaskTransposed
+    nq, nk = -(-Lq // bq), -(-Lkv // bk)
+    return FaBlockMaskTransposed(Bm, Hm, Lq, Lkv, bq, bk, nq, nk, ptr, ptr, ptr, ptr)
+
+
+@pytest.mark.parametrize("case,status,needle", [
+    ("f32", fa.FA_ERR_UNSUPPORTED, "bf16"),
+    ("d64", fa.FA_ERR_UNSUPPORTED, "head dim"),
+    ("dk_shape", fa.FA_ERR_INVALID_ARG, "share one shape"),
+    ("dq_shape", fa.FA_ERR_INVALID_ARG, "share one shape"),
+    ("no_lse", fa.FA_ERR_INVALID_ARG, "lse is NULL"),
+    ("mask_no_bm", fa.FA_ERR_INVALID_ARG, "BlockMask is required"),
+    ("bm_only", fa.FA_ERR_INVALID_ARG, "both"),
+    ("bm_64", fa.FA_ERR_UNSUPPORTED, "128 x 128"),
+    ("bmt_dims", fa.FA_ERR_INVALID_ARG, "transposed"),
+    ("dslopes_no_alibi", fa.FA_ERR_INVALID_ARG, "dslopes"),
+    ("no_ws", fa.FA_ERR_INVALID_ARG, "workspace needs"),
+    ("ws_misaligned", fa.FA_ERR_INVALID_ARG, "16-byte aligned"),
+    ("gqa", fa.FA_ERR_INVALID_ARG, "multiple of Hkv"),
+])
+def test_bwd_validation(case, status, needle):
+    """flexattn_bwd refuses before enqueuing anything (no GPU needed)."""
+    lib = fa.lib()
+    dt = fa.FA_F32 if case == "f32" else fa.FA_BF16
+    D = 64 if case == "d64" else 128
+    q, o, do, dq = (_t(dtype=dt, D=D) for _ in range(4))
+    k, v = _t(dtype=dt, D=D), _t(dtype=dt, D=D)
+    dk = _t(dtype=dt, D=D, L=90 if case == "dk_shape" else 100)
+    dv = _t(dtype=dt, D=D)
+    if case == "dq_shape":
+        dq = _t(dtype=dt, D=D, H=4)
+    if case == "gqa":
+        k, v, dk, dv = (_t(H=3) for _ in range(4))
+    p = FaParams(0.0, 0, 0, 0.0, None, None, None)
+    lse = None if case == "no_lse" else 8192
+    mask = fa.FA_MASK_CAUSAL if case in ("mask_no_bm", "bm_only", "bm_64", "bmt_dims") else 0
+    bm = bmt = None
+    if case in ("bm_only", "bm_64", "bmt_dims"):
+        bm = _bm(bk=64 if case == "bm_64" else 128)
+        if case != "bm_only":
+            bmt = _bmt(bk=64 if case == "bm_64" else 128, Lkv=101 if case == "bmt_dims" else 100)
+    dsl = 8192 if case == "dslopes_no_alibi" else None
+    need = lib.flexattn_bwd_workspace_bytes(1, 2, 100)
+    ws, wsb = 4096, need
+    if case == "no_ws":
+        ws, wsb = None, 0
+    if case == "ws_misaligned":
+        ws = 4100
+    st = lib.flexattn_bwd(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), ctypes.byref(o), ctypes.byref(do), lse,
+                          None if bm is None else ctypes.byref(bm), None if bmt is None else ctypes.byref(bmt),
+                          mask, 0, ctypes.byref(p), ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), dsl,
+                          ws, wsb, None)
+    assert st == status, (st, fa.flexattn_last_error())
+    assert needle in fa.flexattn_last_error(), fa.flexattn_last_error()
+
+
+def test_transpose_validation():
+    lib = fa.lib()
+    bm = _bm()
+    for bad, needle in ((_bmt(Lq=101), "dimensions"), (_bmt(ptr=None), "NULL")):
+        st = lib.flexattn_block_mask_transpose(ctypes.byref(bm), ctypes.byref(bad), None)
+        assert st == fa.FA_ERR_INVALID_ARG and needle in fa.flexattn_last_error(), fa.flexattn_last_error()

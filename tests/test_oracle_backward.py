@@ -177,3 +177,18 @@ def test_transposed_block_mask(spec, L, BQ, BK):
         n = -(-L // BQ)
         assert list(tr["q_num_blocks"][0, 0]) == [1] * n
         assert list(tr["full_q_num_blocks"][0, 0]) == [n - 1 - kb for kb in range(n)]
+
+
+def test_group_independence():
+    """With packed documents, the gradients of one document's tokens are those of the document
+    alone (the full-size GPU checks compare slices cut at document boundaries)."""
+    B, H, L, D = 1, 2, 60, 8
+    q, k, v, do = _rand(11, B, H, H, L, L, D)
+    doc = np.repeat(np.arange(4, dtype=np.int32), [10, 25, 5, 20])[None]
+    spec = {"doc": True, "q_doc": doc, "kv_doc": doc, "causal": True}
+    full = G.attention_backward(q, k, v, do, spec)
+    s, e = 10, 40  # documents 1 and 2
+    part = G.attention_backward(q[:, :, s:e], k[:, :, s:e], v[:, :, s:e], do[:, :, s:e],
+                                dict(spec, q_doc=doc[:, s:e], kv_doc=doc[:, s:e]))
+    for f, p in zip(full[:3], part[:3]):
+        _close(f[:, :, s:e], p)

@@ -24,6 +24,7 @@ from .synth import (  # noqa: F401
     bf16_bits_to_f32,
     decode_workload,
     f32_to_bf16_bits,
+    grad_output,
     grouped_sweep,
     make_workload,
     random_case,

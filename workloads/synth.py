@@ -224,3 +224,10 @@ def random_case(seed: int, *, dtype="bf16", B=1, Hq=2, Hkv=None, Lq=200, Lkv=Non
     return Workload(f"random_{seed}", dtype, B, Hq, Hkv, Lq, Lkv, D, q, k, v,
                     doc=doc, causal=causal, window=window, prefix_len=prefix_len,
                     softcap=softcap, alibi_slopes=slopes, q_doc=q_doc, kv_doc=kv_doc)
+
+
+def grad_output(w: Workload, seed: int) -> np.ndarray:
+    """A seeded output gradient dO for w: standard normal [B, Hq, Lq, D], in w's dtype
+    (bf16 bit patterns or float32), from its own generator so that w's draws are unchanged."""
+    rng = np.random.default_rng(10_000_000 + seed)
+    return _normal(rng, (w.B, w.Hq, w.Lq, w.D), w.dtype)
