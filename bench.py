@@ -223,6 +223,78 @@ def run_decode(args, fa, torch, dev):
               flush=True)
 
 
+BWD_WORKLOADS = ["grouped_variate_4096g_bf16", "doc_causal_b4h16t8192_bf16",
+                 "swa1024_gqa32x8_softcap50_t16384_bf16", "dense_b1h32s24576_bf16"]
+
+
+def run_backward(args, fa, torch, dev):
+    """Backward pass (flexattn_bwd) on the bf16 workloads, BlockMask tiles 128 x 128. Each sample
+    is the mean of 5 back-to-back backward calls between two HIP events; median of 5 after 2
+    warm-up samples. The transposed BlockMask is built once beforehand (timed on its own, as a
+    BlockMask's column lists are built with it). FLOPs: 10 * D per allowed pair per query head
+    (S, dP, dV, dQ, dK products); bytes: Q, K, V, O, dO, lse, document ids and both BlockMask
+    views read once, dQ, dK, dV written once."""
+    from workloads import grad_output, make_workload
+    names = [args.workload] if args.workload != DEFAULT_WORKLOAD else BWD_WORKLOADS
+    bf = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+    stream = torch.cuda.current_stream()
+
+    def time_call(call, inner):
+        samples = []
+        for rep in range(7):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(inner):
+                call()
+            e1.record()
+            torch.cuda.synchronize()
+            if rep >= 2:
+                samples.append(e0.elapsed_time(e1) / inner * 1e3)
+        return float(np.median(samples))
+
+    for name in names:
+        w = make_workload(name)
+        q, k, v, do = bf(w.q), bf(w.k), bf(w.v), bf(grad_output(w, 900))
+        mk = (fa.FA_MASK_DOC if w.doc else 0) | (fa.FA_MASK_CAUSAL if w.causal else 0) \
+            | (fa.FA_MASK_WINDOW if w.window is not None else 0)
+        sk = (fa.FA_SCORE_ALIBI if w.alibi_slopes is not None else 0) | (fa.FA_SCORE_SOFTCAP if w.softcap else 0)
+        qd = kd = sl = None
+        if w.doc:
+            qd = torch.from_numpy(np.ascontiguousarray(w.q_doc)).to(dev)
+            kd = torch.from_numpy(np.ascontiguousarray(w.kv_doc)).to(dev)
+        if w.alibi_slopes is not None:
+            sl = torch.from_numpy(w.alibi_slopes).to(dev)
+        kw = dict(window=w.window or 0, prefix_len=w.prefix_len or 0, softcap=w.softcap or 0.0, alibi_slopes=sl,
+                  q_doc=qd, kv_doc=kd)
+        bm = fa.flexattn_block_mask_build(mk, w.B, w.Lq, w.Lkv, 128, 128, q_doc=qd, kv_doc=kd,
+                                          window=w.window or 0, prefix_len=w.prefix_len or 0, device=dev)
+        bmt = fa.flexattn_block_mask_transpose(bm)
+        out, lse = fa.flexattn_fwd(q, k, v, bm, mk, sk, **kw)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ds = torch.empty(w.Hq, dtype=torch.float32, device=dev) if sl is not None else None
+        ws = torch.empty(max(1, fa.flexattn_bwd_workspace_bytes(w.B, w.Hq, w.Lq)), dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        inner = 5
+        t_us = time_call(lambda: fa.flexattn_bwd(q, k, v, out, do, lse, bm, bmt, mk, sk, dq=dq, dk=dk, dv=dv,
+                                                 dslopes=ds, slope_grad=ds is not None, workspace=ws, stream=stream,
+                                                 **kw), inner)
+        tr_us = time_call(lambda: fa.flexattn_block_mask_transpose(bm, out=bmt, stream=stream), inner)
+        pairs = allowed_pairs(w) * w.Hq
+        flops = 10.0 * w.D * pairs
+        el = 2
+        abytes = (4 * w.B * w.Hq * w.Lq + 4 * w.B * w.Hkv * w.Lkv) * w.D * el + w.B * w.Hq * w.Lq * 4
+        abytes += (w.B * (w.Lq + w.Lkv) * 4) if w.doc else 0
+        live = int(bm.kv_num_blocks.sum().item() + bm.full_kv_num_blocks.sum().item())
+        abytes += 2 * (bm.kv_num_blocks.numel() + bmt.q_num_blocks.numel()) * 4 + 2 * live * 4
+        tf = flops / (t_us * 1e-6) / 1e12
+        gb = abytes / (t_us * 1e-6) / 1e9
+        print(json.dumps({"backward": name, "us": t_us, "transpose_us": tr_us, "tflops": tf, "gbs": gb,
+                          "mfma_frac": tf / BF16_PEAK_TFLOPS, "hbm_frac": gb / HBM_PEAK_GBS,
+                          "live_tiles": live, "algorithmic_bytes": abytes, "flops": flops}), flush=True)
+        del q, k, v, do, out, lse, dq, dk, dv, ws, bm, bmt
+        torch.cuda.empty_cache()
+
+
 def run_sweep(args, fa, torch, dev):
     """Group-count sweep of the grouped variate workload. Each sample is the mean of 100
     back-to-back forward launches between two HIP events (the forwards run for microseconds);
@@ -289,6 +361,8 @@ def main():
     ap.add_argument("--decode", action="store_true",
                     help="decoding shape (B=8, GQA 32/8, 16 queries x 32768 keys): flexattn_fwd and "
                          "flexattn_fwd_splitkv over split counts, one JSON line each")
+    ap.add_argument("--backward", action="store_true",
+                    help="backward pass on the bf16 workloads (or --workload NAME), one JSON line each")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (HBM counter calibration for rocprofv3)")
     args = ap.parse_args()
@@ -316,6 +390,9 @@ def main():
         return
     if args.decode:
         run_decode(args, fa, torch, dev)
+        return
+    if args.backward:
+        run_backward(args, fa, torch, dev)
         return
 
     t_gen = time.perf_counter()

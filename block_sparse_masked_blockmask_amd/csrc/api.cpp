@@ -565,7 +565,7 @@ fa_status flexattn_bwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* 
     if (bm->n_qb != nqb || bm->n_kvb != nkvb)
       return fail(FA_ERR_INVALID_ARG, "BlockMask n_qb/n_kvb do not match its lengths and block sizes");
     if (bm->Bm != 1 && bm->Bm != B) return fail(FA_ERR_INVALID_ARG, "BlockMask Bm must be 1 or B");
-    if (bm->Hm != 1 && bm->Hm != Hq) return fail(FA_ERR_INVALID_ARG, "BlockMask Hm must be 1 or Hq");
+    if (bm->Hm != 1) return fail(FA_ERR_UNSUPPORTED, "the backward needs a head-independent BlockMask (Hm = 1)");
     if (bmt->Bm != bm->Bm || bmt->Hm != bm->Hm || bmt->q_len != Lq || bmt->kv_len != Lkv || bmt->q_block != 128 ||
         bmt->kv_block != 128 || bmt->n_qb != nqb || bmt->n_kvb != nkvb)
       return fail(FA_ERR_INVALID_ARG, "the transposed BlockMask's dimensions differ from the BlockMask's");

@@ -46,6 +46,9 @@ namespace {
 
 constexpr int kRows = 64;                  // rows per LDS tile and per step
 constexpr int kTileBytes = kRows * 256;    // [64][128] bf16
+#ifndef DQ_WAVES_PER_EU
+#define DQ_WAVES_PER_EU 2
+#endif
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 
 // Transposed-read base offset of this lane (see the forward kernel): in each 16-lane group,
@@ -58,6 +61,18 @@ __device__ __forceinline__ int tr_base(int lane) {
   return tile_off(r0, d >> 3) + (d & 7) * 2;
 }
 
+// Operand offsets. The swizzle's fields are disjoint bit ranges of the byte offset, so every
+// operand read of a step is one per-lane base XORed with a constant: row reads (A operand X,
+// row lq, channels 16 ks + 8 hl) at kx0 ^ 32 ks; transposed reads of channel block db and
+// rows + 8 j at tb ^ (64 db + 2080 j). Row blocks of 16 add multiples of 4096 bytes (the
+// swizzle depends on the row modulo 16 only), which fold into the instruction's offset. The
+// bases are re-defined per step by an empty asm, so the compiler keeps one register each
+// instead of one per (buffer, offset) pair.
+__device__ __forceinline__ int launder(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 // A operand of X^T (row = channel in block db, k = 16 tile rows from row0, in the order of the
 // accumulator rows i = 8h .. 8h+7 of a 32x32 tile) from a swizzled [rows][128] tile.
 __device__ __forceinline__ bf16x8 read_xt(const unsigned char* tile, int row0, int db, int tb) {
@@ -68,9 +83,9 @@ __device__ __forceinline__ bf16x8 read_xt(const unsigned char* tile, int row0, i
   return __builtin_bit_cast(bf16x8, cat);
 }
 
-// A operand of X (row = tile row r, k = channels 16 ks + 8 hl .. +8).
-__device__ __forceinline__ bf16x8 read_x(const unsigned char* tile, int r, int ks, int hl) {
-  return *(const bf16x8*)(tile + tile_off(r, 2 * ks + hl));
+// A operand of X (row = row0 + lq, k = channels 16 ks + 8 hl .. +8); kx0 = tile_off(lq, hl).
+__device__ __forceinline__ bf16x8 read_x(const unsigned char* tile, int row0, int ks, int kx0) {
+  return *(const bf16x8*)(tile + row0 * 256 + (kx0 ^ (32 * ks)));
 }
 
 // Score and its derivative factor for one pair: returns f (natural units) and sets dfac =
@@ -86,6 +101,53 @@ __device__ __forceinline__ float score_f(const BwdArgs& a, float r, int qi, int 
     s = a.softcap * th;
   }
   return s;
+}
+
+// Branch-free mask_mod for one pair (the predicates of the forward, evaluated with selects so
+// that partial tiles compile to straight-line code). With d = i - j: CAUSAL needs d >= 0,
+// WINDOW d <= window - 1, PREFIX_LM d >= 0 unless j < prefix_len, DOC equal ids.
+struct PairMask {
+  int dlo, dhi, prefix_len;
+  bool prefix, doc;
+};
+
+__device__ __forceinline__ PairMask make_pair_mask(const BwdArgs& a) {
+  PairMask m;
+  m.dlo = (a.flags & FA_MASK_CAUSAL) ? 0 : INT_MIN;
+  m.dhi = (a.flags & FA_MASK_WINDOW) ? a.window - 1 : INT_MAX;
+  m.prefix = (a.flags & FA_MASK_PREFIX_LM) != 0;
+  m.prefix_len = a.prefix_len;
+  m.doc = (a.flags & FA_MASK_DOC) != 0;
+  return m;
+}
+
+__device__ __forceinline__ bool pair_ok(const PairMask& m, int i, int j, int qd, int kd) {
+  const int d = i - j;
+  const int lo = (m.prefix & (j >= m.prefix_len)) ? 0 : m.dlo;
+  return (d >= lo) & (d <= m.dhi) & (!m.doc | (qd == kd));
+}
+
+// Schedules of the product chains (scheduling-group masks: 0x008 MFMA, 0x100 LDS read): the
+// operand reads run at most a few products ahead instead of all at once, which would hold up to
+// 64 registers of operands in flight.
+// N pairs of products with one 16-byte read each: 4 reads ahead, then 2 products per 2 reads.
+template <int N> __device__ __forceinline__ void sched_pairs() {
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    if (k + 2 < N) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+}
+// N products with two transposed 8-byte reads each: 2 products' reads ahead, then 1 product
+// per 2 reads.
+template <int N> __device__ __forceinline__ void sched_tr() {
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (k + 2 < N) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
 }
 
 // Stage rows [r0, r0 + 64) of two [L][128] bf16 tensors into registers (4 chunks of 16 bytes
@@ -152,24 +214,106 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------
+// Tile transfers. Each step moves 64 rows of two [L][128] bf16 tensors into LDS with
+// global_load_lds_dwordx4 (LDS written directly, no registers): 16 one-KB segments of 4 rows per
+// tensor, segment 4 i + wave issued by that wave. Lane l of a segment writes LDS chunk slot
+// l % 16 of row l / 16; it loads global chunk slot ^ swz(row), so the tile lands swizzled. Rows
+// at or past the end re-read the last row (finite data; the kernels mask them). Row-wise values
+// (16 per wave) follow as 4-byte transfers; every step issues the same number of transfers per
+// wave, so waiting for a step is one s_waitcnt vmcnt with a constant count.
+// ---------------------------------------------------------------------------------------------
+namespace {
+
+__device__ __forceinline__ void dma16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 4, 0, 0);
+}
+// The compiler does not track the LDS writes of global_load_lds: at most N vector-memory
+// operations of this wave may still be outstanding after this.
+template <int N> __device__ __forceinline__ void wait_vmem() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+struct Lane {
+  int wave, lane, hl, lq;
+  int r_l;   // row of this lane in its first segment (4 wave + lane / 16); later segments add 16
+  int ch;    // global chunk this lane loads (slot ^ swz(row), the same for every segment)
+  int tb;    // transposed-read base offset
+  int kx0;   // row-read base offset, tile_off(lq, hl)
+};
+
+__device__ __forceinline__ Lane make_lane() {
+  Lane c;
+  c.lane = threadIdx.x & 63;
+  c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  c.hl = c.lane >> 5;
+  c.lq = c.lane & 31;
+  c.r_l = 4 * c.wave + (c.lane >> 4);
+  c.ch = (c.lane & 15) ^ swz(c.r_l);
+  c.tb = tr_base(c.lane);
+  c.kx0 = tile_off(c.lq, c.hl);
+  return c;
+}
+
+// 8 transfers: rows [r0, r0 + 64) of x and y (row strides xsl, ysl). xoff / yoff are the lane's
+// element offsets in its first segment (r_l * stride + ch * 8), so the address of a full step is
+// a uniform base plus one 32-bit lane offset; a step reaching past row L - 1 clamps per row.
+__device__ __forceinline__ void issue_tiles(const Lane& c, const __bf16* xp, int64_t xsl, int xoff, const __bf16* yp,
+                                            int64_t ysl, int yoff, int r0, int L, unsigned char* sx,
+                                            unsigned char* sy) {
+  if (r0 + kRows <= L) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int seg = 4 * i + c.wave;
+      dma16(xp + (int64_t)(r0 + 16 * i) * xsl + xoff, sx + seg * 1024);
+      dma16(yp + (int64_t)(r0 + 16 * i) * ysl + yoff, sy + seg * 1024);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t r = min(r0 + c.r_l + 16 * i, L - 1);
+      const int seg = 4 * i + c.wave;
+      dma16(xp + r * xsl + c.ch * 8, sx + seg * 1024);
+      dma16(yp + r * ysl + c.ch * 8, sy + seg * 1024);
+    }
+  }
+}
+
+// 1 transfer: 16 row-wise 4-byte values per wave (rows r0 + 16 wave + lane, clamped), from
+// base[row]; base may be a valid dummy address when the values are unused.
+__device__ __forceinline__ void issue_rowvals(const Lane& c, const void* base, bool use, int r0, int L, void* dst) {
+  if (c.lane < 16) {
+    const char* src = (const char*)base + (use ? 4 * (int64_t)min(r0 + 16 * c.wave + c.lane, L - 1) : 0);
+    dma4(src, (char*)dst + 64 * c.wave);
+  }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------------------------
 // dQ (and the slope-gradient partials): one workgroup per (b, hq, 128-query block).
 // ---------------------------------------------------------------------------------------------
 template <int SCORE>
-__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(1024))) unsigned char sK[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char sV[kTileBytes];
-  __shared__ int sDoc[kRows];
+__global__ __launch_bounds__(256, DQ_WAVES_PER_EU) void bwd_dq_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(1024))) unsigned char sK0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char sV0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char sK1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char sV1[kTileBytes];
+  __shared__ __attribute__((aligned(16))) int sD0[kRows];
+  __shared__ __attribute__((aligned(16))) int sD1[kRows];
   __shared__ float sRed[4];
+  constexpr int kOps = 9;  // transfers per wave and step
 
   int w = blockIdx.x;
   const int qb = w % a.nqb;
   w /= a.nqb;
   const int hq = w % a.Hq, b = w / a.Hq;
   const int hkv = hq / a.group;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hl = lane >> 5, lq = lane & 31;
-  const int qi = qb * 128 + wave * 32 + lq;
+  const Lane c = make_lane();
+  const int hl = c.hl, lq = c.lq;
+  const int qi = qb * 128 + c.wave * 32 + lq;
   const bool q_in = qi < a.Lq;
   const int qc = min(qi, a.Lq - 1);
   const bool doc = (a.flags & FA_MASK_DOC) != 0;
@@ -188,11 +332,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
   const float delta = q_in ? a.delta[row] : 0.f;
   const int qdoc = doc ? a.q_doc[(int64_t)b * a.Lq + qc] : 0;
   const float slope = (SCORE & FA_SCORE_ALIBI) ? a.slopes[hq] : 0.f;
-  const MaskSpec ms{a.flags, a.window, a.prefix_len};
-  const int tb = tr_base(lane);
+  const PairMask pm = make_pair_mask(a);
 
   const __bf16* kp = (const __bf16*)a.k + b * a.k_sb + hkv * a.k_sh;
   const __bf16* vp = (const __bf16*)a.v + b * a.v_sb + hkv * a.v_sh;
+  const int* kvdoc = doc ? a.kv_doc + (int64_t)b * a.Lkv : (const int*)kp;
+  const int koff = c.r_l * (int)a.k_sl + c.ch * 8, voff = c.r_l * (int)a.v_sl + c.ch * 8;
 
   int nfull, npart;
   const int* full = nullptr;
@@ -201,8 +346,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
     nfull = (a.Lkv + 127) / 128;
     npart = 0;
   } else {
-    const int bm = a.Bm == 1 ? 0 : b, hm = a.Hm == 1 ? 0 : hq;
-    const int64_t r = ((int64_t)bm * a.Hm + hm) * a.nqb + qb;
+    const int bm = a.Bm == 1 ? 0 : b;
+    const int64_t r = (int64_t)bm * a.nqb + qb;
     nfull = a.full_num[r];
     npart = a.kv_num[r];
     full = a.full_idx + r * a.nkvb;
@@ -217,86 +362,84 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
     masked = partial || kv0 + kRows > a.Lkv;
     return kv0;
   };
+  auto issue = [&](int s, unsigned char* sK, unsigned char* sV, int* sD) {
+    bool m;
+    const int kv0 = step_kv0(s, m);
+    issue_tiles(c, kp, a.k_sl, koff, vp, a.v_sl, voff, kv0, a.Lkv, sK, sV);
+    issue_rowvals(c, kvdoc, doc, kv0, a.Lkv, sD);
+  };
 
   f32x16 dqacc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) dqacc[db] = f32x16{};
   float slope_acc = 0.f;
 
-  Stage st;
-  int dstage = 0;
-  bool m_next = false;
-  int kv_next = nsteps > 0 ? step_kv0(0, m_next) : 0;
-  if (nsteps > 0 && kv_next < a.Lkv) {
-    stage_load(st, kp, a.k_sl, vp, a.v_sl, kv_next, a.Lkv, tid);
-    if (doc && tid < kRows) dstage = a.kv_doc[(int64_t)b * a.Lkv + min(kv_next + tid, a.Lkv - 1)];
-  }
-  for (int s = 0; s < nsteps; ++s) {
-    const int kv0 = kv_next;
-    const bool masked = m_next;
-    if (kv0 >= a.Lkv) {  // second half of a ragged last tile: no keys (uniform over the workgroup)
-      if (s + 1 < nsteps) {
-        kv_next = step_kv0(s + 1, m_next);
-        if (kv_next < a.Lkv) {
-          stage_load(st, kp, a.k_sl, vp, a.v_sl, kv_next, a.Lkv, tid);
-          if (doc && tid < kRows) dstage = a.kv_doc[(int64_t)b * a.Lkv + min(kv_next + tid, a.Lkv - 1)];
-        }
-      }
-      continue;
-    }
-    __syncthreads();  // the previous step's reads of sK / sV are done
-    stage_store(st, sK, sV, kv0, a.Lkv, tid);
-    if (doc && tid < kRows) sDoc[tid] = dstage;
-    __syncthreads();
-    if (s + 1 < nsteps) {
-      kv_next = step_kv0(s + 1, m_next);
-      if (kv_next < a.Lkv) {
-        stage_load(st, kp, a.k_sl, vp, a.v_sl, kv_next, a.Lkv, tid);
-        if (doc && tid < kRows) dstage = a.kv_doc[(int64_t)b * a.Lkv + min(kv_next + tid, a.Lkv - 1)];
-      }
-    }
-
-    f32x16 sacc[2], dpacc[2];
-#pragma unroll
+  auto compute = [&](int s, const unsigned char* sK, const unsigned char* sV, const int* sD) {
+    bool masked;
+    const int kv0 = step_kv0(s, masked);
+    const int kx0 = launder(c.kx0), tb = launder(c.tb);
+#pragma unroll 1
     for (int nb = 0; nb < 2; ++nb) {
-      sacc[nb] = f32x16{};
-      dpacc[nb] = f32x16{};
+      f32x16 sacc = f32x16{}, dpacc = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        sacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_x(sK, nb * 32 + lq, ks, hl), qreg[ks], sacc[nb], 0, 0, 0);
-        dpacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_x(sV, nb * 32 + lq, ks, hl), doreg[ks], dpacc[nb], 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_x(sK, nb * 32, ks, kx0), qreg[ks], sacc, 0, 0, 0);
+        dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_x(sV, nb * 32, ks, kx0), doreg[ks], dpacc, 0, 0, 0);
       }
-    }
-    bf16x8 dsb[2][2];
+      sched_pairs<8>();
+      bf16x8 dsb[2];
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
+      for (int gq = 0; gq < 4; ++gq) {
+        const int kr4 = nb * 32 + 8 * gq + 4 * hl;
+        const i32x4 d4 = *(const i32x4*)(sD + kr4);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int kr = nb * 32 + 8 * (i >> 2) + 4 * hl + (i & 3);
-        const int kv = kv0 + kr;
-        float dfac;
-        const float f = score_f<SCORE>(a, sacc[nb][i], qi, kv, slope, dfac);
-        float p = fast_exp2(fmaf(f, kLog2e, -lse2));
-        if (masked) {
-          const bool keep = kv < a.Lkv && mask_pair(ms, qi, kv, qdoc, doc ? sDoc[kr] : 0);
-          p = keep ? p : 0.f;
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * gq + e;
+          const int kv = kv0 + kr4 + e;
+          float dfac;
+          const float f = score_f<SCORE>(a, sacc[i], qi, kv, slope, dfac);
+          float p = fast_exp2(fmaf(f, kLog2e, -lse2));
+          if (masked) p = ((kv < a.Lkv) & pair_ok(pm, qi, kv, qdoc, d4[e])) ? p : 0.f;
+          float da = p * (dpacc[i] - delta);
+          if constexpr (SCORE & FA_SCORE_SOFTCAP) da *= dfac;
+          if constexpr (SCORE & FA_SCORE_ALIBI) slope_acc = fmaf(-da, fabsf((float)(qi - kv)), slope_acc);
+          dsb[i >> 3][i & 7] = (__bf16)da;
         }
-        float da = p * (dpacc[nb][i] - delta);
-        if constexpr (SCORE & FA_SCORE_SOFTCAP) da *= dfac;
-        if constexpr (SCORE & FA_SCORE_ALIBI) slope_acc = fmaf(-da, fabsf((float)(qi - kv)), slope_acc);
-        dsb[nb][i >> 3][i & 7] = (__bf16)da;
       }
-    }
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
+      for (int db = 0; db < 4; ++db) {
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-          dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_xt(sK, nb * 32 + h * 16, db, tb), dsb[nb][h],
+          dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_xt(sK, nb * 32 + h * 16, db, tb), dsb[h],
                                                               dqacc[db], 0, 0, 0);
       }
+      sched_tr<8>();
     }
+  };
+
+  // Two LDS buffers, selected at compile time (the loop handles two steps per iteration):
+  // step s + 1 is issued into the other buffer before step s is waited for and computed.
+  if (nsteps > 0) issue(0, sK0, sV0, sD0);
+  for (int s = 0; s < nsteps; s += 2) {
+    if (s + 1 < nsteps) {
+      issue(s + 1, sK1, sV1, sD1);
+      wait_vmem<kOps>();
+    } else {
+      wait_vmem<0>();
+    }
+    __syncthreads();
+    compute(s, sK0, sV0, sD0);
+    __syncthreads();
+    if (s + 1 >= nsteps) break;
+    if (s + 2 < nsteps) {
+      issue(s + 2, sK0, sV0, sD0);
+      wait_vmem<kOps>();
+    } else {
+      wait_vmem<0>();
+    }
+    __syncthreads();
+    compute(s + 1, sK1, sV1, sD1);
+    __syncthreads();
   }
 
   // dQ[qi][channel]: lane holds channels 32 db + 8 gq + 4 hl + 0..3 of its query.
@@ -316,9 +459,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
   if constexpr (SCORE & FA_SCORE_ALIBI) {
     if (a.dslopes) {
       const float ws = wave_sum(slope_acc);
-      if (lane == 0) sRed[wave] = ws;
+      if (c.lane == 0) sRed[c.wave] = ws;
       __syncthreads();
-      if (tid == 0) a.slope_part[((int64_t)b * a.Hq + hq) * a.nqb + qb] = (sRed[0] + sRed[1]) + (sRed[2] + sRed[3]);
+      if (threadIdx.x == 0) a.slope_part[((int64_t)b * a.Hq + hq) * a.nqb + qb] = (sRed[0] + sRed[1]) + (sRed[2] + sRed[3]);
     }
   }
 }
@@ -358,7 +501,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   }
   const int kdoc = doc ? a.kv_doc[(int64_t)b * a.Lkv + kc] : 0;
   const MaskSpec ms{a.flags, a.window, a.prefix_len};
-  const int tb = tr_base(lane);
+  const int tb = tr_base(lane), kx0 = tile_off(lq, hl);
 
   f32x16 dkacc[4], dvacc[4];
 #pragma unroll
@@ -422,8 +565,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
         f32x16 sacc = f32x16{}, dpacc = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_x(sQ, sub * 32 + lq, ks, hl), kreg[ks], sacc, 0, 0, 0);
-          dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_x(sO, sub * 32 + lq, ks, hl), vreg[ks], dpacc, 0, 0, 0);
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_x(sQ, sub * 32, ks, kx0), kreg[ks], sacc, 0, 0, 0);
+          dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_x(sO, sub * 32, ks, kx0), vreg[ks], dpacc, 0, 0, 0);
         }
         bf16x8 pb[2], dsb[2];
 #pragma unroll

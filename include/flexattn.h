@@ -221,7 +221,7 @@ size_t flexattn_bwd_workspace_bytes(int B, int Hq, int Lq);
  *   - out and lse are those of flexattn_fwd on the same inputs (lse natural log, float32
  *     [B][Hq][Lq] contiguous; -inf rows get zero gradients);
  *   - bm and bmt: the forward's BlockMask and its transpose (flexattn_block_mask_transpose), both
- *     with 128 x 128 tiles (other tile sizes are FA_ERR_UNSUPPORTED), or both NULL with mask_kind
+ *     with 128 x 128 tiles and Hm = 1 (otherwise FA_ERR_UNSUPPORTED), or both NULL with mask_kind
  *     NONE. As in the forward the BlockMask decides which tiles are visited and mask_kind is
  *     evaluated on partial tiles;
  *   - dslopes: float32 [Hq] device, overwritten with the slope gradient summed over batches; NULL
