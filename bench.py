@@ -235,7 +235,7 @@ def run_backward(args, fa, torch, dev):
     (S, dP, dV, dQ, dK products); bytes: Q, K, V, O, dO, lse, document ids and both BlockMask
     views read once, dQ, dK, dV written once."""
     from workloads import grad_output, make_workload
-    names = [args.workload] if args.workload != DEFAULT_WORKLOAD else BWD_WORKLOADS
+    names = [args.workload] if args.workload else BWD_WORKLOADS
     bf = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
     stream = torch.cuda.current_stream()
 
@@ -348,7 +348,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--workload", default=None, help=f"workload name (default {DEFAULT_WORKLOAD}; with --backward: all bf16 workloads)")
     ap.add_argument("--kv-block", type=int, default=None, help="BlockMask kv block (default 64 bf16, 128 f32)")
     ap.add_argument("--q-block", type=int, default=None, help="BlockMask q block (default 128)")
     ap.add_argument("--quantized", action="store_true",
@@ -394,6 +394,8 @@ def main():
     if args.backward:
         run_backward(args, fa, torch, dev)
         return
+    if args.workload is None:
+        args.workload = DEFAULT_WORKLOAD
 
     t_gen = time.perf_counter()
     w = make_workload(args.workload)

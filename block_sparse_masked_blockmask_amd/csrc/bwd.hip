@@ -20,14 +20,19 @@
 //                       each wave computes S^T = K Q^T and dP^T = V dO^T with Q^T and dO^T held
 //                       in registers as B operands (a lane owns one query), then
 //                       dQ^T += K^T dA^T with dA^T straight from the accumulators as the B
-//                       operand and K^T read from LDS with ds_read_b64_tr_b16. Also sums the
-//                       ALiBi-slope gradient of its rows;
+//                       operand and K^T read from LDS with ds_read_b64_tr_b16. K and V tiles
+//                       stream into two LDS buffers by global_load_lds, one step ahead; two
+//                       waves per SIMD. Also sums the ALiBi-slope gradient of its rows;
 //   bwd_dkdv_kernel     one workgroup of 4 waves per (b, kv head, 128-key block), walking the
 //                       column's q blocks (the transposed BlockMask) for every query head of the
 //                       group, in steps of 64 queries. Mirrored orientation: S = Q K^T and
 //                       dP = dO V^T with K^T and V^T held in registers (a lane owns one key),
 //                       then dV^T += dO^T P and dK^T += Q^T dA, both A operands read transposed
-//                       from LDS. GQA sums over the group inside the workgroup (no atomics);
+//                       from LDS. GQA sums over the group inside the workgroup (no atomics).
+//                       K^T, V^T and both accumulators hold 192 registers, so it runs at one
+//                       wave per SIMD; Q and dO tiles are staged through registers (with LDS-DMA
+//                       at one wave per SIMD, issuing the transfers stalled the only wave and
+//                       measured slower; splitting dK and dV into two kernels spilled);
 //   bwd_slope_kernel    sums the per-block slope partials into dslopes[h] (deterministic).
 //
 // Accumulator layout (32x32 MFMA): element i of lane l holds row 8*(i/4) + 4*(l/32) + i%4 and
@@ -46,9 +51,6 @@ namespace {
 
 constexpr int kRows = 64;                  // rows per LDS tile and per step
 constexpr int kTileBytes = kRows * 256;    // [64][128] bf16
-#ifndef DQ_WAVES_PER_EU
-#define DQ_WAVES_PER_EU 2
-#endif
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 
 // Transposed-read base offset of this lane (see the forward kernel): in each 16-lane group,
@@ -296,7 +298,7 @@ __device__ __forceinline__ void issue_rowvals(const Lane& c, const void* base, b
 // dQ (and the slope-gradient partials): one workgroup per (b, hq, 128-query block).
 // ---------------------------------------------------------------------------------------------
 template <int SCORE>
-__global__ __launch_bounds__(256, DQ_WAVES_PER_EU) void bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char sK0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char sV0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char sK1[kTileBytes];
