@@ -20,7 +20,9 @@ PyTorch 2.5"; sage2 form = FlashRT-Structures PR #1 "LTX-2.5 attention forms"):
                 Mechanics", item 1 (128x128 tile block sparsity).
   quant.py      int8 Q/K and fp8 (OCP E4M3) V quantization — the sage2 form's
                 "qk-int8/pv-fp8" description; encodings from the OCP 8-bit
-                floating point specification (OFP8, E4M3).
+                floating point specification (OFP8, E4M3); the refinements of the
+                same PR (finer per-warp Q/K scales, K centering with its delta
+                correction).
   brute.py      pure-Python loops on tiny inputs; an independent restatement used
                 only to pin attention.py.
   backward.py   dQ, dK, dV and the ALiBi-slope gradient of attention.py's output —

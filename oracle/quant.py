@@ -132,3 +132,48 @@ def attention_dequantized(q8, sq, k8, sk, v8, sv, rows, b, h, *, sm_scale=None, 
     l = p.sum(axis=1, keepdims=True)
     pr = e4m3_decode_array(e4m3_encode(p * E4M3_MAX)) / E4M3_MAX if round_p else p
     return (pr @ vh) / l
+
+
+# ---------------------------------------------------------------------------------------------
+# Refinements of the form (FlashRT-Structures PR #1, "LTX-2.5 attention forms": the sage2 form
+# takes Q/K scales per warp or per thread, and the fused prep of its FP4 sibling centres the
+# inputs and applies a delta correction).
+#
+# Finer Q/K scales: quantize_int8_blocks with block=32 gives one scale per 32 tokens (one wave
+# of 32 queries, or one 32-key sub-block of the kernel).
+#
+# K centering: K' = K - mu with mu[b, h, c] the mean of K over tokens. Softmax rows are
+# invariant to adding a constant per row, and q_i . (k_j - mu) = q_i . k_j - q_i . mu, so the
+# output is unchanged; only lse moves, by sm_scale * (q_i . mu), which the correction restores.
+# Centering removes a common offset of the keys, so the int8 scale of a block follows the
+# spread of the keys rather than their offset.
+# ---------------------------------------------------------------------------------------------
+def k_channel_mean(k_f32: np.ndarray) -> np.ndarray:
+    """mu[b, h, c] = mean over tokens of K, as float32: the exactly rounded sum (math.fsum) divided
+    by L in float64, then rounded to float32. L = 0 gives 0."""
+    import math
+    k = np.asarray(k_f32, dtype=np.float32)
+    B, H, L, D = k.shape
+    mu = np.zeros((B, H, D), dtype=np.float32)
+    if L == 0:
+        return mu
+    for b in range(B):
+        for h in range(H):
+            for c in range(D):
+                mu[b, h, c] = np.float32(math.fsum(k[b, h, :, c].astype(np.float64).tolist()) / L)
+    return mu
+
+
+def center_k(k_f32: np.ndarray, mu: np.ndarray) -> np.ndarray:
+    """K - mu per (b, h, channel), one float32 subtraction per element."""
+    k = np.asarray(k_f32, dtype=np.float32)
+    return (k - np.asarray(mu, dtype=np.float32)[:, :, None, :]).astype(np.float32)
+
+
+def q_dot_mean(q_f32: np.ndarray, mu: np.ndarray) -> np.ndarray:
+    """delta[b, hq, i] = q_i . mu[b, hq // group] in float64 (the lse correction without sm_scale)."""
+    q = np.asarray(q_f32, dtype=np.float64)
+    mu = np.asarray(mu, dtype=np.float64)
+    group = q.shape[1] // mu.shape[1]
+    mq = np.repeat(mu, group, axis=1)                      # [B, Hq, D]
+    return np.einsum("bhld,bhd->bhl", q, mq)

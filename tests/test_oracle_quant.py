@@ -87,3 +87,49 @@ def test_fp8_channels_scale_and_bound():
     # The absmax entry of every channel encodes to +-448 exactly.
     dec = Q.e4m3_decode_array(codes)
     assert np.allclose(np.abs(dec).max(axis=2), 448.0)
+
+
+def test_int8_block32_hand_values():
+    # Two 32-row blocks with different magnitudes: each block gets its own amax / 127.
+    x = np.zeros((1, 1, 64, 4), np.float32)
+    x[0, 0, 3, 1] = 2.54     # block 0 amax
+    x[0, 0, 10, 2] = -1.0
+    x[0, 0, 40, 0] = 0.127   # block 1 amax
+    x[0, 0, 50, 3] = 0.0635
+    codes, scales = Q.quantize_int8_blocks(x, block=32)
+    assert scales.shape == (1, 1, 2)
+    assert scales[0, 0, 0] == np.float32(np.float32(2.54) / np.float32(127.0))
+    assert scales[0, 0, 1] == np.float32(np.float32(0.127) / np.float32(127.0))
+    assert codes[0, 0, 3, 1] == 127 and codes[0, 0, 40, 0] == 127
+    assert codes[0, 0, 10, 2] == -50                        # -1 / 0.02 = -50
+    assert codes[0, 0, 50, 3] == 64                         # 0.0635 / 0.001 = 63.5 -> ties to even 64
+    # The coarse block takes the larger magnitude for both halves.
+    c128, s128 = Q.quantize_int8_blocks(x, block=128)
+    assert s128[0, 0, 0] == scales[0, 0, 0] and c128[0, 0, 40, 0] == 6   # 0.127 / 0.02 = 6.35 -> 6
+
+
+def test_centering_keeps_output_and_shifts_lse():
+    """Closed form: attention(q, k - mu, v) = attention(q, k, v) and lse moves by
+    sm_scale * q . mu (pinned against the separately pinned attention oracle)."""
+    from oracle import attention as A
+    rng = np.random.default_rng(3)
+    B, Hq, Hkv, L, D = 2, 4, 2, 37, 16
+    q = rng.standard_normal((B, Hq, L, D)).astype(np.float32)
+    k = (rng.standard_normal((B, Hkv, L, D)) + 3.0 * rng.standard_normal((1, Hkv, 1, D))).astype(np.float32)
+    v = rng.standard_normal((B, Hkv, L, D)).astype(np.float32)
+    mu = Q.k_channel_mean(k)
+    np.testing.assert_allclose(mu, k.astype(np.float64).mean(axis=2), rtol=0, atol=1e-6)
+    kc = Q.center_k(k, mu)
+    o1, l1 = A.attention(q, k, v, {})
+    o2, l2 = A.attention(q, kc, v, {})
+    delta = Q.q_dot_mean(q, mu)
+    np.testing.assert_allclose(o2, o1, rtol=0, atol=1e-5)
+    np.testing.assert_allclose(l2 + delta / np.sqrt(D), l1, rtol=0, atol=1e-4)
+    assert np.abs(kc.astype(np.float64).mean(axis=2)).max() < 1e-5
+
+
+def test_k_mean_is_exactly_rounded():
+    # Values whose float32 running sum loses bits: the fsum-based mean is exact.
+    k = np.zeros((1, 1, 4, 1), np.float32)
+    k[0, 0, :, 0] = [1e8, 1.0, -1e8, 1.0]
+    assert Q.k_channel_mean(k)[0, 0, 0] == np.float32(0.5)
