@@ -353,6 +353,9 @@ def main():
     ap.add_argument("--q-block", type=int, default=None, help="BlockMask q block (default 128)")
     ap.add_argument("--quantized", action="store_true",
                     help="int8-QK / fp8-PV form (unmasked workloads): step = quantize + quantized forward")
+    ap.add_argument("--refined", action="store_true",
+                    help="with --quantized: 32-token Q/K scales and K centring (flexattn_quantize_qkv_ex + "
+                         "flexattn_fwd_quant)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true", help="skip the achievable-peak measurements")
     ap.add_argument("--sweep", action="store_true",
@@ -426,15 +429,26 @@ def main():
         if mk or sk or w.dtype != "bf16":
             print(json.dumps({"error": "the quantized form serves unmasked bf16 workloads only"}))
             sys.exit(2)
-        qbufs = fa.flexattn_quantize_qkv(q, k, v, stream=stream)
+        if args.refined:
+            qbufs = fa.flexattn_quantize_qkv_ex(q, k, v, qk_block=32, center_k=True, stream=stream)
+            qws = torch.empty(max(1, fa.flexattn_quantize_qkv_ex_workspace_bytes(w.B, w.Hkv, w.Lkv)),
+                              dtype=torch.uint8, device=dev)
+        else:
+            qbufs = fa.flexattn_quantize_qkv(q, k, v, stream=stream)
         bm = None
 
     def step_quant(ev=None):
-        fa.flexattn_quantize_qkv(q, k, v, out=qbufs, stream=stream)
+        if args.refined:
+            fa.flexattn_quantize_qkv_ex(q, k, v, qk_block=32, center_k=True, out=qbufs, workspace=qws, stream=stream)
+        else:
+            fa.flexattn_quantize_qkv(q, k, v, out=qbufs, stream=stream)
         if ev is not None:
             ev[0].record(stream)
-        fa.flexattn_fwd(qbufs["q8"], qbufs["k8"], qbufs["v8"], q_scale=qbufs["q_scale"], k_scale=qbufs["k_scale"],
-                        v_scale=qbufs["v_scale"], out=out, lse=lse, stream=stream)
+        if args.refined:
+            fa.flexattn_fwd_quant(qbufs, out=out, lse=lse, stream=stream)
+        else:
+            fa.flexattn_fwd(qbufs["q8"], qbufs["k8"], qbufs["v8"], q_scale=qbufs["q_scale"],
+                            k_scale=qbufs["k_scale"], v_scale=qbufs["v_scale"], out=out, lse=lse, stream=stream)
         if ev is not None:
             ev[1].record(stream)
 
@@ -480,7 +494,7 @@ def main():
     fwd_tflops = flops / (fwd_avg_ms * 1e-3) / 1e12
     fwd_gbs = abytes / (fwd_avg_ms * 1e-3) / 1e9
     hbm_bound = (flops / abytes) < (BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9))
-    traffic = read_traffic(args.workload + ("_quantized" if args.quantized else ""))
+    traffic = read_traffic(args.workload + ("_quantized" if args.quantized else "")) if not args.refined else None
     if args.quantized:
         roof = {"bound": "mfma", "achieved": fwd_tflops, "peak": INT8_FP8_PEAK_TOPS, "unit": "TFLOP/s"}
     elif w.dtype == "f32":
@@ -503,7 +517,9 @@ def main():
         "data": "synthetic (seeded numpy PCG64)",
         "config": {"workload": args.workload, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Lq": w.Lq, "Lkv": w.Lkv,
                    "D": w.D, "mask": mk, "score": sk, "q_block": args.q_block, "kv_block": args.kv_block,
-                   "step": "quantize_qkv + fwd (int8 QK, fp8 PV)" if args.quantized else "block_mask_build + fwd"},
+                   "step": ("quantize_qkv_ex (32-token Q/K scales, K centring) + fwd_quant (int8 QK, fp8 PV)"
+                            if args.refined else "quantize_qkv + fwd (int8 QK, fp8 PV)") if args.quantized
+                   else "block_mask_build + fwd"},
         "hbm_gbs": abytes / (ms_per_step * 1e-3) / 1e9,
         "fwd_only": {"ms": fwd_avg_ms, "tflops": fwd_tflops, "gbs": fwd_gbs},
         "roofline": roof,

@@ -12,7 +12,8 @@ from .flexattn import (  # noqa: F401
     flexattn_block_mask_build, flexattn_block_mask_build_host, flexattn_block_mask_count_bytes,
     flexattn_block_mask_index_bytes, flexattn_block_mask_transpose, flexattn_bwd, flexattn_bwd_workspace_bytes,
     flexattn_block_mask_workspace_bytes, flexattn_fwd, flexattn_fwd_splitkv, flexattn_fwd_splitkv_workspace_bytes,
-    flexattn_last_error, flexattn_quantize_qkv,
+    flexattn_fwd_quant, flexattn_last_error, flexattn_quantize_qkv, flexattn_quantize_qkv_ex,
+    flexattn_quantize_qkv_ex_workspace_bytes,
     flexattn_version,
     lib, tensor_desc,
 )

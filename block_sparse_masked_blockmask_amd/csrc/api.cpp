@@ -222,7 +222,7 @@ static fa_status check_tensor(const fa_tensor* t, const char* name, int elem_ali
 
 static fa_status fwd_quantized(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_block_mask* bm,
                                int mask_kind, int score_kind, const fa_params* p, fa_tensor* out, float* lse,
-                               hipStream_t stream);
+                               int qk_block, const float* q_delta, hipStream_t stream);
 
 size_t flexattn_fwd_splitkv_workspace_bytes(int B, int Hq, int Lq, int n_splits) {
   if (B < 0 || Hq < 0 || Lq < 0 || n_splits < 1) return 0;
@@ -368,7 +368,7 @@ fa_status flexattn_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* 
                        int mask_kind, int score_kind, const fa_params* p, fa_tensor* out, float* lse,
                        hipStream_t stream) {
   if (!q || !k || !v || !out) return fail(FA_ERR_INVALID_ARG, "q, k, v and out must not be NULL");
-  if (q->dtype == FA_I8) return fwd_quantized(q, k, v, bm, mask_kind, score_kind, p, out, lse, stream);
+  if (q->dtype == FA_I8) return fwd_quantized(q, k, v, bm, mask_kind, score_kind, p, out, lse, 128, nullptr, stream);
   return fwd_impl(q, k, v, bm, mask_kind, score_kind, p, out, lse, 1, nullptr, 0, stream);
 }
 
@@ -379,6 +379,12 @@ fa_status flexattn_fwd_splitkv(const fa_tensor* q, const fa_tensor* k, const fa_
   if (n_splits < 1 || n_splits > 256) return fail(FA_ERR_INVALID_ARG, "n_splits must be in [1, 256] (got %d)", n_splits);
   if (q->dtype == FA_I8) return fail(FA_ERR_UNSUPPORTED, "split-KV does not serve the quantized form");
   return fwd_impl(q, k, v, bm, mask_kind, score_kind, p, out, lse, n_splits, workspace, workspace_bytes, stream);
+}
+
+fa_status flexattn_fwd_quant(const fa_tensor* q8, const fa_tensor* k8, const fa_tensor* v8, int qk_block,
+                             const float* q_delta, const fa_params* p, fa_tensor* out, float* lse, hipStream_t stream) {
+  if (!q8 || !k8 || !v8 || !out) return fail(FA_ERR_INVALID_ARG, "q8, k8, v8 and out must not be NULL");
+  return fwd_quantized(q8, k8, v8, nullptr, FA_MASK_NONE, FA_SCORE_NONE, p, out, lse, qk_block, q_delta, stream);
 }
 
 static fa_status check_q_tensor(const fa_tensor* t, const char* name, int dtype, int elem_align) {
@@ -395,9 +401,16 @@ static fa_status check_q_tensor(const fa_tensor* t, const char* name, int dtype,
   return FA_OK;
 }
 
-fa_status flexattn_quantize_qkv(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, fa_tensor* q8,
-                                fa_tensor* k8, fa_tensor* v8, hipStream_t stream) {
+size_t flexattn_quantize_qkv_ex_workspace_bytes(int B, int Hkv, int Lkv) {
+  if (B < 0 || Hkv < 0 || Lkv < 0) return 0;
+  return (size_t)B * Hkv * fa::quant_mean_chunks(Lkv) * 128 * sizeof(double);
+}
+
+static fa_status quantize_impl(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, fa_tensor* q8,
+                               fa_tensor* k8, fa_tensor* v8, int qk_block, float* k_mean, float* q_delta,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
   fa_status st;
+  if (qk_block != 128 && qk_block != 32) return fail(FA_ERR_UNSUPPORTED, "qk_block must be 128 or 32 (got %d)", qk_block);
   if ((st = check_q_tensor(q, "q", FA_BF16, 8)) != FA_OK) return st;
   if ((st = check_q_tensor(k, "k", FA_BF16, 8)) != FA_OK) return st;
   if ((st = check_q_tensor(v, "v", FA_BF16, 8)) != FA_OK) return st;
@@ -411,7 +424,25 @@ fa_status flexattn_quantize_qkv(const fa_tensor* q, const fa_tensor* k, const fa
     return fail(FA_ERR_INVALID_ARG, "quantized outputs must have the shapes of their sources");
   if ((int64_t)q->B * q->H > 65535 || (int64_t)k->B * k->H > 65535 || q->B > 65535)
     return fail(FA_ERR_UNSUPPORTED, "B and H above the grid limits");
+  if ((k_mean == nullptr) != (q_delta == nullptr))
+    return fail(FA_ERR_INVALID_ARG, "K centering needs both k_mean and q_delta (or neither)");
+  if (q->H % k->H != 0) return fail(FA_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", q->H, k->H);
+  if (k_mean && (q->B != k->B)) return fail(FA_ERR_INVALID_ARG, "batch sizes differ");
+  if ((reinterpret_cast<uintptr_t>(k_mean) & 3u) || (reinterpret_cast<uintptr_t>(q_delta) & 3u))
+    return fail(FA_ERR_INVALID_ARG, "k_mean and q_delta must be 4-byte aligned");
+  const int chunks = fa::quant_mean_chunks(k->L);
+  if (k_mean) {
+    const size_t need = flexattn_quantize_qkv_ex_workspace_bytes(k->B, k->H, k->L);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+      return fail(FA_ERR_INVALID_ARG, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+    if (reinterpret_cast<uintptr_t>(workspace) & 15u) return fail(FA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  }
   fa::QuantArgs a{};
+  a.qk_block = qk_block;
+  a.k_mean = k_mean;
+  a.q_delta = q_delta;
+  a.mean_part = static_cast<double*>(workspace);
+  a.mean_chunks = chunks;
   auto src = [](const fa_tensor* t) {
     return fa::QuantTensor{static_cast<const unsigned short*>(t->data), t->B, t->H, t->L, t->stride_b, t->stride_h, t->stride_l};
   };
@@ -422,18 +453,31 @@ fa_status flexattn_quantize_qkv(const fa_tensor* q, const fa_tensor* k, const fa
   a.q = src(q);
   a.k = src(k);
   a.v = src(v);
-  a.q8 = dst(q8, cdiv(q->L, 128));
-  a.k8 = dst(k8, cdiv(k->L, 128));
+  a.q8 = dst(q8, cdiv(q->L, qk_block));
+  a.k8 = dst(k8, cdiv(k->L, qk_block));
   a.v8 = dst(v8, 128);
   hipError_t e = fa::launch_quantize(a, stream);
   if (e != hipSuccess) return fail(FA_ERR_DEVICE, "quantize launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 
+fa_status flexattn_quantize_qkv(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, fa_tensor* q8,
+                                fa_tensor* k8, fa_tensor* v8, hipStream_t stream) {
+  return quantize_impl(q, k, v, q8, k8, v8, 128, nullptr, nullptr, nullptr, 0, stream);
+}
+
+fa_status flexattn_quantize_qkv_ex(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, fa_tensor* q8,
+                                   fa_tensor* k8, fa_tensor* v8, int qk_block, float* k_mean, float* q_delta,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return quantize_impl(q, k, v, q8, k8, v8, qk_block, k_mean, q_delta, workspace, workspace_bytes, stream);
+}
+
 static fa_status fwd_quantized(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_block_mask* bm,
                                int mask_kind, int score_kind, const fa_params* p, fa_tensor* out, float* lse,
-                               hipStream_t stream) {
+                               int qk_block, const float* q_delta, hipStream_t stream) {
   fa_status st;
+  if (qk_block != 128 && qk_block != 32) return fail(FA_ERR_UNSUPPORTED, "qk_block must be 128 or 32 (got %d)", qk_block);
+  if (reinterpret_cast<uintptr_t>(q_delta) & 3u) return fail(FA_ERR_INVALID_ARG, "q_delta must be 4-byte aligned");
   if ((st = check_q_tensor(q, "q", FA_I8, 16)) != FA_OK) return st;
   if ((st = check_q_tensor(k, "k", FA_I8, 16)) != FA_OK) return st;
   if ((st = check_q_tensor(v, "v", FA_FP8_E4M3, 16)) != FA_OK) return st;
@@ -461,9 +505,12 @@ static fa_status fwd_quantized(const fa_tensor* q, const fa_tensor* k, const fa_
   a.o_sb = out->stride_b; a.o_sh = out->stride_h; a.o_sl = out->stride_l;
   a.q_scale = q->scale; a.k_scale = k->scale; a.v_scale = v->scale;
   a.B = q->B; a.Hq = q->H; a.Hkv = k->H; a.Lq = q->L; a.Lkv = k->L; a.group = q->H / k->H;
-  a.nqb = cdiv(q->L, 128); a.nkb = cdiv(k->L, 128);
+  a.nqb = cdiv(q->L, qk_block); a.nkb = cdiv(k->L, qk_block); a.nqw = cdiv(q->L, 128);
+  a.qk_block = qk_block;
+  a.q_delta = q_delta;
   const float sm = (p && p->sm_scale > 0.f) ? p->sm_scale : 1.0f / std::sqrt(128.0f);
   a.scale_log2 = sm * 1.4426950408889634f;
+  a.sm_scale = sm;
   a.total_wg = (int)total;
   hipError_t e = fa::launch_fwd_quant(a, stream);
   if (e != hipSuccess) return fail(FA_ERR_DEVICE, "forward launch failed: %s", hipGetErrorString(e));

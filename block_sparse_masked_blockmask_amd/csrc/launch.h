@@ -135,6 +135,11 @@ struct QuantOut {
 struct QuantArgs {
   QuantTensor q, k, v;
   QuantOut q8, k8, v8;
+  int qk_block;        // tokens per Q/K scale: 128 or 32
+  float* k_mean;       // K centering: float32 [B][Hkv][128] written (NULL: no centering)
+  float* q_delta;      // with centering: q . k_mean per query row, float32 [B][Hq][Lq] (may be NULL)
+  double* mean_part;   // with centering: per-chunk partial sums [B][Hkv][chunks][128]
+  int mean_chunks;
 };
 
 struct QuantFwdArgs {
@@ -147,13 +152,19 @@ struct QuantFwdArgs {
   const float* q_scale;  // [B][Hq][nqb]
   const float* k_scale;  // [B][Hkv][nkb]
   const float* v_scale;  // [B][Hkv][128]
-  int B, Hq, Hkv, Lq, Lkv, group, nqb, nkb;
+  int B, Hq, Hkv, Lq, Lkv, group;
+  int nqb, nkb;          // Q and K scale blocks per (batch, head): ceil(L / qk_block)
+  int nqw;               // 128-query work blocks per (batch, query head)
   float scale_log2;      // sm_scale * log2(e)
   int total_wg;
+  int qk_block;          // tokens per Q/K scale: 128 or 32
+  const float* q_delta;  // K centering: lse += sm_scale * q_delta[row] (NULL: none)
+  float sm_scale;
 };
 
 hipError_t launch_block_mask(const BlockMaskArgs& a, hipStream_t stream);
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
+int quant_mean_chunks(int L);  // partial sums of the K mean (1024 rows each)
 hipError_t launch_fwd_quant(const QuantFwdArgs& a, hipStream_t stream);
 // dtype 0 = f32, 1 = bf16; q_block 128 (f32, bf16) or 256 (bf16); kv_block in {64, 128};
 // score bits FA_SCORE_*.

@@ -29,6 +29,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
 constexpr float kE4M3Max = 448.0f;
+constexpr int kMeanRows = 1024;  // rows per partial sum of the K mean
 
 __device__ __forceinline__ float bf16_to_f32(unsigned short b) { return __uint_as_float((unsigned)b << 16); }
 
@@ -44,54 +45,142 @@ __device__ __forceinline__ float block_max_256(float x, float* s_red) {
 
 }  // namespace
 
-// One workgroup per (128-token block, head, batch) of Q or K: absmax scale and int8 codes.
+// One workgroup per (128-token block, head, batch) of Q or K: absmax scales and int8 codes, with
+// one scale per 128 tokens or per 32 tokens (qk_block). With K centering, K is quantized as
+// K - mean (one float32 subtraction per element, mean from quant_k_mean_*), and the Q pass also
+// writes q . mean of its kv head per row.
 __global__ __launch_bounds__(256) void quant_qk_kernel(QuantArgs a, int which) {
   const QuantTensor& src = which == 0 ? a.q : a.k;
   const QuantOut& dst = which == 0 ? a.q8 : a.k8;
   const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  __shared__ float s_red[4];
+  __shared__ float s_red[4][4];
   const int tid = threadIdx.x;
   const int r0 = blk * 128;
   const int rows = min(128, src.L - r0);
-  // Thread t handles rows t/16 + 16*i (i = 0..7) and channels 8*(t%16) .. +8.
+  const bool fine = a.qk_block == 32;
+  // Thread t handles rows t/16 + 16*i (i = 0..7; 32-token sub-block i/2) and channels
+  // 8*(t%16) .. +8.
   const unsigned short* base = src.data + b * src.sb + h * src.sh;
+  const int c0 = 8 * (tid % 16);
+  float mu[8];
+  const float* mean_kv = nullptr;
+  if (a.k_mean) {
+    const int hkv = which == 0 ? h / (a.q.H / a.k.H) : h;
+    mean_kv = a.k_mean + ((int64_t)b * a.k.H + hkv) * 128;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) mu[e] = (which == 1 && mean_kv) ? mean_kv[c0 + e] : 0.f;
   float x[8][8];
-  float amax = 0.f;
+  float am[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int r = tid / 16 + 16 * i;
     if (r < rows) {
-      const i32x4 raw = *(const i32x4*)(base + (int64_t)(r0 + r) * src.sl + 8 * (tid % 16));
+      const i32x4 raw = *(const i32x4*)(base + (int64_t)(r0 + r) * src.sl + c0);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        x[i][2 * e] = bf16_to_f32((unsigned short)(raw[e] & 0xffff));
-        x[i][2 * e + 1] = bf16_to_f32((unsigned short)((unsigned)raw[e] >> 16));
+        x[i][2 * e] = bf16_to_f32((unsigned short)(raw[e] & 0xffff)) - mu[2 * e];
+        x[i][2 * e + 1] = bf16_to_f32((unsigned short)((unsigned)raw[e] >> 16)) - mu[2 * e + 1];
       }
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[i][e] = 0.f;
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[i][e]));
+    for (int e = 0; e < 8; ++e) am[i >> 1] = fmaxf(am[i >> 1], fabsf(x[i][e]));
   }
-  amax = block_max_256(amax, s_red);
-  const float scale = amax / 127.0f;  // correctly rounded division
-  if (tid == 0) dst.scale[((int64_t)b * src.H + h) * dst.nblocks + blk] = scale;
+  // Block maxima of the four 32-row sub-blocks (and of the whole block).
+  const int wave = tid >> 6;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) am[j] = fmaxf(am[j], __shfl_xor(am[j], o, 64));
+    if ((tid & 63) == 0) s_red[wave][j] = am[j];
+  }
+  __syncthreads();
+  float scale[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    am[j] = fmaxf(fmaxf(s_red[0][j], s_red[1][j]), fmaxf(s_red[2][j], s_red[3][j]));
+  if (fine) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) scale[j] = am[j] / 127.0f;  // correctly rounded division
+    if (tid < 4 && 32 * tid < rows) dst.scale[((int64_t)b * src.H + h) * dst.nblocks + blk * 4 + tid] = scale[tid];
+  } else {
+    const float s1 = fmaxf(fmaxf(am[0], am[1]), fmaxf(am[2], am[3])) / 127.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) scale[j] = s1;
+    if (tid == 0) dst.scale[((int64_t)b * src.H + h) * dst.nblocks + blk] = s1;
+  }
   signed char* out = dst.data + b * dst.sb + h * dst.sh;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int r = tid / 16 + 16 * i;
     if (r >= rows) continue;
+    const float sc = scale[i >> 1];
     unsigned lo = 0, hi = 0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       int c = 0;
-      if (scale > 0.f) c = (int)fminf(fmaxf(rintf(x[i][e] / scale), -127.f), 127.f);
+      if (sc > 0.f) c = (int)fminf(fmaxf(rintf(x[i][e] / sc), -127.f), 127.f);
       const unsigned byte = (unsigned)(c & 0xff);
       if (e < 4) lo |= byte << (8 * e); else hi |= byte << (8 * (e - 4));
     }
-    *(i32x2*)(out + (int64_t)(r0 + r) * dst.sl + 8 * (tid % 16)) = i32x2{(int)lo, (int)hi};
+    *(i32x2*)(out + (int64_t)(r0 + r) * dst.sl + c0) = i32x2{(int)lo, (int)hi};
   }
+  if (which == 0 && a.q_delta && mean_kv) {
+    // q . mean per row: 8 channels per thread, then the 16 threads of the row (lanes l ^ 1..8).
+    float mk[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mk[e] = mean_kv[c0 + e];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = tid / 16 + 16 * i;
+      float d = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) d = fmaf(x[i][e], mk[e], d);
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) d += __shfl_xor(d, o, 64);
+      if ((tid & 15) == 0 && r < rows) a.q_delta[((int64_t)b * src.H + h) * src.L + r0 + r] = d;
+    }
+  }
+}
+
+// K centering, pass 1: per (chunk of rows, head, batch), fp64 sums of each channel over the
+// chunk (bf16 values, so the sums are exact while they fit 53 bits), written to mean_part.
+__global__ __launch_bounds__(256) void quant_k_mean_part_kernel(QuantArgs a, int rows_per_wg) {
+  const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x;
+  __shared__ double s_part[16][128];
+  const unsigned short* base = a.k.data + b * a.k.sb + h * a.k.sh;
+  const int r_begin = chunk * rows_per_wg, r_end = min(a.k.L, r_begin + rows_per_wg);
+  double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int r = r_begin + tid / 16; r < r_end; r += 16) {
+    const i32x4 raw = *(const i32x4*)(base + (int64_t)r * a.k.sl + 8 * (tid % 16));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[2 * e] += (double)bf16_to_f32((unsigned short)(raw[e] & 0xffff));
+      acc[2 * e + 1] += (double)bf16_to_f32((unsigned short)((unsigned)raw[e] >> 16));
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s_part[tid / 16][8 * (tid % 16) + e] = acc[e];
+  __syncthreads();
+  if (tid < 128) {
+    double sum = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sum += s_part[i][tid];
+    a.mean_part[(((int64_t)b * a.k.H + h) * a.mean_chunks + chunk) * 128 + tid] = sum;
+  }
+}
+
+// K centering, pass 2: mean = (sum of the partial sums, in chunk order) / L, rounded to float32.
+__global__ __launch_bounds__(128) void quant_k_mean_final_kernel(QuantArgs a) {
+  const int h = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
+  const double* part = a.mean_part + ((int64_t)b * a.k.H + h) * a.mean_chunks * 128;
+  double sum = 0;
+  for (int i = 0; i < a.mean_chunks; ++i) sum += part[(int64_t)i * 128 + c];
+  a.k_mean[((int64_t)b * a.k.H + h) * 128 + c] = a.k.L > 0 ? (float)(sum / (double)a.k.L) : 0.f;
 }
 
 __global__ __launch_bounds__(256) void quant_zero_kernel(float* p, int n) {
@@ -159,8 +248,16 @@ __global__ __launch_bounds__(256) void quant_v_encode_kernel(QuantArgs a, int ro
   }
 }
 
+int quant_mean_chunks(int L) { return (L + kMeanRows - 1) / kMeanRows; }
+
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream) {
   const int qb = (a.q.L + 127) / 128, kb = (a.k.L + 127) / 128;
+  if (a.k_mean && a.k.B > 0) {  // centering: the mean first (the Q and K passes read it)
+    if (a.mean_chunks > 0)
+      hipLaunchKernelGGL(quant_k_mean_part_kernel, dim3(a.mean_chunks, a.k.H, a.k.B), dim3(256), 0, stream, a,
+                         kMeanRows);
+    hipLaunchKernelGGL(quant_k_mean_final_kernel, dim3(a.k.H, a.k.B), dim3(128), 0, stream, a);
+  }
   if (a.q.B > 0 && qb > 0)
     hipLaunchKernelGGL(quant_qk_kernel, dim3(qb, a.q.H, a.q.B), dim3(256), 0, stream, a, 0);
   if (a.k.B > 0 && kb > 0)
@@ -243,7 +340,7 @@ __device__ __forceinline__ void qissue(const QuantFwdArgs& a, const QCtx& c, int
 
 template <int B>
 __device__ __forceinline__ void qcompute(const QuantFwdArgs& a, const QCtx& c, const i32x4 (&qreg)[4], QState& st,
-                                         int kv0, float kscale) {
+                                         int kv0, float2 kscale) {
   const unsigned char* sK = qkbuf<B>();
   const unsigned char* sV = qvbuf<B>();
   // S^T = K8 Q8^T: exact int32 dot products, 4 k-steps of 32 channels per 32-key sub-block.
@@ -258,7 +355,7 @@ __device__ __forceinline__ void qcompute(const QuantFwdArgs& a, const QCtx& c, c
       iacc[nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qreg[ks], iacc[nb], 0, 0, 0);
     }
   }
-  const float sc = c.qscale * kscale;
+  const float scs[2] = {c.qscale * kscale.x, c.qscale * kscale.y};  // per 32-key sub-block
   float t[2][16];
   float mx = -INFINITY;
 #pragma unroll
@@ -266,7 +363,7 @@ __device__ __forceinline__ void qcompute(const QuantFwdArgs& a, const QCtx& c, c
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int kv = kv0 + nb * 32 + (i >> 2) * 8 + c.hl * 4 + (i & 3);
-      t[nb][i] = kv < a.Lkv ? (float)iacc[nb][i] * sc : -INFINITY;
+      t[nb][i] = kv < a.Lkv ? (float)iacc[nb][i] * scs[nb] : -INFINITY;
       mx = fmaxf(mx, t[nb][i]);
     }
   }
@@ -318,8 +415,8 @@ __global__ __launch_bounds__(256, 2) void fwd_quant_kernel(QuantFwdArgs a) {
   int w = xcd_remap(blockIdx.x, a.total_wg);
   const int g = w % a.group;
   w /= a.group;
-  const int qb = a.nqb - 1 - (w % a.nqb);
-  w /= a.nqb;
+  const int qb = a.nqw - 1 - (w % a.nqw);
+  w /= a.nqw;
   const int hkv = w % a.Hkv, b = w / a.Hkv;
   const int hq = hkv * a.group + g;
 
@@ -335,15 +432,28 @@ __global__ __launch_bounds__(256, 2) void fwd_quant_kernel(QuantFwdArgs a) {
   c.kp = a.k + b * a.k_sb + hkv * a.k_sh;
   c.vp = a.v + b * a.v_sb + hkv * a.v_sh;
   c.ks = a.k_scale + ((int64_t)b * a.Hkv + hkv) * a.nkb;
-  c.qscale = a.q_scale[((int64_t)b * a.Hq + hq) * a.nqb + qb] * a.scale_log2;
+  // Q scale of this wave's 32 queries: one per 128-query block, or one per wave (32-token
+  // blocks); a wave past the end reads the last block's scale (its rows are not written).
+  const int qsb = a.qk_block == 32 ? min(qb * 4 + c.wave, a.nqb - 1) : qb;
+  c.qscale = a.q_scale[((int64_t)b * a.Hq + hq) * a.nqb + qsb] * a.scale_log2;
 
   const int nsteps = (a.Lkv + kQStep - 1) / kQStep;
-  // K scale of step s: a 64-key step lies inside one 128-key block. Each step's scale is loaded
-  // with its transfers, one step ahead, so that its wait is the step's own.
-  float ks_cur = 0.f;
+  // K scales of step s for its two 32-key sub-blocks: a 64-key step lies inside one 128-key
+  // block; with 32-token blocks each sub-block has its own (past the end: the last one, whose
+  // keys are masked). Each step's scales are loaded with its transfers, one step ahead, so
+  // that their wait is the step's own.
+  auto kscales = [&](int kv0) {
+    if (a.qk_block == 32) {
+      const int i0 = kv0 >> 5;
+      return make_float2(c.ks[i0], c.ks[min(i0 + 1, a.nkb - 1)]);
+    }
+    const float x = c.ks[kv0 >> 7];
+    return make_float2(x, x);
+  };
+  float2 ks_cur = make_float2(0.f, 0.f);
   if (nsteps > 0) {
     qissue<0>(a, c, 0);
-    ks_cur = c.ks[0];
+    ks_cur = kscales(0);
   }
 
   // Q8^T as the int8 B operand: lane holds Q8[qi][32*ks + 16*hl .. +16] for ks = 0..3.
@@ -362,10 +472,10 @@ __global__ __launch_bounds__(256, 2) void fwd_quant_kernel(QuantFwdArgs a) {
   for (int s = 0; s < nsteps; s += 2) {
     qwait_vmem();
     __syncthreads();
-    float ks_nxt = 0.f;
+    float2 ks_nxt = make_float2(0.f, 0.f);
     if (s + 1 < nsteps) {
       qissue<1>(a, c, (s + 1) * kQStep);
-      ks_nxt = c.ks[((s + 1) * kQStep) >> 7];
+      ks_nxt = kscales((s + 1) * kQStep);
     }
     qcompute<0>(a, c, qreg, st, s * kQStep, ks_cur);
     ks_cur = ks_nxt;
@@ -374,7 +484,7 @@ __global__ __launch_bounds__(256, 2) void fwd_quant_kernel(QuantFwdArgs a) {
       __syncthreads();
       if (s + 2 < nsteps) {
         qissue<0>(a, c, (s + 2) * kQStep);
-        ks_nxt = c.ks[((s + 2) * kQStep) >> 7];
+        ks_nxt = kscales((s + 2) * kQStep);
       }
       qcompute<1>(a, c, qreg, st, (s + 1) * kQStep, ks_cur);
       ks_cur = ks_nxt;
@@ -401,8 +511,12 @@ __global__ __launch_bounds__(256, 2) void fwd_quant_kernel(QuantFwdArgs a) {
         *(bf16x4*)(op + d) = o4;
       }
     }
-    if (a.lse && c.hl == 0)
-      a.lse[((int64_t)b * a.Hq + hq) * a.Lq + c.qi] = l_tot > 0.f ? (st.m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+    if (a.lse && c.hl == 0) {
+      // With centred keys the scores are shifted by -sm_scale (q . mean): add it back.
+      const int64_t row = ((int64_t)b * a.Hq + hq) * a.Lq + c.qi;
+      const float corr = a.q_delta ? a.sm_scale * a.q_delta[row] : 0.f;
+      a.lse[row] = l_tot > 0.f ? (st.m_run + __log2f(l_tot)) * kLn2 + corr : -INFINITY;
+    }
   }
 }
 

@@ -88,6 +88,14 @@ def lib() -> ctypes.CDLL:
                                            POINTER(FaTensor), c_void_p, c_int, c_void_p, c_size_t, c_void_p]
         L.flexattn_fwd_splitkv.restype = c_int
         L.flexattn_quantize_qkv.argtypes = [POINTER(FaTensor)] * 6 + [c_void_p]
+        L.flexattn_quantize_qkv_ex_workspace_bytes.argtypes = [c_int] * 3
+        L.flexattn_quantize_qkv_ex_workspace_bytes.restype = c_size_t
+        L.flexattn_quantize_qkv_ex.argtypes = [POINTER(FaTensor)] * 6 + [c_int, c_void_p, c_void_p, c_void_p,
+                                                                          c_size_t, c_void_p]
+        L.flexattn_quantize_qkv_ex.restype = c_int
+        L.flexattn_fwd_quant.argtypes = [POINTER(FaTensor)] * 3 + [c_int, c_void_p, POINTER(FaParams),
+                                                                   POINTER(FaTensor), c_void_p, c_void_p]
+        L.flexattn_fwd_quant.restype = c_int
         L.flexattn_block_mask_transpose.argtypes = [POINTER(FaBlockMask), POINTER(FaBlockMaskTransposed), c_void_p]
         L.flexattn_block_mask_transpose.restype = c_int
         L.flexattn_bwd_workspace_bytes.argtypes = [c_int] * 3
@@ -323,6 +331,60 @@ def flexattn_quantize_qkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, 
              tensor_desc(out["k8"], out["k_scale"]), tensor_desc(out["v8"], out["v_scale"])]
     _check(lib().flexattn_quantize_qkv(*[ctypes.byref(d) for d in descs], _stream(stream)))
     return out
+
+
+def flexattn_quantize_qkv_ex_workspace_bytes(B: int, Hkv: int, Lkv: int) -> int:
+    return lib().flexattn_quantize_qkv_ex_workspace_bytes(B, Hkv, Lkv)
+
+
+def flexattn_quantize_qkv_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, qk_block: int = 32,
+                             center_k: bool = True, out=None, workspace=None, stream=None):
+    """Quantize with the refinements (flexattn_quantize_qkv_ex): qk_block tokens per Q/K scale and,
+    with center_k, K centering. Returns the dict of flexattn_quantize_qkv plus "qk_block", and with
+    centering "k_mean" [B,Hkv,128] and "q_delta" [B,Hq,Lq] (float32)."""
+    def blocks(t):
+        return -(-t.shape[2] // qk_block)
+    if out is None:
+        out = {
+            "q8": torch.empty(q.shape, dtype=torch.int8, device=q.device),
+            "k8": torch.empty(k.shape, dtype=torch.int8, device=k.device),
+            "v8": torch.empty(v.shape, dtype=torch.uint8, device=v.device),
+            "q_scale": torch.empty((q.shape[0], q.shape[1], blocks(q)), dtype=torch.float32, device=q.device),
+            "k_scale": torch.empty((k.shape[0], k.shape[1], blocks(k)), dtype=torch.float32, device=k.device),
+            "v_scale": torch.empty((v.shape[0], v.shape[1], v.shape[3]), dtype=torch.float32, device=v.device),
+        }
+        if center_k:
+            out["k_mean"] = torch.empty((k.shape[0], k.shape[1], k.shape[3]), dtype=torch.float32, device=k.device)
+            out["q_delta"] = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    out["qk_block"] = qk_block
+    ws_bytes = flexattn_quantize_qkv_ex_workspace_bytes(k.shape[0], k.shape[1], k.shape[2]) if center_k else 0
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    descs = [tensor_desc(q), tensor_desc(k), tensor_desc(v), tensor_desc(out["q8"], out["q_scale"]),
+             tensor_desc(out["k8"], out["k_scale"]), tensor_desc(out["v8"], out["v_scale"])]
+    _check(lib().flexattn_quantize_qkv_ex(*[ctypes.byref(d) for d in descs], qk_block,
+                                          _ptr(out.get("k_mean") if center_k else None),
+                                          _ptr(out.get("q_delta") if center_k else None), _ptr(workspace),
+                                          workspace.numel() if workspace is not None else 0, _stream(stream)))
+    return out
+
+
+def flexattn_fwd_quant(qz: dict, *, sm_scale: float = 0.0, out: Optional[torch.Tensor] = None,
+                       lse: Optional[torch.Tensor] = None, return_lse: bool = True, stream=None):
+    """Quantized forward (flexattn_fwd_quant) on the dict returned by flexattn_quantize_qkv_ex
+    (or flexattn_quantize_qkv, qk_block 128); returns (out bf16, lse)."""
+    q8 = qz["q8"]
+    if out is None:
+        out = torch.empty(q8.shape, dtype=torch.bfloat16, device=q8.device)
+    if lse is None and return_lse:
+        lse = torch.empty(q8.shape[:3], dtype=torch.float32, device=q8.device)
+    tq, tk = tensor_desc(q8, qz["q_scale"]), tensor_desc(qz["k8"], qz["k_scale"])
+    tv, to = tensor_desc(qz["v8"], qz["v_scale"]), tensor_desc(out)
+    p = _params(sm_scale=sm_scale)
+    _check(lib().flexattn_fwd_quant(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), qz.get("qk_block", 128),
+                                    _ptr(qz.get("q_delta")), ctypes.byref(p), ctypes.byref(to), _ptr(lse),
+                                    _stream(stream)))
+    return out, lse
 
 
 class BlockMaskTransposed:

@@ -144,6 +144,33 @@ fa_status flexattn_block_mask_build_host(int mask_kind, const fa_params* p, int 
 fa_status flexattn_quantize_qkv(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v,
                                 fa_tensor* q8, fa_tensor* k8, fa_tensor* v8, hipStream_t stream);
 
+/* Refinements of the quantized form (FlashRT-Structures PR #1, "LTX-2.5 attention forms": the
+ * sage2 form scales Q/K per warp or per thread; the fused prep of its FP4 sibling centres the
+ * inputs and applies a delta correction). As flexattn_quantize_qkv, plus:
+ *   - qk_block: tokens per Q/K scale, 128 or 32 (32 = one wave of 32 queries, or one 32-key
+ *     sub-block of the forward); q8->scale / k8->scale are float32 [B][H][ceil(L / qk_block)];
+ *   - K centering when k_mean != NULL: mean[b][h][c] = (sum over tokens of K, exact while it fits
+ *     a double) / L, rounded to float32, written to k_mean (float32 [B][Hkv][128]); K is quantized
+ *     as K - mean (one float32 subtraction per element), which leaves softmax(q.k) unchanged and
+ *     moves each score row by -(q . mean) * sm_scale; q_delta (float32 [B][Hq][Lq], required with
+ *     k_mean) receives q_i . mean of the row's kv head, which flexattn_fwd_quant adds back to lse;
+ *   - workspace: flexattn_quantize_qkv_ex_workspace_bytes(B, Hkv, Lkv) bytes, 16-byte aligned,
+ *     used only with centering (fp64 partial sums of the mean; contents afterwards unspecified).
+ * qk_block other than 128 or 32 is FA_ERR_UNSUPPORTED. */
+size_t flexattn_quantize_qkv_ex_workspace_bytes(int B, int Hkv, int Lkv);
+fa_status flexattn_quantize_qkv_ex(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, fa_tensor* q8,
+                                   fa_tensor* k8, fa_tensor* v8, int qk_block, float* k_mean, float* q_delta,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Quantized forward for the output of flexattn_quantize_qkv_ex: q8, k8 FA_I8 and v8 FA_FP8_E4M3
+ * with their scale arrays at qk_block tokens per Q/K scale (128 or 32, as quantized), out FA_BF16.
+ * q_delta (may be NULL without centering) is the array flexattn_quantize_qkv_ex wrote: lse gets
+ * sm_scale * q_delta[row] added, so it is the lse of the uncentred scores. Unmasked attention
+ * without score_mod, as the quantized path of flexattn_fwd (which is this call with qk_block 128
+ * and q_delta NULL). */
+fa_status flexattn_fwd_quant(const fa_tensor* q8, const fa_tensor* k8, const fa_tensor* v8, int qk_block,
+                             const float* q_delta, const fa_params* p, fa_tensor* out, float* lse, hipStream_t stream);
+
 /* Forward pass. q [B][Hq][Lq][D], k and v [B][Hkv][Lkv][D], out [B][Hq][Lq][D],
  * lse [B][Hq][Lq] float32 contiguous (natural log; may be NULL). Supported envelope:
  *   - D = 128;
