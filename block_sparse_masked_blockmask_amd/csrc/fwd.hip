@@ -57,8 +57,23 @@ __device__ __forceinline__ WorkItem decode_work(const FwdArgs& a) {
   }
   const int qbr = w % a.nqb;
   w /= a.nqb;
-  it.hkv = w % a.Hkv;
-  it.b = w / a.Hkv;
+  // w now indexes the (batch, kv head) pairs in dispatch order. The contiguous ranges that the
+  // XCDs receive are taken over a permutation of the pairs: range c holds pairs c, c + 8,
+  // c + 16, ..., so every XCD mixes batches (whose document structures, and therefore work,
+  // differ) instead of taking one batch's heads. All query blocks of a pair stay in one range.
+  const int npair = a.B * a.Hkv;
+  const int q8 = npair / 8, r8 = npair % 8;
+  int c, k;
+  if (w < r8 * (q8 + 1)) {
+    c = w / (q8 + 1);
+    k = w % (q8 + 1);
+  } else {
+    c = r8 + (w - r8 * (q8 + 1)) / q8;
+    k = (w - r8 * (q8 + 1)) % q8;
+  }
+  const int pair = 8 * k + c;
+  it.hkv = pair % a.Hkv;
+  it.b = pair / a.Hkv;
   it.qb = a.nqb - 1 - qbr;
   it.hq = it.hkv * a.group + g;
   return it;
