@@ -356,6 +356,10 @@ def main():
     ap.add_argument("--refined", action="store_true",
                     help="with --quantized: 32-token Q/K scales and K centring (flexattn_quantize_qkv_ex + "
                          "flexattn_fwd_quant)")
+    ap.add_argument("--row-order", choices=("on", "off"), default=None,
+                    help="build the BlockMask's schedule array (query blocks by decreasing cost) inside the "
+                         "step and let the forward start costly rows first (default: on for causal document "
+                         "masks, off otherwise)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true", help="skip the achievable-peak measurements")
     ap.add_argument("--sweep", action="store_true",
@@ -420,7 +424,10 @@ def main():
     kd = torch.from_numpy(w.kv_doc).to(dev) if w.doc else None
     out = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
-    bm = fa.BlockMask(w.B if w.doc else 1, 1, w.Lq, w.Lkv, args.q_block, args.kv_block, dev)
+    if args.row_order is None:
+        args.row_order = "on" if (w.doc and w.causal) else "off"
+    bm = fa.BlockMask(w.B if w.doc else 1, 1, w.Lq, w.Lkv, args.q_block, args.kv_block, dev,
+                      row_order=args.row_order == "on")
     ws_bytes = fa.flexattn_block_mask_workspace_bytes(mk, w.B, w.Lq, w.Lkv, args.q_block, args.kv_block)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
@@ -519,7 +526,7 @@ def main():
                    "D": w.D, "mask": mk, "score": sk, "q_block": args.q_block, "kv_block": args.kv_block,
                    "step": ("quantize_qkv_ex (32-token Q/K scales, K centring) + fwd_quant (int8 QK, fp8 PV)"
                             if args.refined else "quantize_qkv + fwd (int8 QK, fp8 PV)") if args.quantized
-                   else "block_mask_build + fwd"},
+                   else "block_mask_build + fwd", "row_order": None if args.quantized else args.row_order},
         "hbm_gbs": abytes / (ms_per_step * 1e-3) / 1e9,
         "fwd_only": {"ms": fwd_avg_ms, "tflops": fwd_tflops, "gbs": fwd_gbs},
         "roofline": roof,

@@ -134,6 +134,7 @@ fa_status flexattn_block_mask_build(int mask_kind, const fa_params* p, int B, in
   a.kv_idx = out->kv_indices;
   a.full_num = out->full_kv_num_blocks;
   a.full_idx = out->full_kv_indices;
+  a.row_order = out->row_order;
   hipError_t e = fa::launch_block_mask(a, stream);
   if (e != hipSuccess) return fail(FA_ERR_DEVICE, "block mask launch failed: %s", hipGetErrorString(e));
   return ok();
@@ -201,6 +202,20 @@ fa_status flexattn_block_mask_build_host(int mask_kind, const fa_params* p, int 
       for (int j = np; j < nkvb; ++j) part[j] = 0;
       out->full_kv_num_blocks[row] = nf;
       out->kv_num_blocks[row] = np;
+    }
+    if (out->row_order) {
+      int32_t* order = out->row_order + (size_t)bm * nqb;
+      if (nqb > fa::kRowOrderMax) {
+        for (int qb = 0; qb < nqb; ++qb) order[qb] = qb;
+      } else {
+        std::vector<uint32_t> keys(nqb);
+        for (int qb = 0; qb < nqb; ++qb) {
+          const size_t row = (size_t)bm * nqb + qb;
+          keys[qb] = fa::row_order_key(out->full_kv_num_blocks[row], out->kv_num_blocks[row], qb);
+        }
+        std::sort(keys.begin(), keys.end());
+        for (int r = 0; r < nqb; ++r) order[r] = (int32_t)(keys[r] & fa::kRowOrderQbMask);
+      }
     }
   }
   return ok();
@@ -293,6 +308,7 @@ fa_status fwd_impl(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, c
     a.all_full = 0;
     a.Bm = bm->Bm;
     a.Hm = bm->Hm;
+    a.row_order = nsplit == 1 && bm->n_qb > 0 ? bm->row_order : nullptr;  // schedule only
     a.nqb = bm->n_qb;
     a.nkvb = bm->n_kvb;
     a.kv_num = bm->kv_num_blocks;

@@ -180,6 +180,41 @@ __global__ __launch_bounds__(256) void bm_classify(BlockMaskArgs a) {
   }
 }
 
+// Schedule of each mask row set (optional): its query blocks sorted by row_order_key, i.e. by
+// decreasing cost. One workgroup of 1024 threads per row set sorts the keys in LDS with a
+// bitonic network; in every stage each thread takes whole compare-exchange pairs (pair t joins
+// index i, t with a zero inserted at bit log2(j), and i + j), so no thread idles.
+constexpr int kOrderThreads = 1024;
+__global__ __launch_bounds__(kOrderThreads) void bm_order(BlockMaskArgs a) {
+  __shared__ unsigned s_key[kRowOrderMax];
+  const int64_t row0 = (int64_t)blockIdx.x * a.nqb;
+  int* order = a.row_order + row0;
+  const int tid = threadIdx.x;
+  if (a.nqb > kRowOrderMax) {
+    for (int i = tid; i < a.nqb; i += kOrderThreads) order[i] = i;
+    return;
+  }
+  int n = 2;
+  while (n < a.nqb) n <<= 1;
+  for (int i = tid; i < n; i += kOrderThreads)
+    s_key[i] = i < a.nqb ? row_order_key(a.full_num[row0 + i], a.kv_num[row0 + i], i) : 0xffffffffu;
+  __syncthreads();
+  for (int k = 2; k <= n; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int t = tid; t < n / 2; t += kOrderThreads) {
+        const int i = 2 * t - (t & (j - 1)), l = i + j;
+        const unsigned x = s_key[i], y = s_key[l];
+        if ((x > y) == ((i & k) == 0)) {
+          s_key[i] = y;
+          s_key[l] = x;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = tid; i < a.nqb; i += kOrderThreads) order[i] = (int)(s_key[i] & kRowOrderQbMask);
+}
+
 hipError_t launch_block_mask(const BlockMaskArgs& a, hipStream_t stream) {
   if (a.nqb == 0) return hipSuccess;
   if (a.flags & FA_MASK_DOC) {
@@ -189,6 +224,9 @@ hipError_t launch_block_mask(const BlockMaskArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(bm_classify, dim3(a.nqb, a.Bm), dim3(256), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.row_order == nullptr) return e;
+  hipLaunchKernelGGL(bm_order, dim3(a.Bm), dim3(kOrderThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -46,6 +46,27 @@ __device__ __forceinline__ WorkItem decode_work(const FwdArgs& a) {
   // under causal masks) to the first, then kv head, batch.
   WorkItem it;
   it.split = 0;
+  if constexpr (MODE == 0) {
+    if (a.row_order != nullptr) {
+      // Scheduled order: rank r of the row order outermost, so the costliest query blocks of
+      // every (batch, head) start first, and consecutive workgroups (which the hardware deals
+      // round-robin to the 8 XCDs) take the (batch, kv head) pairs fastest, then the query heads
+      // of a kv head: with 8 | B * Hkv, XCD x always serves pairs x, x + 8, ..., so each K/V
+      // head is read through one L2.
+      const int w0 = blockIdx.x;
+      const int npair = a.B * a.Hkv;
+      const int per_rank = npair * a.group;
+      const int idx = w0 % per_rank, r = w0 / per_rank;
+      const int pair = idx % npair, g = idx / npair;
+      it.hkv = pair % a.Hkv;
+      it.b = pair / a.Hkv;
+      it.hq = it.hkv * a.group + g;
+      const int bm = a.Bm == 1 ? 0 : it.b;
+      const int hm = a.Hm == 1 ? 0 : it.hq;
+      it.qb = min(max(a.row_order[((int64_t)bm * a.Hm + hm) * a.nqb + r], 0), a.nqb - 1);
+      return it;
+    }
+  }
   if constexpr (MODE > 0) {
     it.split = w % a.nsplit;
     w /= a.nsplit;

@@ -17,6 +17,7 @@ struct BlockMaskArgs {
   int* kv_idx;
   int* full_num;
   int* full_idx;
+  int* row_order;  // [Bm][nqb] query blocks by decreasing cost, or null
 };
 
 struct FwdArgs {
@@ -36,6 +37,7 @@ struct FwdArgs {
   const int* full_num;
   const int* full_idx;
   int Bm, Hm, nqb, nkvb, all_full;
+  const int* row_order;  // [Bm][Hm][nqb] schedule (query blocks by decreasing cost), or null
   // mask_mod / score_mod
   int flags, window, prefix_len;
   const int* q_doc;

@@ -67,4 +67,18 @@ __host__ __device__ inline int classify_closed(int flags, int window, int prefix
   return 3;
 }
 
+// Schedule key of a BlockMask row (the optional row_order of fa_block_mask): rows are sorted by
+// increasing key, i.e. by decreasing estimated cost 4 * full + 5 * partial live tiles (a partial
+// tile also evaluates the mask on every score), ties by increasing query block. The cost is
+// saturated to 19 bits and the query block takes the low 13 bits, so keys are unique and an
+// ascending sort of them is the whole order.
+constexpr int kRowOrderMax = 8192;  // query blocks per row set that are sorted (else identity)
+constexpr unsigned kRowOrderQbMask = kRowOrderMax - 1;
+__host__ __device__ inline unsigned row_order_key(int nfull, int npart, int qb) {
+  const unsigned cmax = (1u << 19) - 1;
+  unsigned cost = 4u * (unsigned)nfull + 5u * (unsigned)npart;
+  cost = cost < cmax ? cost : cmax;
+  return ((cmax - cost) << 13) | (unsigned)qb;
+}
+
 }  // namespace fa

@@ -38,7 +38,8 @@ class FaBlockMask(ctypes.Structure):
     _fields_ = [("Bm", c_int32), ("Hm", c_int32), ("q_len", c_int32), ("kv_len", c_int32),
                 ("q_block", c_int32), ("kv_block", c_int32), ("n_qb", c_int32), ("n_kvb", c_int32),
                 ("kv_num_blocks", c_void_p), ("kv_indices", c_void_p),
-                ("full_kv_num_blocks", c_void_p), ("full_kv_indices", c_void_p)]
+                ("full_kv_num_blocks", c_void_p), ("full_kv_indices", c_void_p),
+                ("row_order", c_void_p)]
 
 
 class FaBlockMaskTransposed(ctypes.Structure):
@@ -167,9 +168,12 @@ def flexattn_block_mask_workspace_bytes(mask_kind, B, q_len, kv_len, q_block, kv
 
 
 class BlockMask:
-    """Device BlockMask: the four int32 arrays plus their dimensions (caller-owned memory)."""
+    """Device BlockMask: the four int32 arrays plus their dimensions (caller-owned memory).
 
-    def __init__(self, Bm, Hm, q_len, kv_len, q_block, kv_block, device):
+    row_order=True also allocates the optional schedule array (query blocks of each row set by
+    decreasing cost), which the builders fill and the forward uses to start costly rows first."""
+
+    def __init__(self, Bm, Hm, q_len, kv_len, q_block, kv_block, device, row_order: bool = False):
         self.Bm, self.Hm, self.q_len, self.kv_len = Bm, Hm, q_len, kv_len
         self.q_block, self.kv_block = q_block, kv_block
         self.n_qb = -(-q_len // q_block)
@@ -179,19 +183,22 @@ class BlockMask:
         self.full_kv_num_blocks = torch.empty((Bm, Hm, self.n_qb), **z)
         self.kv_indices = torch.empty((Bm, Hm, self.n_qb, self.n_kvb), **z)
         self.full_kv_indices = torch.empty((Bm, Hm, self.n_qb, self.n_kvb), **z)
+        self.row_order = torch.empty((Bm, Hm, self.n_qb), **z) if row_order else None
 
     def to(self, device) -> "BlockMask":
         """A copy of this BlockMask with its arrays on `device`."""
         bm = BlockMask.__new__(BlockMask)
         bm.__dict__.update(self.__dict__)
-        for k in ("kv_num_blocks", "full_kv_num_blocks", "kv_indices", "full_kv_indices"):
-            setattr(bm, k, getattr(self, k).to(device))
+        for k in ("kv_num_blocks", "full_kv_num_blocks", "kv_indices", "full_kv_indices", "row_order"):
+            if getattr(self, k) is not None:
+                setattr(bm, k, getattr(self, k).to(device))
         return bm
 
     def as_struct(self) -> FaBlockMask:
         return FaBlockMask(self.Bm, self.Hm, self.q_len, self.kv_len, self.q_block, self.kv_block,
                            self.n_qb, self.n_kvb, self.kv_num_blocks.data_ptr(), self.kv_indices.data_ptr(),
-                           self.full_kv_num_blocks.data_ptr(), self.full_kv_indices.data_ptr())
+                           self.full_kv_num_blocks.data_ptr(), self.full_kv_indices.data_ptr(),
+                           _ptr(getattr(self, "row_order", None)))
 
 
 def _params(window=0, prefix_len=0, softcap=0.0, alibi_slopes=None, q_doc=None, kv_doc=None, sm_scale=0.0):
@@ -202,13 +209,15 @@ def _params(window=0, prefix_len=0, softcap=0.0, alibi_slopes=None, q_doc=None, 
 def flexattn_block_mask_build(mask_kind: int, B: int, q_len: int, kv_len: int, q_block: int = 128,
                               kv_block: int = 128, *, q_doc=None, kv_doc=None, window: int = 0,
                               prefix_len: int = 0, device=None, stream=None, out: Optional[BlockMask] = None,
-                              workspace: Optional[torch.Tensor] = None) -> BlockMask:
-    """Build a BlockMask on the device (create_block_mask of the FlexAttention guide)."""
+                              workspace: Optional[torch.Tensor] = None, row_order: bool = False) -> BlockMask:
+    """Build a BlockMask on the device (create_block_mask of the FlexAttention guide).
+    row_order=True (with out=None) also computes the schedule array; with `out`, the schedule is
+    computed when out.row_order is allocated."""
     if device is None:
         device = q_doc.device if q_doc is not None else torch.device("cuda", torch.cuda.current_device())
     if out is None:
         Bm = B if (mask_kind & FA_MASK_DOC) else 1
-        out = BlockMask(Bm, 1, q_len, kv_len, q_block, kv_block, device)
+        out = BlockMask(Bm, 1, q_len, kv_len, q_block, kv_block, device, row_order=row_order)
     ws_bytes = flexattn_block_mask_workspace_bytes(mask_kind, B, q_len, kv_len, q_block, kv_block)
     if ws_bytes and workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=device)
@@ -236,8 +245,9 @@ def block_mask_all_partial(Bm: int, Hm: int, q_len: int, kv_len: int, q_block: i
 
 def flexattn_block_mask_build_host(mask_kind: int, B: int, q_len: int, kv_len: int, q_block: int = 128,
                                    kv_block: int = 128, *, q_doc=None, kv_doc=None, window: int = 0,
-                                   prefix_len: int = 0) -> BlockMask:
-    """Build a BlockMask on the host: document ids and the returned arrays are CPU memory."""
+                                   prefix_len: int = 0, row_order: bool = False) -> BlockMask:
+    """Build a BlockMask on the host: document ids and the returned arrays are CPU memory.
+    row_order=True also computes the schedule array (as the device builder does)."""
     def host_ids(x):
         if x is None:
             return None
@@ -247,7 +257,7 @@ def flexattn_block_mask_build_host(mask_kind: int, B: int, q_len: int, kv_len: i
         return t
     qd, kd = host_ids(q_doc), host_ids(kv_doc)
     Bm = B if (mask_kind & FA_MASK_DOC) else 1
-    out = BlockMask(Bm, 1, q_len, kv_len, q_block, kv_block, torch.device("cpu"))
+    out = BlockMask(Bm, 1, q_len, kv_len, q_block, kv_block, torch.device("cpu"), row_order=row_order)
     p = _params(window=window, prefix_len=prefix_len, q_doc=qd, kv_doc=kd)
     s = out.as_struct()
     _check(lib().flexattn_block_mask_build_host(mask_kind, ctypes.byref(p), B, q_len, kv_len, ctypes.byref(s)))

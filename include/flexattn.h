@@ -90,13 +90,23 @@ typedef struct {
  *   kv_indices, full_kv_indices       : [Bm][Hm][n_qb][n_kvb]
  * n_qb = ceil(q_len / q_block), n_kvb = ceil(kv_len / kv_block). Bm is 1 (one row set for
  * every batch) or B; Hm is 1 or Hq. A tile is classified over its in-range pairs only, so a
- * ragged edge tile whose in-range pairs are all allowed is full. */
+ * ragged edge tile whose in-range pairs are all allowed is full.
+ *
+ * row_order (optional, int32 [Bm][Hm][n_qb], NULL when unused) is a schedule, not part of the
+ * mask: for each mask row set, the query blocks sorted by decreasing estimated cost
+ * 4 * full + 5 * partial live tiles, ties by increasing query block (identity order when
+ * n_qb > 8192). The builders fill it when the pointer is set. When it is set, the forward
+ * starts the costliest query blocks first, so that long rows (long documents under causal
+ * masks) do not finish last; results are identical with or without it. A caller-written
+ * row_order must be a permutation of 0..n_qb-1 in each row set (entries are clamped into
+ * range; a repeated entry leaves some output rows unwritten). */
 typedef struct {
   int32_t Bm, Hm, q_len, kv_len, q_block, kv_block, n_qb, n_kvb;
   int32_t* kv_num_blocks;
   int32_t* kv_indices;
   int32_t* full_kv_num_blocks;
   int32_t* full_kv_indices;
+  int32_t* row_order;
 } fa_block_mask;
 
 /* Bytes of ONE index array ([Bm][Hm][n_qb][n_kvb] int32) and of ONE count array

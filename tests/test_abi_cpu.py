@@ -36,7 +36,7 @@ def test_struct_sizes_match_abi():
     # fa_tensor: ptr, 5 x int32, 3 x int64, ptr with natural alignment.
     assert ctypes.sizeof(FaTensor) == 8 + 4 * 5 + 4 + 8 * 3 + 8
     assert ctypes.sizeof(FaParams) == 4 * 4 + 8 * 3
-    assert ctypes.sizeof(FaBlockMask) == 4 * 8 + 8 * 4
+    assert ctypes.sizeof(FaBlockMask) == 4 * 8 + 8 * 5  # four index arrays and the optional row_order
 
 
 def test_sizes():

@@ -85,3 +85,59 @@ def test_host_builder_empty_and_errors():
     with pytest.raises(fa.FlexAttnError) as e:
         fa.flexattn_block_mask_build_host(fa.FA_MASK_DOC, 1, 64, 64, 64, 64)
     assert e.value.status == fa.FA_ERR_INVALID_ARG
+
+
+def _expected_order(full_num, part_num):
+    """The documented schedule: per row set, query blocks by decreasing 4 * full + 5 * partial
+    live tiles, ties by increasing query block."""
+    Bm, Hm, nqb = full_num.shape
+    out = np.empty_like(full_num)
+    for bm in range(Bm):
+        for hm in range(Hm):
+            cost = 4 * full_num[bm, hm].astype(np.int64) + 5 * part_num[bm, hm].astype(np.int64)
+            out[bm, hm] = sorted(range(nqb), key=lambda qb: (-cost[qb], qb))
+    return out
+
+
+@pytest.mark.parametrize("si", range(len(SPECS)))
+@pytest.mark.parametrize("shape", [(2, 333, 333, 128, 128), (1, 700, 517, 64, 128), (2, 2000, 2000, 128, 64),
+                                   (1, 1, 1, 128, 64)])
+def test_host_row_order(si, shape):
+    """The optional schedule array: a permutation of the query blocks of each row set in the
+    documented cost order; the mask arrays are the same with and without it."""
+    B, Lq, Lkv, BQ, BK = shape
+    spec = dict(SPECS[si])
+    if spec.get("doc"):
+        w = random_case(3000 + si, B=B, Lq=Lq, Lkv=Lkv, D=8, doc=True, n_docs=7)
+        spec["q_doc"], spec["kv_doc"] = w.q_doc, w.kv_doc
+    fa = _fa()
+    qd = kd = None
+    if spec.get("doc"):
+        qd = np.ascontiguousarray(spec["q_doc"], np.int32)
+        kd = np.ascontiguousarray(spec["kv_doc"], np.int32)
+    kw = dict(q_doc=qd, kv_doc=kd, window=spec.get("window") or 0, prefix_len=spec.get("prefix_len") or 0)
+    bm = fa.flexattn_block_mask_build_host(_mask_kind(fa, spec), B, Lq, Lkv, BQ, BK, row_order=True, **kw)
+    plain = fa.flexattn_block_mask_build_host(_mask_kind(fa, spec), B, Lq, Lkv, BQ, BK, **kw)
+    for k in KEYS:
+        assert np.array_equal(getattr(bm, k).numpy(), getattr(plain, k).numpy()), k
+    order = bm.row_order.numpy()
+    want = _expected_order(bm.full_kv_num_blocks.numpy(), bm.kv_num_blocks.numpy())
+    assert np.array_equal(order, want)
+    for row in order.reshape(-1, order.shape[-1]):
+        assert np.array_equal(np.sort(row), np.arange(order.shape[-1]))
+
+
+def test_host_row_order_identity_beyond_limit():
+    """More than 8192 query blocks in a row set: the schedule is the identity order."""
+    fa = _fa()
+    nqb = 8193
+    bm = fa.flexattn_block_mask_build_host(fa.FA_MASK_CAUSAL, 1, nqb * 64, 64, 64, 64, row_order=True)
+    assert np.array_equal(bm.row_order.numpy()[0, 0], np.arange(nqb))
+    small = fa.flexattn_block_mask_build_host(fa.FA_MASK_CAUSAL, 1, 8192 * 64, 8192 * 64 // 4, 64, 64,
+                                              row_order=True)
+    want = _expected_order(small.full_kv_num_blocks.numpy(), small.kv_num_blocks.numpy())
+    assert np.array_equal(small.row_order.numpy(), want)
+    # Row 2047 (2047 full + 1 partial) costs most; rows past the keys tie (2048 full each) and
+    # follow in increasing order; row 0 (one partial tile) is last.
+    o = want[0, 0]
+    assert list(o[:4]) == [2047, 2048, 2049, 2050] and o[-1] == 0
