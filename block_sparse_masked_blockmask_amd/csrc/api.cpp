@@ -348,6 +348,15 @@ fa_status fwd_impl(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, c
   a.scale_log2 = sm * 1.4426950408889634f;
   a.softcap = (score_kind & FA_SCORE_SOFTCAP) ? p->softcap : 0.f;
   a.inv_softcap = (score_kind & FA_SCORE_SOFTCAP) ? 1.0f / p->softcap : 0.f;
+  {
+    // score_mod constants folded into the log2 domain (see score_log2 in fwd.hip).
+    const double l2e = 1.4426950408889634;
+    const double cap = (score_kind & FA_SCORE_SOFTCAP) ? (double)p->softcap : 1.0;
+    a.sc_in = (float)((double)sm * 2.0 * l2e / cap);
+    a.sc_out = (float)(cap * l2e);
+    a.sc_out2 = (float)(-2.0 * cap * l2e);
+    a.slope_mul = (float)((score_kind & FA_SCORE_SOFTCAP) ? 2.0 * l2e / cap : l2e);
+  }
   a.slopes = (score_kind & FA_SCORE_ALIBI) ? p->alibi_slopes : nullptr;
   a.total_wg = (int)total;
   a.nsplit = nsplit;

@@ -128,16 +128,23 @@ __device__ __forceinline__ TileList tile_list(const FwdArgs& a, const WorkItem& 
 }
 
 // Score transform for one accumulator value of query qi and key kv; returns the log2-domain
-// logit. SCORE bits: FA_SCORE_ALIBI, FA_SCORE_SOFTCAP (ALiBi first, then the soft-cap).
+// logit. SCORE bits: FA_SCORE_ALIBI, FA_SCORE_SOFTCAP (ALiBi first, then the soft-cap). The
+// constants are folded on the host: with s = acc * sm_scale - slope * |qi - kv| and
+// tanh(x) = 1 - 2 / (1 + e^(2x)), the soft-capped logit in log2 units is
+//   C log2(e) - 2 C log2(e) / (1 + 2^(s * 2 log2(e) / C)),
+// one multiply (or FMA with ALiBi), exp2, add, reciprocal and FMA per score; `slope` arrives
+// pre-multiplied by log2(e) (ALiBi alone) or 2 log2(e) / C (with the soft-cap). exp2 saturates
+// to inf or 0 for large |s / C|, giving exactly +-C log2(e).
 template <int SCORE>
 __device__ __forceinline__ float score_log2(const FwdArgs& a, float acc, int qi, int kv, float slope) {
   if constexpr (SCORE == 0) {
     return acc * a.scale_log2;
+  } else if constexpr (SCORE == FA_SCORE_ALIBI) {
+    return fmaf(-slope, fabsf((float)(qi - kv)), acc * a.scale_log2);
   } else {
-    float s = acc * a.sm_scale;
-    if constexpr (SCORE & FA_SCORE_ALIBI) s = fmaf(-slope, fabsf((float)(qi - kv)), s);
-    if constexpr (SCORE & FA_SCORE_SOFTCAP) s = a.softcap * fast_tanh(s * a.inv_softcap);
-    return s * kLog2e;
+    float u = acc * a.sc_in;
+    if constexpr (SCORE & FA_SCORE_ALIBI) u = fmaf(-slope, fabsf((float)(qi - kv)), u);
+    return fmaf(a.sc_out2, __builtin_amdgcn_rcpf(1.0f + fast_exp2(u)), a.sc_out);
   }
 }
 
@@ -682,7 +689,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(FwdArgs
   };
   int chunk_base = 0;
   int chunk = chunk_init;
-  c.slope = (SCORE & FA_SCORE_ALIBI) ? a.slopes[c.hq] : 0.f;
+  c.slope = (SCORE & FA_SCORE_ALIBI) ? a.slopes[c.hq] * a.slope_mul : 0.f;
 
   // Step s -> StepInfo (steps past the end re-read row 0 and are not computed).
   auto info = [&](int s) {
@@ -830,7 +837,7 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_kernel(FwdArgs a) {
 #pragma unroll
   for (int ks = 0; ks < 64; ++ks) qreg[ks] = q_in ? qp[(int64_t)qi * a.q_sl + 2 * ks + hl] : 0.f;
   const int qdoc = ((a.flags & FA_MASK_DOC) && q_in) ? a.q_doc[(int64_t)it.b * a.Lq + qi] : 0;
-  const float slope = (SCORE & FA_SCORE_ALIBI) ? a.slopes[it.hq] : 0.f;
+  const float slope = (SCORE & FA_SCORE_ALIBI) ? a.slopes[it.hq] * a.slope_mul : 0.f;
   const MaskSpec ms{a.flags, a.window, a.prefix_len};
 
   f32x16 oacc[4];

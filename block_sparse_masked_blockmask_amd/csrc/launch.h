@@ -43,6 +43,9 @@ struct FwdArgs {
   const int* q_doc;
   const int* kv_doc;
   float sm_scale, scale_log2, softcap, inv_softcap;
+  // Folded score_mod constants (log2 domain): soft-cap input and output factors, and the
+  // factor applied to each ALiBi slope.
+  float sc_in, sc_out, sc_out2, slope_mul;
   const float* slopes;
   int total_wg;
   // Split-KV: nsplit > 1 cuts each work item's tile list into nsplit contiguous ranges, one
