@@ -457,7 +457,14 @@ __device__ __forceinline__ void compute_step(const FwdArgs& a, const Ctx& c, con
       if (!(L & (1u << nb))) continue;
       const int kbase = kv0 + nb * 32 + c.hl * 4;   // key of element i is kbase + (i/4)*8 + i%4
       // The allowed keys [lo, hi) relative to kbase: element offsets are the constants 0..27.
-      const int rlo = lo - kbase, rhi = hi - kbase;
+      // They become one bitmask per lane (bit off set: offset off allowed); each score then
+      // takes its bit with a signed bitfield extract (0 or all ones) and keeps its bits or
+      // those of -inf with a bitfield insert: two vector operations and no lane masks.
+      unsigned abits = 0;
+      if constexpr (MASKED) {
+        const int l0 = min(max(lo - kbase, 0), 31), h0 = min(max(hi - kbase, 0), 31);
+        abits = ((1u << h0) - 1u) & ~((1u << l0) - 1u);
+      }
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         i32x4 kd4 = i32x4{};
@@ -468,9 +475,9 @@ __device__ __forceinline__ void compute_step(const FwdArgs& a, const Ctx& c, con
           const int off = g * 8 + e;
           float x = SCORE == 0 ? sacc[nb][i] : score_log2<SCORE>(a, sacc[nb][i], qi, kbase + off, c.slope);
           if constexpr (MASKED) {
-            bool keep = (rlo <= off) & (rhi > off);
-            if constexpr (DOC) keep = keep & (kd4[e] == c.qdoc);
-            x = keep ? x : -INFINITY;
+            const int keep = (int)(abits << (31 - off)) >> 31;
+            x = __int_as_float((__float_as_int(x) & keep) | (int)(0xff800000u & ~(unsigned)keep));
+            if constexpr (DOC) x = kd4[e] == c.qdoc ? x : -INFINITY;
           }
           sacc[nb][i] = x;
           mx = fmaxf(mx, x);
