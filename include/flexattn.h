@@ -15,6 +15,9 @@
  *   - Every buffer is owned by the caller. The library allocates no device memory and never
  *     synchronises the host; all work is enqueued on the caller's `stream` and is asynchronous.
  *     Kernel faults surface at the caller's next synchronisation.
+ *   - The device entry points enqueue kernels only (no memset, copy or allocation), so a
+ *     sequence of calls can be captured in a HIP graph and replayed; a replay reads the
+ *     buffers' current contents.
  *   - Device pointers must point into memory of the current HIP device.
  *   - On any status other than FA_OK nothing has been enqueued and no output has been written;
  *     flexattn_last_error() gives the reason. There is no silent fallback path.
