@@ -421,7 +421,8 @@ def main():
 
     q, k, v = dev_tensor(w.q), dev_tensor(w.k), dev_tensor(w.v)
     qd = torch.from_numpy(w.q_doc).to(dev) if w.doc else None
-    kd = torch.from_numpy(w.kv_doc).to(dev) if w.doc else None
+    # Self-attention packing passes one id array for both sides (the ABI allows the alias).
+    kd = (qd if w.kv_doc is w.q_doc else torch.from_numpy(w.kv_doc).to(dev)) if w.doc else None
     out = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     if args.row_order is None:

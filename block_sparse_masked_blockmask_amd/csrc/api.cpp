@@ -135,6 +135,7 @@ fa_status flexattn_block_mask_build(int mask_kind, const fa_params* p, int B, in
   a.full_num = out->full_kv_num_blocks;
   a.full_idx = out->full_kv_indices;
   a.row_order = out->row_order;
+  a.self_ids = (mask_kind & FA_MASK_DOC) && p->q_doc == p->kv_doc && q_len == kv_len;
   hipError_t e = fa::launch_block_mask(a, stream);
   if (e != hipSuccess) return fail(FA_ERR_DEVICE, "block mask launch failed: %s", hipGetErrorString(e));
   return ok();
@@ -149,6 +150,7 @@ fa_status flexattn_block_mask_build_host(int mask_kind, const fa_params* p, int 
   const int prefix_len = (mask_kind & FA_MASK_PREFIX_LM) ? p->prefix_len : 0;
   const bool doc = (mask_kind & FA_MASK_DOC) != 0;
   const int BQ = out->q_block, BK = out->kv_block, nqb = out->n_qb, nkvb = out->n_kvb;
+  const bool self_ids = doc && p->q_doc == p->kv_doc && q_len == kv_len;
   // Per-block document-id summaries of one batch: [min, max, dense] (see tile_class.h).
   auto summarise = [](const int32_t* ids, int L, int blk, int n, std::vector<int>& sum) {
     sum.assign((size_t)3 * n, 0);
@@ -185,7 +187,8 @@ fa_status flexattn_block_mask_build_host(int mask_kind, const fa_params* p, int 
         const int k0 = kb * BK, k1 = std::min(kv_len, k0 + BK);
         int cls = fa::classify_closed(flags, window, prefix_len, q0, q1, k0, k1, doc ? qs[3 * qb] : 0,
                                       doc ? qs[3 * qb + 1] : 0, doc ? qs[3 * qb + 2] : 0, doc ? ks[3 * kb] : 0,
-                                      doc ? ks[3 * kb + 1] : 0, doc ? ks[3 * kb + 2] : 0);
+                                      doc ? ks[3 * kb + 1] : 0, doc ? ks[3 * kb + 2] : 0,
+                                      self_ids);
         if (cls == 3) {  // every in-range pair, until one is allowed
           cls = 0;
           for (int i = q0; i < q1 && !cls; ++i)

@@ -114,7 +114,8 @@ __global__ __launch_bounds__(256) void bm_classify(BlockMaskArgs a) {
         const int k0 = kb * a.BK, k1 = min(a.Lkv, k0 + a.BK);
         int4 ks = make_int4(0, 0, 0, 0);
         if (doc) ks = *(const int4*)(a.kvsum + 4 * (b * a.nkvb + kb));
-        cls = classify_closed(a.flags, a.window, a.prefix_len, q0, q1, k0, k1, qs.x, qs.y, qs.z, ks.x, ks.y, ks.z);
+        cls = classify_closed(a.flags, a.window, a.prefix_len, q0, q1, k0, k1, qs.x, qs.y, qs.z, ks.x, ks.y, ks.z,
+                              a.self_ids != 0);
         if (cls == 3) s_amb[atomicAdd(&s_namb, 1)] = loc;
       }
       s_cls[loc] = (unsigned char)cls;

@@ -18,6 +18,7 @@ struct BlockMaskArgs {
   int* full_num;
   int* full_idx;
   int* row_order;  // [Bm][nqb] query blocks by decreasing cost, or null
+  int self_ids;    // DOC with q_doc and kv_doc the same array (and Lq == Lkv)
 };
 
 struct FwdArgs {

@@ -28,9 +28,11 @@ __host__ __device__ inline bool mask_pair_flags(int flags, int window, int prefi
 // Class of the tile [q0, q1) x [k0, k1) (non-empty ranges): 0 empty, 1 partial, 2 full, 3 not
 // settled by closed forms. Under DOC, [qmin, qmax] and [kmin, kmax] are the id ranges of the
 // query and key blocks, and qdense / kdense flag blocks whose consecutive ids differ by 0 or 1
-// (every id of the range then occurs in the block).
+// (every id of the range then occurs in the block). self_ids: the query and key document ids
+// are one array (same memory, q_len == kv_len), so position i has the same id on both sides.
 __host__ __device__ inline int classify_closed(int flags, int window, int prefix_len, int q0, int q1, int k0, int k1,
-                                               int qmin, int qmax, int qdense, int kmin, int kmax, int kdense) {
+                                               int qmin, int qmax, int qdense, int kmin, int kmax, int kdense,
+                                               bool self_ids = false) {
   const int dmin = q0 - (k1 - 1), dmax = (q1 - 1) - k0;  // range of q - kv over the box
   bool all = true, none = false;
   if (flags & FA_MASK_CAUSAL) {
@@ -52,6 +54,10 @@ __host__ __device__ inline int classify_closed(int flags, int window, int prefix
   }
   if (all) return 2;
   if (none) return 0;
+  // A box that holds a diagonal pair (i, i) has an allowed pair: causal, window (> 0) and
+  // prefix-LM all allow j = i, and with self_ids so does the document predicate.
+  const bool diag = (q0 > k0 ? q0 : k0) < (q1 < k1 ? q1 : k1);
+  if (diag && (self_ids || !(flags & FA_MASK_DOC))) return 1;
   if (!(flags & FA_MASK_DOC)) {
     // Causal and window together allow exactly the pairs with q - kv in [0, window): the box's
     // q - kv values form one integer interval, and each predicate alone was not all-false, so

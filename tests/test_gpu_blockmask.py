@@ -31,7 +31,10 @@ def build_gpu(spec, B, Lq, Lkv, BQ, BK):
     qd = kd = None
     if spec.get("doc"):
         qd = torch.from_numpy(np.ascontiguousarray(spec["q_doc"], np.int32)).to(dev)
-        kd = torch.from_numpy(np.ascontiguousarray(spec["kv_doc"], np.int32)).to(dev)
+        # One id array for both sides (the builder's self-attention closed form) when the
+        # spec's ids are one array; separate copies otherwise.
+        kd = qd if spec["kv_doc"] is spec["q_doc"] else \
+            torch.from_numpy(np.ascontiguousarray(spec["kv_doc"], np.int32)).to(dev)
     bm = fa.flexattn_block_mask_build(_mask_kind(fa, spec), B, Lq, Lkv, BQ, BK, q_doc=qd, kv_doc=kd,
                                       window=spec.get("window") or 0, prefix_len=spec.get("prefix_len") or 0,
                                       device=dev)
@@ -119,3 +122,45 @@ def test_workload_block_masks(name, bq, bk):
         # Every row of the packed groups has only partial tiles (no group is tile-aligned).
         tot_p = int(got["kv_num_blocks"].sum())
         print(f"{name}: partial tiles {tot_p}, full {int(got['full_kv_num_blocks'].sum())}")
+
+
+@pytest.mark.parametrize("mask", ["doc_sorted", "doc_unsorted", "causal_window"])
+def test_multi_pass_rows(mask):
+    """Rows longer than one classification pass (9,375 kv blocks of 64 keys, three passes):
+    the device lists equal the oracle on sampled rows and the host builder on every row."""
+    import block_sparse_masked_blockmask_amd as fa
+    rng = np.random.default_rng(77)
+    B, Lq, Lkv, BQ, BK = 1, 700, 600_000, 128, 64
+    if mask == "causal_window":
+        spec = {"causal": True, "window": 250_000}
+        Lq = Lkv = 600_000
+    else:
+        qd = np.sort(rng.integers(0, 40, size=(B, Lq))).astype(np.int32)
+        kd = np.sort(rng.integers(0, 40, size=(B, Lkv))).astype(np.int32)
+        if mask == "doc_unsorted":
+            # ids repeat far apart: tiles the closed forms cannot settle in every pass
+            kd = (np.arange(Lkv, dtype=np.int64) // 5000 % 40).astype(np.int32)[None, :]
+        spec = {"doc": True, "q_doc": qd, "kv_doc": kd}
+    got = build_gpu(spec, B, Lq, Lkv, BQ, BK)
+    nqb = -(-Lq // BQ)
+    rows = [(0, qb) for qb in sorted({0, nqb // 2, nqb - 1})]
+    ref = ref_bm.block_mask(spec, B, Lq, Lkv, BQ, BK, rows=rows)
+    assert_same(got, ref, rows)
+    host = fa.flexattn_block_mask_build_host(
+        _mask_kind(fa, spec), B, Lq, Lkv, BQ, BK,
+        q_doc=None if mask == "causal_window" else np.ascontiguousarray(spec["q_doc"]),
+        kv_doc=None if mask == "causal_window" else np.ascontiguousarray(spec["kv_doc"]),
+        window=spec.get("window") or 0)
+    for k in KEYS:
+        assert np.array_equal(got[k], getattr(host, k).numpy()), k
+
+
+@pytest.mark.parametrize("alias", [True, False])
+def test_aliased_ids_equal_copies(alias):
+    """The same ids passed as one array (self-attention closed form for diagonal tiles) or as
+    two copies give identical lists, equal to the oracle."""
+    w = random_case(2100, B=2, Lq=3000, Lkv=3000, D=8, doc=True, n_docs=25)
+    spec = {"doc": True, "causal": True, "q_doc": w.q_doc, "kv_doc": w.q_doc if alias else w.q_doc.copy()}
+    got = build_gpu(spec, 2, 3000, 3000, 128, 64)
+    ref = ref_bm.block_mask(spec, 2, 3000, 3000, 128, 64)
+    assert_same(got, ref)
