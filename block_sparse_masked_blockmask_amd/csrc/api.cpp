@@ -77,6 +77,10 @@ fa_status check_build(int mask_kind, const fa_params* p, int B, int q_len, int k
     return fail(FA_ERR_INVALID_ARG, "BlockMask count arrays are NULL");
   if (out->n_qb > 0 && out->n_kvb > 0 && (!out->kv_indices || !out->full_kv_indices))
     return fail(FA_ERR_INVALID_ARG, "BlockMask index arrays are NULL");
+  for (const void* ptr : {(const void*)out->kv_num_blocks, (const void*)out->full_kv_num_blocks,
+                          (const void*)out->kv_indices, (const void*)out->full_kv_indices,
+                          (const void*)out->row_order})
+    if (reinterpret_cast<uintptr_t>(ptr) & 3u) return fail(FA_ERR_INVALID_ARG, "BlockMask arrays must be 4-byte aligned");
   return FA_OK;
 }
 

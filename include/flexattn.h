@@ -128,6 +128,7 @@ size_t flexattn_block_mask_workspace_bytes(int mask_kind, int B, int q_len, int 
  * kv_len, q_block, kv_block, n_qb, n_kvb) and its four array pointers; Bm must be B when DOC is
  * set (1 or B otherwise), Hm must be 1 (no flag depends on the head). q_block is 64, 128 or
  * 256 and kv_block is 64 or 128. Reads p->q_doc / p->kv_doc (DOC), p->window (WINDOW), p->prefix_len (PREFIX_LM).
+ * The arrays of `out` must be 4-byte aligned (FA_ERR_INVALID_ARG otherwise).
  * `workspace` must hold flexattn_block_mask_workspace_bytes(...) bytes, 16-byte aligned (may be
  * NULL if 0).
  * Classification is exact: the lists equal exhaustive evaluation of every in-range pair. */
