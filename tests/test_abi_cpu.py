@@ -143,6 +143,13 @@ def test_block_mask_build_validation():
     assert st == fa.FA_ERR_INVALID_ARG and "window" in fa.flexattn_last_error()
     st = lib.flexattn_block_mask_build(64, ctypes.byref(p), 1, 100, 100, ctypes.byref(bm), None, 0, None)
     assert st == fa.FA_ERR_INVALID_ARG and "unknown" in fa.flexattn_last_error()
+    # Misaligned arrays (including the optional schedule) are refused before anything runs.
+    bm5 = FaBlockMask(1, 1, 100, 100, 128, 128, 1, 1, 64, 66, 64, 64)
+    st = lib.flexattn_block_mask_build(fa.FA_MASK_CAUSAL, ctypes.byref(p), 1, 100, 100, ctypes.byref(bm5), None, 0, None)
+    assert st == fa.FA_ERR_INVALID_ARG and "aligned" in fa.flexattn_last_error()
+    bm6 = FaBlockMask(1, 1, 100, 100, 128, 128, 1, 1, 64, 64, 64, 64, 70)
+    st = lib.flexattn_block_mask_build_host(fa.FA_MASK_CAUSAL, ctypes.byref(p), 1, 100, 100, ctypes.byref(bm6))
+    assert st == fa.FA_ERR_INVALID_ARG and "aligned" in fa.flexattn_last_error()
 
 
 def test_product_path_does_not_import_oracle():
