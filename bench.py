@@ -347,7 +347,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warm-up steps (default: at least 3 steps and 200 ms of completed steps, "
+                         "so that the GPU clocks have settled; the count run is reported)")
     ap.add_argument("--workload", default=None, help=f"workload name (default {DEFAULT_WORKLOAD}; with --backward: all bf16 workloads)")
     ap.add_argument("--kv-block", type=int, default=None, help="BlockMask kv block (default 64 bf16, 128 f32)")
     ap.add_argument("--q-block", type=int, default=None, help="BlockMask q block (default 128)")
@@ -473,8 +475,18 @@ def main():
 
     if args.quantized:
         step = step_quant  # noqa: F811
-    for _ in range(args.warmup):
-        step()
+    if args.warmup is None:
+        # The clocks take tens of milliseconds of sustained load to settle (forward durations
+        # drift by up to 12% over the first 30 ms), so warm up for a fixed time, not a count.
+        n, t_w = 0, time.perf_counter()
+        while n < 3 or (time.perf_counter() - t_w < 0.2 and n < 20000):
+            step()
+            torch.cuda.synchronize()
+            n += 1
+        args.warmup = n
+    else:
+        for _ in range(args.warmup):
+            step()
     torch.cuda.synchronize()
     # Timed region: exactly K steps, bracketed by device synchronisation. It records no events:
     # on this platform each timing event costs about 10 us of the step (measured), so the
