@@ -882,15 +882,10 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_kernel(FwdArgs a) {
     }
     __syncthreads();
 
-    // Sub-blocks and P.V products whose keys all lie past the last key are skipped (scalar
-    // branches): their scores are masked to -inf and their V rows are zero, so they would add
-    // nothing. A short key range (a few dozen keys, as in small grouped inputs) then costs
-    // only the products it needs.
     f32x16 sacc[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       sacc[nb] = f32x16{};
-      if (kv0 + nb * 32 >= a.Lkv) continue;
       const float* krow = sK + (nb * 32 + lq) * P + hl;
 #pragma unroll
       for (int ks = 0; ks < 64; ++ks)
@@ -938,8 +933,6 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_kernel(FwdArgs a) {
       for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          // Keys of this product: r for the lower lane half, r + 4 for the upper one.
-          if (kv0 + nb * 32 + (i >> 2) * 8 + (i & 3) >= a.Lkv) continue;
           const int r = nb * 32 + (i >> 2) * 8 + hl * 4 + (i & 3);
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(sV[r * P + db * 32 + lq], sacc[nb][i], oacc[db], 0, 0, 0);
         }
