@@ -38,9 +38,11 @@ struct WorkItem {
 
 // MODE 0: plain forward; 1: split-KV; 2: split-KV with the query heads of one kv head packed
 // into one workgroup (rows = (head, query) pairs, all queries of all heads of the group).
+// wg: the work item's index in dispatch order (the workgroup id, or the workgroup id / 4 for the
+// split-key fp32 kernel, whose four workgroups share one work item).
 template <int MODE = 0>
-__device__ __forceinline__ WorkItem decode_work(const FwdArgs& a) {
-  int w = xcd_remap(blockIdx.x, a.total_wg);
+__device__ __forceinline__ WorkItem decode_work(const FwdArgs& a, int wg) {
+  int w = xcd_remap(wg, a.total_wg);
   // Order: splits of one work item fastest (they read the same Q rows), then query heads of
   // one kv head (they read the same K/V tiles), then query blocks from the last (most tiles
   // under causal masks) to the first, then kv head, batch.
@@ -53,7 +55,7 @@ __device__ __forceinline__ WorkItem decode_work(const FwdArgs& a) {
       // round-robin to the 8 XCDs) take the (batch, kv head) pairs fastest, then the query heads
       // of a kv head: with 8 | B * Hkv, XCD x always serves pairs x, x + 8, ..., so each K/V
       // head is read through one L2.
-      const int w0 = blockIdx.x;
+      const int w0 = wg;
       const int npair = a.B * a.Hkv;
       const int per_rank = npair * a.group;
       const int idx = w0 % per_rank, r = w0 / per_rank;
@@ -593,7 +595,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(FwdArgs
   constexpr int BQ = 32 * WAVES;
   constexpr int OPS = step_ops<WAVES>();
 
-  const WorkItem it = decode_work<MODE>(a);
+  const WorkItem it = decode_work<MODE>(a, blockIdx.x);
   Ctx c;
   c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar registers
   c.lane = threadIdx.x & 63;
@@ -830,7 +832,7 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_kernel(FwdArgs a) {
   __shared__ float sV[BK * P];
   __shared__ int sDoc[BK];
 
-  const WorkItem it = decode_work(a);
+  const WorkItem it = decode_work(a, blockIdx.x);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int hl = lane >> 5, lq = lane & 31;
   const int qi = it.qb * kBQ + wave * 32 + lq;
@@ -963,6 +965,182 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_kernel(FwdArgs a) {
   }
 }
 
+// fp32 work items below which the split-key kernel runs (one work item per CU or fewer).
+constexpr int kF32SplitBelow = 256;
+
+// ---------------------------------------------------------------------------------------------
+// f32 split-key kernel, for inputs too small to fill the GPU (a few hundred queries per head, as
+// in the grouped-variate layer): the four workgroups of one work item take 32 queries each, and
+// the four waves of a workgroup share those queries and take one 32-key sub-block each of every
+// tile (sub-blocks nb = wave, wave + 4, ...). Each wave keeps its own online-softmax state; at the
+// end the partial results are merged in a fixed wave order through LDS:
+//   m = max_w m_w,  f_w = 2^(m_w - m),  l = sum_w f_w l_w,  O = (sum_w f_w O_w) / l.
+// A wave reads each K/V sub-block once, so a tile costs each wave a quarter of the products.
+// ---------------------------------------------------------------------------------------------
+template <int BK, int SCORE>
+__global__ __launch_bounds__(256, 1) void fwd_f32_split_kernel(FwdArgs a) {
+  constexpr int NB = BK / 32;
+  constexpr int P = 130;
+  __shared__ float sK[BK * P];
+  __shared__ float sV[BK * P];
+  __shared__ int sDoc[BK];
+  __shared__ float s_m[4][32];
+  __shared__ float s_l[4][32];
+
+  const WorkItem it = decode_work(a, blockIdx.x >> 2);
+  const int sub = blockIdx.x & 3;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int hl = lane >> 5, lq = lane & 31;
+  const int q0 = it.qb * kBQ + sub * 32;
+  if (q0 >= a.Lq) return;  // the whole workgroup: no query in this 32-row slice
+  const int qi = q0 + lq;
+  const bool q_in = qi < a.Lq;
+
+  const float* qp = (const float*)a.q + it.b * a.q_sb + it.hq * a.q_sh;
+  const float* kp = (const float*)a.k + it.b * a.k_sb + it.hkv * a.k_sh;
+  const float* vp = (const float*)a.v + it.b * a.v_sb + it.hkv * a.v_sh;
+
+  float qreg[64];
+#pragma unroll
+  for (int ks = 0; ks < 64; ++ks) qreg[ks] = q_in ? qp[(int64_t)qi * a.q_sl + 2 * ks + hl] : 0.f;
+  const int qdoc = ((a.flags & FA_MASK_DOC) && q_in) ? a.q_doc[(int64_t)it.b * a.Lq + qi] : 0;
+  const float slope = (SCORE & FA_SCORE_ALIBI) ? a.slopes[it.hq] * a.slope_mul : 0.f;
+  const MaskSpec ms{a.flags, a.window, a.prefix_len};
+
+  f32x16 oacc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) oacc[db] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const TileList tl = tile_list(a, it);
+  const int ntiles = tl.nfull + tl.npart;
+  for (int t = 0; t < ntiles; ++t) {
+    const bool partial = t >= tl.nfull;
+    const int kb = partial ? tl.part[t - tl.nfull] : (a.all_full ? t : tl.full[t]);
+    if (kb < 0 || kb >= a.nkvb) continue;
+    const int kv0 = kb * BK;
+    const bool masked = partial || (kv0 + BK > a.Lkv);
+
+    __syncthreads();
+    for (int id = tid; id < BK * 32; id += 256) {  // float4 chunks
+      const int r = id >> 5, c4 = id & 31;
+      const int kv = kv0 + r;
+      f32x4 kx = f32x4{}, vx = f32x4{};
+      if (kv < a.Lkv) {
+        kx = *(const f32x4*)(kp + (int64_t)kv * a.k_sl + c4 * 4);
+        vx = *(const f32x4*)(vp + (int64_t)kv * a.v_sl + c4 * 4);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sK[r * P + c4 * 4 + e] = kx[e];
+        sV[r * P + c4 * 4 + e] = vx[e];
+      }
+    }
+    if (masked && (a.flags & FA_MASK_DOC) && tid < BK) {
+      const int kv = kv0 + tid;
+      sDoc[tid] = kv < a.Lkv ? a.kv_doc[(int64_t)it.b * a.Lkv + kv] : 0;
+    }
+    __syncthreads();
+
+    for (int nb = wave; nb < NB; nb += 4) {
+      if (kv0 + nb * 32 >= a.Lkv) break;  // this and later sub-blocks lie past the last key
+      f32x16 sacc = f32x16{};
+      const float* krow = sK + (nb * 32 + lq) * P + hl;
+#pragma unroll
+      for (int ks = 0; ks < 64; ++ks) sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(krow[2 * ks], qreg[ks], sacc, 0, 0, 0);
+
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int kv = kv0 + nb * 32 + (i >> 2) * 8 + hl * 4 + (i & 3);
+        float x = score_log2<SCORE>(a, sacc[i], qi, kv, slope);
+        if (masked) {
+          const int kvdoc = (a.flags & FA_MASK_DOC) ? sDoc[kv - kv0] : 0;
+          const bool keep = kv < a.Lkv && mask_pair(ms, qi, kv, qdoc, kvdoc);
+          x = keep ? x : -INFINITY;
+        }
+        sacc[i] = x;
+        mx = fmaxf(mx, x);
+      }
+      mx = half_swap_max(mx);
+      const float m_new = fmaxf(m_run, mx);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run - m_use);
+      m_run = m_new;
+      float rs = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = fast_exp2(sacc[i] - m_use);
+        rs += p;
+        sacc[i] = p;
+      }
+      l_run = l_run * alpha + rs;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        oacc[db] *= alpha;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = nb * 32 + (i >> 2) * 8 + hl * 4 + (i & 3);
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(sV[r * P + db * 32 + lq], sacc[i], oacc[db], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // Merge of the four waves' partial results, in wave order (deterministic).
+  const float l_w = half_swap_sum(l_run);
+  __syncthreads();  // every wave is done with sK / sV
+  if (hl == 0) {
+    s_m[wave][lq] = m_run;
+    s_l[wave][lq] = l_w;
+  }
+  __syncthreads();
+  float m = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) m = fmaxf(m, s_m[w][lq]);
+  float l = 0.f, f_self = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float mw = s_m[w][lq];
+    const float f = mw == -INFINITY ? 0.f : fast_exp2(mw - m);
+    l += f * s_l[w][lq];
+    if (w == wave) f_self = f;
+  }
+  // Partial outputs accumulate in sK viewed as [32 queries][128 channels], one wave after the
+  // other; the element layout is the accumulator's, identical in every wave.
+  float* sO = sK;
+  for (int w = 0; w < 4; ++w) {
+    if (w == wave) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int ch = db * 32 + (i >> 2) * 8 + hl * 4 + (i & 3);
+          const float v = oacc[db][i] * f_self;
+          sO[lq * 128 + ch] = w == 0 ? v : sO[lq * 128 + ch] + v;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  const float inv = l > 0.f ? 1.0f / l : 0.f;
+  // Store: wave w writes channels [32 w, 32 w + 32) of the 32 rows (lane = row, two halves of 16).
+  if (q_in) {
+    float* op = (float*)a.o + it.b * a.o_sb + it.hq * a.o_sh + (int64_t)qi * a.o_sl;
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) {
+      const int ch = wave * 32 + hl * 16 + c4 * 4;
+      f32x4 o4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o4[e] = sO[lq * 128 + ch + e] * inv;
+      *(f32x4*)(op + ch) = o4;
+    }
+    if (a.lse && wave == 0 && hl == 0) {
+      a.lse[((int64_t)it.b * a.Hq + it.hq) * a.Lq + qi] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------------------------
 template <int BK, int SCORE>
 static hipError_t launch_t(const FwdArgs& a, int dtype, int q_block, hipStream_t stream) {
@@ -975,6 +1153,9 @@ static hipError_t launch_t(const FwdArgs& a, int dtype, int q_block, hipStream_t
       hipLaunchKernelGGL((fwd_bf16_kernel<BK, SCORE, 4, 2, 1>), dim3(a.total_wg), dim3(256), 0, stream, a);
     else
       hipLaunchKernelGGL((fwd_bf16_kernel<BK, SCORE, 4, 2, 0>), dim3(a.total_wg), dim3(256), 0, stream, a);
+  } else if (a.total_wg < kF32SplitBelow) {
+    // Too few work items to fill the GPU: four workgroups per item, keys split over the waves.
+    hipLaunchKernelGGL((fwd_f32_split_kernel<BK, SCORE>), dim3(4 * a.total_wg), dim3(256), 0, stream, a);
   } else {
     hipLaunchKernelGGL((fwd_f32_kernel<BK, SCORE>), dim3(a.total_wg), dim3(256), 0, stream, a);
   }

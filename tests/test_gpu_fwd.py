@@ -243,3 +243,20 @@ def test_workloads_full_size(name, blocks):
     vmin = vf.min(axis=2).min()
     vmax = vf.max(axis=2).max()
     assert np.isfinite(o).all() and o.min() >= vmin - 1e-2 and o.max() <= vmax + 1e-2
+
+
+@pytest.mark.parametrize("kw", [dict(doc=True, causal=True), dict(causal=True, window=300, alibi=True)])
+def test_f32_both_launch_shapes(kw):
+    """fp32 inputs with fewer than 256 work items run the split-key kernel (four workgroups per
+    work item, keys split over the waves); larger ones the one-workgroup kernel. Both against
+    the oracle: B=2, 16 heads, 1100 queries is 288 work items; one head of it is 9."""
+    w = random_case(610, dtype="f32", B=2, Hq=16, Hkv=8, Lq=1100, Lkv=1100, **kw)
+    qf, kf, vf = w.qkv_f32()
+    o_ref, l_ref = ref_attn.attention(qf, kf, vf, spec_of(w))
+    out, lse, _ = run_gpu(w)
+    check_close(out.float().cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref, "f32", "f32 288 work items")
+    w1 = random_case(611, dtype="f32", B=1, Hq=1, Hkv=1, Lq=1100, Lkv=1100, **kw)
+    qf, kf, vf = w1.qkv_f32()
+    o_ref, l_ref = ref_attn.attention(qf, kf, vf, spec_of(w1))
+    out, lse, _ = run_gpu(w1)
+    check_close(out.float().cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref, "f32", "f32 9 work items")
