@@ -29,6 +29,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
 constexpr float kE4M3Max = 448.0f;
+constexpr float kLog2E4M3Max = 8.807354922057604f;  // log2(448)
 constexpr int kMeanRows = 1024;  // rows per partial sum of the K mean
 
 __device__ __forceinline__ float bf16_to_f32(unsigned short b) { return __uint_as_float((unsigned)b << 16); }
@@ -338,7 +339,11 @@ __device__ __forceinline__ void qissue(const QuantFwdArgs& a, const QCtx& c, int
   }
 }
 
-template <int B>
+// RAGGED: the step reaches past the last key (only the last step can), so scores of keys past
+// it are set to -inf; other steps skip that test. The numerators are produced already scaled by
+// 448: exp2(t - (m - log2 448)) = 448 P, which is the E4M3 code's input; the running sum l_run
+// therefore holds 448 times the row sum (the epilogue divides by it as it stands).
+template <int B, bool RAGGED>
 __device__ __forceinline__ void qcompute(const QuantFwdArgs& a, const QCtx& c, const i32x4 (&qreg)[4], QState& st,
                                          int kv0, float2 kscale) {
   const unsigned char* sK = qkbuf<B>();
@@ -363,7 +368,7 @@ __device__ __forceinline__ void qcompute(const QuantFwdArgs& a, const QCtx& c, c
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int kv = kv0 + nb * 32 + (i >> 2) * 8 + c.hl * 4 + (i & 3);
-      t[nb][i] = kv < a.Lkv ? (float)iacc[nb][i] * scs[nb] : -INFINITY;
+      t[nb][i] = (!RAGGED || kv < a.Lkv) ? (float)iacc[nb][i] * scs[nb] : -INFINITY;
       mx = fmaxf(mx, t[nb][i]);
     }
   }
@@ -379,16 +384,19 @@ __device__ __forceinline__ void qcompute(const QuantFwdArgs& a, const QCtx& c, c
     st.m_run = m_new;
   }
   // P^T as the fp8 B operand: byte j of the 32 holds key position (j / 16, element j % 16).
+  // 448 P <= 448 up to the exponential's last-place error, far below 464, where the conversion
+  // stops rounding to 448.
+  const float m448 = st.m_run - kLog2E4M3Max;
   i32x8 pb;
 #pragma unroll
   for (int w = 0; w < 8; ++w) {
     const int nb = w >> 2, i0 = (w & 3) * 4;
-    const float p0 = fast_exp2(t[nb][i0] - st.m_run), p1 = fast_exp2(t[nb][i0 + 1] - st.m_run);
-    const float p2 = fast_exp2(t[nb][i0 + 2] - st.m_run), p3 = fast_exp2(t[nb][i0 + 3] - st.m_run);
+    const float p0 = fast_exp2(t[nb][i0] - m448), p1 = fast_exp2(t[nb][i0 + 1] - m448);
+    const float p2 = fast_exp2(t[nb][i0 + 2] - m448), p3 = fast_exp2(t[nb][i0 + 3] - m448);
     st.l_run += (p0 + p1) + (p2 + p3);
     int word = 0;
-    word = __builtin_amdgcn_cvt_pk_fp8_f32(p0 * kE4M3Max, p1 * kE4M3Max, word, false);
-    word = __builtin_amdgcn_cvt_pk_fp8_f32(p2 * kE4M3Max, p3 * kE4M3Max, word, true);
+    word = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, word, false);
+    word = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, word, true);
     pb[w] = word;
   }
   // O^T += V8^T P8^T. Transposed reads: in each 16-lane group, source lane s points at physical
@@ -477,7 +485,8 @@ __global__ __launch_bounds__(256, 2) void fwd_quant_kernel(QuantFwdArgs a) {
       qissue<1>(a, c, (s + 1) * kQStep);
       ks_nxt = kscales((s + 1) * kQStep);
     }
-    qcompute<0>(a, c, qreg, st, s * kQStep, ks_cur);
+    if ((s + 1) * kQStep <= a.Lkv) qcompute<0, false>(a, c, qreg, st, s * kQStep, ks_cur);
+    else qcompute<0, true>(a, c, qreg, st, s * kQStep, ks_cur);
     ks_cur = ks_nxt;
     if (s + 1 < nsteps) {
       qwait_vmem();
@@ -486,14 +495,16 @@ __global__ __launch_bounds__(256, 2) void fwd_quant_kernel(QuantFwdArgs a) {
         qissue<0>(a, c, (s + 2) * kQStep);
         ks_nxt = kscales((s + 2) * kQStep);
       }
-      qcompute<1>(a, c, qreg, st, (s + 1) * kQStep, ks_cur);
+      if ((s + 2) * kQStep <= a.Lkv) qcompute<1, false>(a, c, qreg, st, (s + 1) * kQStep, ks_cur);
+      else qcompute<1, true>(a, c, qreg, st, (s + 1) * kQStep, ks_cur);
       ks_cur = ks_nxt;
     }
   }
 
-  // Epilogue: out = O * scale_V[channel] / (448 l), bf16; lse in natural log.
+  // Epilogue: out = O * scale_V[channel] / (448 l), bf16 (l_tot is already 448 l); lse in
+  // natural log.
   const float l_tot = half_swap_sum(st.l_run);
-  const float inv = l_tot > 0.f ? 1.0f / (kE4M3Max * l_tot) : 0.f;
+  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
   if (c.q_in) {
     const float* vs = a.v_scale + ((int64_t)b * a.Hkv + hkv) * 128;
     __bf16* op = a.o + b * a.o_sb + hq * a.o_sh + (int64_t)c.qi * a.o_sl;
@@ -515,7 +526,7 @@ __global__ __launch_bounds__(256, 2) void fwd_quant_kernel(QuantFwdArgs a) {
       // With centred keys the scores are shifted by -sm_scale (q . mean): add it back.
       const int64_t row = ((int64_t)b * a.Hq + hq) * a.Lq + c.qi;
       const float corr = a.q_delta ? a.sm_scale * a.q_delta[row] : 0.f;
-      a.lse[row] = l_tot > 0.f ? (st.m_run + __log2f(l_tot)) * kLn2 + corr : -INFINITY;
+      a.lse[row] = l_tot > 0.f ? (st.m_run - kLog2E4M3Max + __log2f(l_tot)) * kLn2 + corr : -INFINITY;
     }
   }
 }
