@@ -50,6 +50,22 @@ namespace fa {
 namespace {
 
 constexpr int kRows = 64;                  // rows per LDS tile and per step
+
+// Position w of the (batch, kv head) pairs in dispatch order -> pair index: the XCDs receive
+// contiguous ranges of work, and range c holds pairs c, c + 8, c + 16, ..., so every XCD mixes
+// batches (whose document structures, and work, differ).
+__device__ __forceinline__ int permute_pair(int w, int npair) {
+  const int q8 = npair / 8, r8 = npair % 8;
+  int c, k;
+  if (w < r8 * (q8 + 1)) {
+    c = w / (q8 + 1);
+    k = w % (q8 + 1);
+  } else {
+    c = r8 + (w - r8 * (q8 + 1)) / q8;
+    k = (w - r8 * (q8 + 1)) % q8;
+  }
+  return 8 * k + c;
+}
 constexpr int kTileBytes = kRows * 256;    // [64][128] bf16
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 
@@ -308,11 +324,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   __shared__ float sRed[4];
   constexpr int kOps = 9;  // transfers per wave and step
 
-  int w = blockIdx.x;
-  const int qb = w % a.nqb;
+  // Order: query heads of one kv head fastest (they read the same K/V tiles), then query blocks
+  // from last to first (the longest rows under causal masks first), then (batch, kv head)
+  // pairs; each XCD takes one contiguous range, the pairs permuted so that ranges mix batches.
+  int w = xcd_remap(blockIdx.x, (int)((int64_t)a.B * a.Hq * a.nqb));
+  const int g = w % a.group;
+  w /= a.group;
+  const int qb = a.nqb - 1 - (w % a.nqb);
   w /= a.nqb;
-  const int hq = w % a.Hq, b = w / a.Hq;
-  const int hkv = hq / a.group;
+  const int pair = permute_pair(w, a.B * (a.Hq / a.group));
+  const int hkv = pair % (a.Hq / a.group), b = pair / (a.Hq / a.group);
+  const int hq = hkv * a.group + g;
   const Lane c = make_lane();
   const int hl = c.hl, lq = c.lq;
   const int qi = qb * 128 + c.wave * 32 + lq;
@@ -480,10 +502,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float sDl[kRows];
   __shared__ __attribute__((aligned(16))) int sDoc[kRows];
 
-  int w = blockIdx.x;
+  // Order: key blocks from first to last (the longest columns under causal masks first), then
+  // (batch, kv head) pairs; each XCD takes one contiguous range, pairs permuted as in dQ.
+  int w = xcd_remap(blockIdx.x, (int)((int64_t)a.B * a.Hkv * a.nkvb));
   const int kb = w % a.nkvb;
   w /= a.nkvb;
-  const int hkv = w % a.Hkv, b = w / a.Hkv;
+  const int pair = permute_pair(w, a.B * a.Hkv);
+  const int hkv = pair % a.Hkv, b = pair / a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane >> 5, lq = lane & 31;
