@@ -261,13 +261,16 @@ def run_backward(args, fa, torch, dev):
         qd = kd = sl = None
         if w.doc:
             qd = torch.from_numpy(np.ascontiguousarray(w.q_doc)).to(dev)
-            kd = torch.from_numpy(np.ascontiguousarray(w.kv_doc)).to(dev)
+            kd = qd if w.kv_doc is w.q_doc else torch.from_numpy(np.ascontiguousarray(w.kv_doc)).to(dev)
         if w.alibi_slopes is not None:
             sl = torch.from_numpy(w.alibi_slopes).to(dev)
         kw = dict(window=w.window or 0, prefix_len=w.prefix_len or 0, softcap=w.softcap or 0.0, alibi_slopes=sl,
                   q_doc=qd, kv_doc=kd)
+        # The schedule (query blocks by decreasing cost) where row costs vary: causal document masks.
+        order = args.row_order == "on" if args.row_order else bool(w.doc and w.causal)
         bm = fa.flexattn_block_mask_build(mk, w.B, w.Lq, w.Lkv, 128, 128, q_doc=qd, kv_doc=kd,
-                                          window=w.window or 0, prefix_len=w.prefix_len or 0, device=dev)
+                                          window=w.window or 0, prefix_len=w.prefix_len or 0, device=dev,
+                                          row_order=order)
         bmt = fa.flexattn_block_mask_transpose(bm)
         out, lse = fa.flexattn_fwd(q, k, v, bm, mk, sk, **kw)
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)

@@ -655,6 +655,7 @@ fa_status flexattn_bwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* 
     a.all_full = 0;
     a.Bm = bm->Bm;
     a.Hm = bm->Hm;
+    a.row_order = bm->row_order;  // schedule of the dq pass only
     a.kv_num = bm->kv_num_blocks;
     a.kv_idx = bm->kv_indices;
     a.full_num = bm->full_kv_num_blocks;

@@ -327,14 +327,29 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   // Order: query heads of one kv head fastest (they read the same K/V tiles), then query blocks
   // from last to first (the longest rows under causal masks first), then (batch, kv head)
   // pairs; each XCD takes one contiguous range, the pairs permuted so that ranges mix batches.
-  int w = xcd_remap(blockIdx.x, (int)((int64_t)a.B * a.Hq * a.nqb));
-  const int g = w % a.group;
-  w /= a.group;
-  const int qb = a.nqb - 1 - (w % a.nqb);
-  w /= a.nqb;
-  const int pair = permute_pair(w, a.B * (a.Hq / a.group));
-  const int hkv = pair % (a.Hq / a.group), b = pair / (a.Hq / a.group);
-  const int hq = hkv * a.group + g;
+  // With the BlockMask's schedule: rank r of the row order outermost (the costliest query
+  // blocks first), then (batch, kv head) pairs, then the query heads of a kv head, dealt
+  // round-robin to the XCDs as the forward does.
+  int qb, hq, hkv, b;
+  if (a.row_order != nullptr) {
+    const int npair = a.B * a.Hkv, per_rank = npair * a.group;
+    const int idx = blockIdx.x % per_rank, r = blockIdx.x / per_rank;
+    const int pair = idx % npair, g = idx / npair;
+    hkv = pair % a.Hkv;
+    b = pair / a.Hkv;
+    hq = hkv * a.group + g;
+    qb = min(max(a.row_order[(int64_t)(a.Bm == 1 ? 0 : b) * a.nqb + r], 0), a.nqb - 1);
+  } else {
+    int w = xcd_remap(blockIdx.x, (int)((int64_t)a.B * a.Hq * a.nqb));
+    const int g = w % a.group;
+    w /= a.group;
+    qb = a.nqb - 1 - (w % a.nqb);
+    w /= a.nqb;
+    const int pair = permute_pair(w, a.B * a.Hkv);
+    hkv = pair % a.Hkv;
+    b = pair / a.Hkv;
+    hq = hkv * a.group + g;
+  }
   const Lane c = make_lane();
   const int hl = c.hl, lq = c.lq;
   const int qi = qb * 128 + c.wave * 32 + lq;

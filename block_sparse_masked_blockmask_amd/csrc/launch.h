@@ -93,7 +93,9 @@ struct BwdArgs {
   int64_t dv_sb, dv_sh, dv_sl;
   int B, Hq, Hkv, Lq, Lkv, group;
   // Row lists (per 128-query block) for dq, column lists (per 128-key block) for dk/dv;
-  // all_full = 1: no BlockMask, every tile is full.
+  // all_full = 1: no BlockMask, every tile is full. row_order: the BlockMask's optional
+  // schedule (query blocks of each row set by decreasing cost), used by the dq pass, or null.
+  const int* row_order;
   const int* kv_num;
   const int* kv_idx;
   const int* full_num;

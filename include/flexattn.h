@@ -99,8 +99,9 @@ typedef struct {
  * mask: for each mask row set, the query blocks sorted by decreasing estimated cost
  * 4 * full + 5 * partial live tiles, ties by increasing query block (identity order when
  * n_qb > 8192). The builders fill it when the pointer is set. When it is set, the forward
- * starts the costliest query blocks first, so that long rows (long documents under causal
- * masks) do not finish last; results are identical with or without it. A caller-written
+ * (and the dq pass of flexattn_bwd) starts the costliest query blocks first, so that long
+ * rows (long documents under causal masks) do not finish last; results are identical with or
+ * without it. A caller-written
  * row_order must be a permutation of 0..n_qb-1 in each row set (entries are clamped into
  * range; a repeated entry leaves some output rows unwritten). */
 typedef struct {

@@ -258,3 +258,31 @@ def test_workloads_full_size(name):
         exp = do64[:, h * hq:(h + 1) * hq].sum(axis=(1, 2))
         err = np.abs(dv[:, h].sum(axis=1) - exp)
         assert np.all(err <= 2e-2 * np.sqrt((dv[:, h] ** 2).sum(axis=1)) + 1e-3), f"{name}: sum_j dV_j"
+
+
+def test_backward_with_schedule_bit_identical():
+    """A BlockMask carrying the cost-ordered schedule changes only when the dq pass's work
+    items run: dq, dk, dv and the slope gradient are bit-identical to the plain BlockMask's."""
+    import torch
+    import block_sparse_masked_blockmask_amd as fa
+    from tests._util import to_device
+    from workloads import grad_output, random_case
+    dev = torch.device("cuda", 0)
+    w = random_case(4700, dtype="bf16", B=2, Hq=4, Hkv=2, Lq=1500, Lkv=1500, doc=True, causal=True, alibi=True)
+    q, k, v = (to_device(x, "bf16", dev) for x in (w.q, w.k, w.v))
+    do = to_device(grad_output(w, 4700), "bf16", dev)
+    qd = torch.from_numpy(np.ascontiguousarray(w.q_doc)).to(dev)
+    sl = torch.from_numpy(w.alibi_slopes).to(dev)
+    mk, sk = fa.FA_MASK_DOC | fa.FA_MASK_CAUSAL, fa.FA_SCORE_ALIBI
+    res = []
+    for order in (False, True):
+        bm = fa.flexattn_block_mask_build(mk, w.B, w.Lq, w.Lkv, 128, 128, q_doc=qd, kv_doc=qd, device=dev,
+                                          row_order=order)
+        bmt = fa.flexattn_block_mask_transpose(bm)
+        out, lse = fa.flexattn_fwd(q, k, v, bm, mk, sk, alibi_slopes=sl, q_doc=qd, kv_doc=qd)
+        dq, dk, dv, ds = fa.flexattn_bwd(q, k, v, out, do, lse, bm, bmt, mk, sk, alibi_slopes=sl, q_doc=qd, kv_doc=qd,
+                                         slope_grad=True)
+        torch.cuda.synchronize()
+        res.append([t.float().cpu() for t in (out, lse, dq, dk, dv, ds)])
+    for a, b in zip(*res):
+        assert torch.equal(a, b)
