@@ -579,11 +579,6 @@ __device__ __forceinline__ void compute_step(const FwdArgs& a, const Ctx& c, con
   }
 }
 
-template <int TB, int WAVES, int NBUF>
-struct StepPlan {
-  static constexpr int HALVES = TB / kStep;  // steps per BlockMask tile
-};
-
 }  // namespace
 
 // MODE > 0: the split-KV form (a range of each tile list, partial results; waves without a
