@@ -271,7 +271,7 @@ def run_backward(args, fa, torch, dev):
         bm = fa.flexattn_block_mask_build(mk, w.B, w.Lq, w.Lkv, 128, 128, q_doc=qd, kv_doc=kd,
                                           window=w.window or 0, prefix_len=w.prefix_len or 0, device=dev,
                                           row_order=order)
-        bmt = fa.flexattn_block_mask_transpose(bm)
+        bmt = fa.flexattn_block_mask_transpose(bm, col_order=order)
         out, lse = fa.flexattn_fwd(q, k, v, bm, mk, sk, **kw)
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
         ds = torch.empty(w.Hq, dtype=torch.float32, device=dev) if sl is not None else None

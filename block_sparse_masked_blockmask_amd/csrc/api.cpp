@@ -586,7 +586,16 @@ fa_status flexattn_block_mask_transpose(const fa_block_mask* bm, fa_block_mask_t
   t.q_idx = out->q_indices;
   t.fullq_num = out->full_q_num_blocks;
   t.fullq_idx = out->full_q_indices;
+  if (reinterpret_cast<uintptr_t>(out->col_order) & 3u) return fail(FA_ERR_INVALID_ARG, "col_order must be 4-byte aligned");
   hipError_t e = fa::launch_block_mask_transpose(t, stream);
+  if (e == hipSuccess && out->col_order && bm->n_kvb > 0) {
+    fa::BlockMaskArgs o{};
+    o.nqb = bm->n_kvb;  // the schedule kernel sorts rows of nqb entries: here columns
+    o.full_num = out->full_q_num_blocks;
+    o.kv_num = out->q_num_blocks;
+    o.row_order = out->col_order;
+    e = fa::launch_block_mask_order(o, bm->Bm * bm->Hm, stream);
+  }
   if (e != hipSuccess) return fail(FA_ERR_DEVICE, "transpose launch failed: %s", hipGetErrorString(e));
   return ok();
 }
@@ -655,7 +664,8 @@ fa_status flexattn_bwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* 
     a.all_full = 0;
     a.Bm = bm->Bm;
     a.Hm = bm->Hm;
-    a.row_order = bm->row_order;  // schedule of the dq pass only
+    a.row_order = bm->row_order;    // schedule of the dq pass
+    a.col_order = bmt->col_order;   // schedule of the dk/dv pass
     a.kv_num = bm->kv_num_blocks;
     a.kv_idx = bm->kv_indices;
     a.full_num = bm->full_kv_num_blocks;

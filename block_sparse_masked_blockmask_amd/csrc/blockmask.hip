@@ -231,4 +231,10 @@ hipError_t launch_block_mask(const BlockMaskArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+hipError_t launch_block_mask_order(const BlockMaskArgs& a, int nsets, hipStream_t stream) {
+  if (nsets <= 0 || a.nqb <= 0) return hipSuccess;
+  hipLaunchKernelGGL(bm_order, dim3(nsets), dim3(kOrderThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
 }  // namespace fa

@@ -519,11 +519,23 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
 
   // Order: key blocks from first to last (the longest columns under causal masks first), then
   // (batch, kv head) pairs; each XCD takes one contiguous range, pairs permuted as in dQ.
-  int w = xcd_remap(blockIdx.x, (int)((int64_t)a.B * a.Hkv * a.nkvb));
-  const int kb = w % a.nkvb;
-  w /= a.nkvb;
-  const int pair = permute_pair(w, a.B * a.Hkv);
-  const int hkv = pair % a.Hkv, b = pair / a.Hkv;
+  // With the transposed BlockMask's column schedule: rank r outermost (the costliest columns
+  // first), (batch, kv head) pairs fastest, dealt round-robin to the XCDs.
+  int kb, hkv, b;
+  if (a.col_order != nullptr) {
+    const int npair = a.B * a.Hkv;
+    const int pair = blockIdx.x % npair, r = blockIdx.x / npair;
+    hkv = pair % a.Hkv;
+    b = pair / a.Hkv;
+    kb = min(max(a.col_order[(int64_t)(a.Bm == 1 ? 0 : b) * a.nkvb + r], 0), a.nkvb - 1);
+  } else {
+    int w = xcd_remap(blockIdx.x, (int)((int64_t)a.B * a.Hkv * a.nkvb));
+    kb = w % a.nkvb;
+    w /= a.nkvb;
+    const int pair = permute_pair(w, a.B * a.Hkv);
+    hkv = pair % a.Hkv;
+    b = pair / a.Hkv;
+  }
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane >> 5, lq = lane & 31;

@@ -96,6 +96,7 @@ struct BwdArgs {
   // all_full = 1: no BlockMask, every tile is full. row_order: the BlockMask's optional
   // schedule (query blocks of each row set by decreasing cost), used by the dq pass, or null.
   const int* row_order;
+  const int* col_order;  // the transposed BlockMask's optional column schedule (dk/dv pass), or null
   const int* kv_num;
   const int* kv_idx;
   const int* full_num;
@@ -126,6 +127,7 @@ struct TransposeArgs {
   int* q_idx;
   int* fullq_num;
   int* fullq_idx;
+  int* col_order;  // [Bm][Hm][nkvb] columns by decreasing cost, or null
 };
 
 // Quantized form: bf16 sources and int8 / E4M3 outputs (element strides; int8 elements are bytes).
@@ -181,5 +183,8 @@ hipError_t launch_splitkv_merge(const MergeArgs& m, hipStream_t stream);
 // Backward: delta/lse2 preparation, dq (+ slope partials), dk/dv, slope reduction.
 hipError_t launch_bwd(const BwdArgs& a, int score, hipStream_t stream);
 hipError_t launch_block_mask_transpose(const TransposeArgs& t, hipStream_t stream);
+// Sort nsets row sets of a.nqb entries by row_order_key of (a.full_num, a.kv_num) into
+// a.row_order (the builder's schedule kernel, also used for the transposed BlockMask's columns).
+hipError_t launch_block_mask_order(const BlockMaskArgs& a, int nsets, hipStream_t stream);
 
 }  // namespace fa

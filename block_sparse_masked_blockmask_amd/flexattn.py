@@ -46,7 +46,8 @@ class FaBlockMaskTransposed(ctypes.Structure):
     _fields_ = [("Bm", c_int32), ("Hm", c_int32), ("q_len", c_int32), ("kv_len", c_int32),
                 ("q_block", c_int32), ("kv_block", c_int32), ("n_qb", c_int32), ("n_kvb", c_int32),
                 ("q_num_blocks", c_void_p), ("q_indices", c_void_p),
-                ("full_q_num_blocks", c_void_p), ("full_q_indices", c_void_p)]
+                ("full_q_num_blocks", c_void_p), ("full_q_indices", c_void_p),
+                ("col_order", c_void_p)]
 
 
 class FlexAttnError(RuntimeError):
@@ -398,9 +399,11 @@ def flexattn_fwd_quant(qz: dict, *, sm_scale: float = 0.0, out: Optional[torch.T
 
 
 class BlockMaskTransposed:
-    """Device column view of a BlockMask (q-block lists per kv block; caller-owned memory)."""
+    """Device column view of a BlockMask (q-block lists per kv block; caller-owned memory).
+    col_order=True also allocates the optional column schedule (kv blocks by decreasing cost),
+    which the transpose fills and the backward's dk/dv pass uses."""
 
-    def __init__(self, bm: BlockMask):
+    def __init__(self, bm: BlockMask, col_order: bool = False):
         self.Bm, self.Hm, self.q_len, self.kv_len = bm.Bm, bm.Hm, bm.q_len, bm.kv_len
         self.q_block, self.kv_block, self.n_qb, self.n_kvb = bm.q_block, bm.kv_block, bm.n_qb, bm.n_kvb
         z = dict(dtype=torch.int32, device=bm.kv_num_blocks.device)
@@ -408,18 +411,21 @@ class BlockMaskTransposed:
         self.full_q_num_blocks = torch.empty((self.Bm, self.Hm, self.n_kvb), **z)
         self.q_indices = torch.empty((self.Bm, self.Hm, self.n_kvb, self.n_qb), **z)
         self.full_q_indices = torch.empty((self.Bm, self.Hm, self.n_kvb, self.n_qb), **z)
+        self.col_order = torch.empty((self.Bm, self.Hm, self.n_kvb), **z) if col_order else None
 
     def as_struct(self) -> FaBlockMaskTransposed:
         return FaBlockMaskTransposed(self.Bm, self.Hm, self.q_len, self.kv_len, self.q_block, self.kv_block,
                                      self.n_qb, self.n_kvb, self.q_num_blocks.data_ptr(), self.q_indices.data_ptr(),
-                                     self.full_q_num_blocks.data_ptr(), self.full_q_indices.data_ptr())
+                                     self.full_q_num_blocks.data_ptr(), self.full_q_indices.data_ptr(),
+                                     _ptr(self.col_order))
 
 
 def flexattn_block_mask_transpose(block_mask: BlockMask, *, out: Optional[BlockMaskTransposed] = None,
-                                  stream=None) -> BlockMaskTransposed:
-    """Column view of a device BlockMask (flexattn_block_mask_transpose)."""
+                                  stream=None, col_order: bool = False) -> BlockMaskTransposed:
+    """Column view of a device BlockMask (flexattn_block_mask_transpose); col_order=True (with
+    out=None) also computes the column schedule."""
     if out is None:
-        out = BlockMaskTransposed(block_mask)
+        out = BlockMaskTransposed(block_mask, col_order=col_order)
     s, t = block_mask.as_struct(), out.as_struct()
     _check(lib().flexattn_block_mask_transpose(ctypes.byref(s), ctypes.byref(t), _stream(stream)))
     return out

@@ -232,13 +232,19 @@ fa_status flexattn_fwd_splitkv(const fa_tensor* q, const fa_tensor* k, const fa_
  * Shapes (int32, device):
  *   q_num_blocks, full_q_num_blocks : [Bm][Hm][n_kvb]   (flexattn_block_mask_count_bytes(Bm, Hm,
  *                                                          kv_len, kv_block) bytes each)
- *   q_indices, full_q_indices       : [Bm][Hm][n_kvb][n_qb]  (flexattn_block_mask_index_bytes) */
+ *   q_indices, full_q_indices       : [Bm][Hm][n_kvb][n_qb]  (flexattn_block_mask_index_bytes)
+ * col_order (optional, int32 [Bm][Hm][n_kvb], NULL when unused) is the columns' schedule, as
+ * row_order is the rows': the kv blocks of each row set by decreasing cost 4 * full + 5 * partial
+ * live tiles, ties by increasing kv block (identity when n_kvb > 8192). The transpose fills it
+ * when the pointer is set; the dk/dv pass of flexattn_bwd then starts the costliest columns
+ * first. Results are identical with or without it. */
 typedef struct {
   int32_t Bm, Hm, q_len, kv_len, q_block, kv_block, n_qb, n_kvb;
   int32_t* q_num_blocks;
   int32_t* q_indices;
   int32_t* full_q_num_blocks;
   int32_t* full_q_indices;
+  int32_t* col_order;
 } fa_block_mask_transposed;
 
 /* Transpose a BlockMask into its column view on the device (the same tiles and classes, listed

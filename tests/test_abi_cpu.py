@@ -206,7 +206,7 @@ def test_splitkv_validation(case, status, needle):
 
 def test_bwd_sizes_and_struct():
     from block_sparse_masked_blockmask_amd.flexattn import FaBlockMaskTransposed
-    assert ctypes.sizeof(FaBlockMaskTransposed) == 4 * 8 + 8 * 4
+    assert ctypes.sizeof(FaBlockMaskTransposed) == 4 * 8 + 8 * 5  # four index arrays and the optional col_order
     rows4 = (2 * 3 * 130 + 3) // 4 * 4
     assert fa.flexattn_bwd_workspace_bytes(2, 3, 130) == (2 * rows4 + 2 * 3 * 2) * 4
     assert fa.flexattn_bwd_workspace_bytes(0, 3, 130) == 0

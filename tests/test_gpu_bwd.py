@@ -261,8 +261,9 @@ def test_workloads_full_size(name):
 
 
 def test_backward_with_schedule_bit_identical():
-    """A BlockMask carrying the cost-ordered schedule changes only when the dq pass's work
-    items run: dq, dk, dv and the slope gradient are bit-identical to the plain BlockMask's."""
+    """A BlockMask and transpose carrying the cost-ordered schedules change only when the dq
+    and dk/dv passes' work items run: dq, dk, dv and the slope gradient are bit-identical to
+    the plain ones'."""
     import torch
     import block_sparse_masked_blockmask_amd as fa
     from tests._util import to_device
@@ -278,7 +279,16 @@ def test_backward_with_schedule_bit_identical():
     for order in (False, True):
         bm = fa.flexattn_block_mask_build(mk, w.B, w.Lq, w.Lkv, 128, 128, q_doc=qd, kv_doc=qd, device=dev,
                                           row_order=order)
-        bmt = fa.flexattn_block_mask_transpose(bm)
+        bmt = fa.flexattn_block_mask_transpose(bm, col_order=order)
+        if order:
+            # The column schedule: kv blocks by decreasing 4 * full + 5 * partial, ties by kv block.
+            fullc = bmt.full_q_num_blocks.cpu().numpy().astype(np.int64)
+            partc = bmt.q_num_blocks.cpu().numpy().astype(np.int64)
+            got = bmt.col_order.cpu().numpy()
+            for bb in range(got.shape[0]):
+                cost = 4 * fullc[bb, 0] + 5 * partc[bb, 0]
+                want = sorted(range(got.shape[-1]), key=lambda kb: (-cost[kb], kb))
+                assert list(got[bb, 0]) == want
         out, lse = fa.flexattn_fwd(q, k, v, bm, mk, sk, alibi_slopes=sl, q_doc=qd, kv_doc=qd)
         dq, dk, dv, ds = fa.flexattn_bwd(q, k, v, out, do, lse, bm, bmt, mk, sk, alibi_slopes=sl, q_doc=qd, kv_doc=qd,
                                          slope_grad=True)
