@@ -32,7 +32,6 @@ PyTorch 2.5"; sage2 form = FlashRT-Structures PR #1 "LTX-2.5 attention forms"):
                 q-block lists a backward walks.
 
 Parity status: every function here is pinned by tests under tests/ marked
-"not gpu" (library routines, closed forms, invariants, brute force), except the
-quantized-attention diagnostic `quant.attention_dequantized`, whose output is
-"parity unpinned" beyond the cosine gate against the unquantized oracle.
+"not gpu" (library routines, closed forms, invariants, brute force, values worked
+by hand under tests/golden/).
 """

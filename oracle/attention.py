@@ -177,3 +177,83 @@ def attention_by_groups(q, k, v, q_doc, *, sm_scale=None):
                 out[b, hq, s0:e0] = (p @ v[b, hk, s0:e0]) / l
                 lse[b, hq, s0:e0] = (m + np.log(l))[:, 0]
     return out, lse
+
+
+def attention_by_documents_causal(q, k, v, q_doc, *, sm_scale=None):
+    """Attention under document equality AND causality, evaluated document by document.
+
+    Self-attention over packed documents (Lq == Lkv, one id array, each document a
+    contiguous run of equal ids; guide, "Production Engineering" 1, with the
+    demo's causal predicate): a query attends to the keys of its own run at or
+    before its position, so each run is plain causal attention on its own slice.
+    Pinned against `attention` with doc and causal on small packed cases.
+    Returns (out, lse) like `attention`.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, Hq, Lq, D = q.shape
+    assert k.shape[2] == Lq, "self-attention only"
+    group = Hq // k.shape[1]
+    scale = resolve_scale(D, sm_scale)
+    out = np.zeros(q.shape)
+    lse = np.zeros((B, Hq, Lq))
+    for b in range(B):
+        ids = np.asarray(q_doc[b])
+        starts = np.flatnonzero(np.r_[True, ids[1:] != ids[:-1]])
+        ends = np.r_[starts[1:], Lq]
+        assert len(np.unique(ids[starts])) == len(starts), "ids must be contiguous runs"
+        for s0, e0 in zip(starts, ends):
+            n = e0 - s0
+            upper = np.triu(np.ones((n, n), dtype=bool), 1)   # key after query: masked
+            for hq in range(Hq):
+                hk = hq // group
+                sc = q[b, hq, s0:e0] @ k[b, hk, s0:e0].T * scale
+                sc[upper] = -np.inf
+                m = sc.max(axis=1, keepdims=True)               # the diagonal is always allowed
+                p = np.exp(sc - m)
+                l = p.sum(axis=1, keepdims=True)
+                out[b, hq, s0:e0] = (p @ v[b, hk, s0:e0]) / l
+                lse[b, hq, s0:e0] = (m + np.log(l))[:, 0]
+    return out, lse
+
+
+def attention_band(q, k, v, window, *, softcap=None, alibi_slopes=None, sm_scale=None, heads=None,
+                   chunk=128):
+    """Causal sliding-window attention (i >= j and i - j < window), evaluated on the band.
+
+    Query rows [r0, r1) can only see keys [r0 - window + 1, r1), so only that band
+    of the score matrix is materialised; score_mod (ALiBi, then soft-cap) and the
+    two predicates are those of `attention`. Self-attention (Lq == Lkv).
+    heads: optional list of (b, hq) to compute (others left 0). Pinned against
+    `attention` with causal, window and the score transforms on small cases.
+    Returns (out, lse) like `attention`.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, Hq, Lq, D = q.shape
+    assert k.shape[2] == Lq, "self-attention only"
+    group = Hq // k.shape[1]
+    scale = resolve_scale(D, sm_scale)
+    out = np.zeros(q.shape)
+    lse = np.zeros((B, Hq, Lq))
+    todo = heads if heads is not None else [(b, h) for b in range(B) for h in range(Hq)]
+    for b, hq in todo:
+        hk = hq // group
+        slope = None if alibi_slopes is None else float(np.float32(alibi_slopes[hq]))
+        for r0 in range(0, Lq, chunk):
+            r1 = min(Lq, r0 + chunk)
+            c0 = max(0, r0 - window + 1)
+            rows = np.arange(r0, r1)
+            cols = np.arange(c0, r1)
+            sc = q[b, hq, r0:r1] @ k[b, hk, c0:r1].T * scale
+            sc = score_mod(sc, rows, cols, alibi_slope=slope, softcap=softcap)
+            keep = mask_mod(rows, cols, causal=True, window=window)
+            sc[~keep] = -np.inf
+            m = sc.max(axis=1, keepdims=True)                   # j = i is always allowed
+            p = np.exp(sc - m)
+            l = p.sum(axis=1, keepdims=True)
+            out[b, hq, r0:r1] = (p @ v[b, hk, c0:r1]) / l
+            lse[b, hq, r0:r1] = (m + np.log(l))[:, 0]
+    return out, lse

@@ -118,8 +118,10 @@ def attention_dequantized(q8, sq, k8, sk, v8, sv, rows, b, h, *, sm_scale=None, 
     """Diagnostic: unmasked fp64 attention on dequantized inputs for some rows.
 
     P is rounded through E4M3 at a fixed x448 scale (P in [0, 1], relative to the
-    final row maximum); the row sum uses the unrounded P. Parity unpinned: this
-    only bounds how much of the quantized form's error is the quantization itself.
+    final row maximum); the row sum uses the unrounded P. It bounds how much of the
+    quantized form's error is the quantization itself. Pinned by two checks: without
+    the P rounding it equals the attention oracle on the dequantized tensors, and a
+    two-key case worked by hand puts 448 P on an E4M3 tie (tests/golden).
     """
     qh = dequantize_int8(q8[b:b + 1, h:h + 1], sq[b:b + 1, h:h + 1])[0, 0]
     kh = dequantize_int8(k8[b:b + 1, h:h + 1], sk[b:b + 1, h:h + 1])[0, 0]

@@ -231,3 +231,54 @@ def test_bf16_widening_exact():
     assert vals[4] == (2 - 2 ** -7) * 2.0 ** 127
     assert vals[5] == 2.0 ** -133
     assert vals[6] == 3.140625
+
+
+def test_documents_causal_restatement():
+    """attention_by_documents_causal: every document equals causal SDPA on its own slice (library
+    routine), and the whole equals the definition with doc AND causal, GQA included."""
+    q, k, v = _rand(21, 2, 4, 2, 150, 150, 16)
+    docs = np.stack([_doc_runs(22, 150, 9), _doc_runs(23, 150, 3)])
+    out, lse = A.attention_by_documents_causal(q, k, v, docs)
+    for b in range(2):
+        for g in np.unique(docs[b]):
+            sl = np.flatnonzero(docs[b] == g)
+            kk = np.repeat(k[b:b + 1, :, sl], 2, axis=1)
+            vv = np.repeat(v[b:b + 1, :, sl], 2, axis=1)
+            ref = _sdpa(q[b:b + 1, :, sl], kk, vv, is_causal=True)
+            np.testing.assert_allclose(out[b:b + 1, :, sl], ref, rtol=0, atol=1e-12)
+    o_def, l_def = A.attention(q, k, v, {"doc": True, "causal": True, "q_doc": docs, "kv_doc": docs})
+    np.testing.assert_allclose(out, o_def, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, l_def, rtol=0, atol=1e-12)
+    # One document is plain causal attention.
+    one = np.zeros((2, 150), np.int32)
+    o1, _ = A.attention_by_documents_causal(q, k, v, one)
+    ref = _sdpa(q, np.repeat(k, 2, axis=1), np.repeat(v, 2, axis=1), is_causal=True)
+    np.testing.assert_allclose(o1, ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("window,score", [(1, None), (7, None), (40, "softcap"), (64, "alibi_softcap"), (300, None)])
+def test_band_restatement(window, score):
+    """attention_band equals the definition with causal AND window (and the score transforms);
+    window 1 keeps only the diagonal (out_i = v_i, lse_i = s_ii); a window wider than the
+    sequence is causal SDPA (library routine)."""
+    q, k, v = _rand(30 + window, 2, 4, 2, 260, 260, 16)
+    kw, spec = {}, {"causal": True, "window": window}
+    if score:
+        kw["softcap"] = spec["softcap"] = 1.5
+    if score == "alibi_softcap":
+        kw["alibi_slopes"] = spec["alibi_slopes"] = np.linspace(0.1, 0.8, 4).astype(np.float32)
+    out, lse = A.attention_band(q, k, v, window, chunk=64, **kw)
+    o_def, l_def = A.attention(q, k, v, spec)
+    np.testing.assert_allclose(out, o_def, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, l_def, rtol=0, atol=1e-12)
+    if window == 1:
+        np.testing.assert_allclose(out, np.repeat(v, 2, axis=1), rtol=0, atol=1e-15)
+        s_ii = np.einsum("bhld,bhld->bhl", q, np.repeat(k, 2, axis=1)) / 4.0
+        np.testing.assert_allclose(lse, s_ii, rtol=0, atol=1e-12)
+    if window == 300:
+        ref = _sdpa(q, np.repeat(k, 2, axis=1), np.repeat(v, 2, axis=1), is_causal=True)
+        np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+    # Selected heads only.
+    o_h, _ = A.attention_band(q, k, v, window, heads=[(1, 3)], chunk=64, **kw)
+    np.testing.assert_array_equal(o_h[1, 3], out[1, 3])
+    assert not o_h[0].any()

@@ -133,3 +133,55 @@ def test_k_mean_is_exactly_rounded():
     k = np.zeros((1, 1, 4, 1), np.float32)
     k[0, 0, :, 0] = [1e8, 1.0, -1e8, 1.0]
     assert Q.k_channel_mean(k)[0, 0, 0] == np.float32(0.5)
+
+
+def test_attention_dequantized_without_rounding_is_attention_on_dequantized_inputs():
+    """With round_p=False the diagnostic is plain attention on the dequantized tensors, so it must
+    equal the (separately pinned) attention oracle run on dequantize_int8 / dequantize_fp8 outputs."""
+    from oracle import attention as A
+    rng = np.random.default_rng(11)
+    B, H, L, D = 2, 3, 150, 16
+    q = rng.standard_normal((B, H, L, D)).astype(np.float32)
+    k = rng.standard_normal((B, H, L, D)).astype(np.float32)
+    v = (rng.standard_normal((B, H, L, D)) * rng.uniform(0.5, 2, (1, H, 1, D))).astype(np.float32)
+    q8, sq = Q.quantize_int8_blocks(q)
+    k8, sk = Q.quantize_int8_blocks(k)
+    v8, sv = Q.quantize_fp8_channels(v)
+    qd, kd, vd = Q.dequantize_int8(q8, sq), Q.dequantize_int8(k8, sk), Q.dequantize_fp8(v8, sv)
+    o_ref, _ = A.attention(qd, kd, vd, {})
+    for b, h in ((0, 0), (1, 2)):
+        rows = np.arange(L)
+        got = Q.attention_dequantized(q8, sq, k8, sk, v8, sv, rows, b, h, round_p=False)
+        np.testing.assert_allclose(got, o_ref[b, h], rtol=0, atol=1e-12)
+    # An explicit scale is the attention oracle's sm_scale.
+    o_ref2, _ = A.attention(qd, kd, vd, {"sm_scale": 0.3})
+    got = Q.attention_dequantized(q8, sq, k8, sk, v8, sv, np.arange(L), 1, 1, sm_scale=0.3, round_p=False)
+    np.testing.assert_allclose(got, o_ref2[1, 1], rtol=0, atol=1e-12)
+
+
+def test_attention_dequantized_p_rounding_hand_case():
+    """Two keys worked by hand (tests/golden/quant_p_tie.json): 448 P lands exactly on the midpoint of
+    the E4M3 values 160 and 176 and must round to the even code (160); the row sum must use the
+    unrounded P."""
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "quant_p_tie.json")))
+    s = -float(np.log(g["p_key1"]))
+    while np.exp(-s) != g["p_key1"]:  # the precondition of the derivation: exp(-s) is exactly 0.375
+        s = float(np.nextafter(s, 0.0))
+    q8 = np.array(g["q_codes"], np.int8).reshape(1, 1, 1, 4)
+    k8 = np.array(g["k_codes"], np.int8).reshape(1, 1, 2, 4)
+    v8 = np.array(g["v_codes"], np.uint8).reshape(1, 1, 2, 4)
+    one = np.ones((1, 1, 1), np.float32)
+    sv = np.array(g["v_scales"], np.float32).reshape(1, 1, 4)
+    want_r = np.array([n / d for n, d in g["out_round_p"]])
+    want_x = np.array([n / d for n, d in g["out_exact_p"]])
+    got_r = Q.attention_dequantized(q8, one, k8, one, v8, sv, [0], 0, 0, sm_scale=s, round_p=True)[0]
+    got_x = Q.attention_dequantized(q8, one, k8, one, v8, sv, [0], 0, 0, sm_scale=s, round_p=False)[0]
+    np.testing.assert_allclose(got_r, want_r, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(got_x, want_x, rtol=0, atol=1e-15)
+    # The plausible wrong readings give different values (the pin can tell them apart).
+    v0 = np.array([1.0, 1.0, -2.0, 0.5])
+    v1 = np.array([2.0, -0.5, 8.0, 1.0])
+    assert np.abs(got_r - (28 * v0 + 11 * v1) / 38.5).max() > 1e-3   # tie rounded up to 176
+    assert np.abs(got_r - (14 * v0 + 5 * v1) / 19.0).max() > 1e-3    # row sum of the rounded P
