@@ -6,16 +6,19 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include <vector>
 
+#include "api_internal.h"
 #include "flexattn.h"
 #include "launch.h"
 #include "tile_class.h"
 
-namespace {
+namespace fa_api {
 
 thread_local std::string g_last_error;
 
@@ -40,6 +43,43 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 const int kValidMask = FA_MASK_DOC | FA_MASK_CAUSAL | FA_MASK_WINDOW | FA_MASK_PREFIX_LM;
 const int kValidScore = FA_SCORE_ALIBI | FA_SCORE_SOFTCAP;
+
+// The kernels are built for gfx950 only. Every launching entry point checks, after validating
+// its arguments and before enqueuing anything, that the current device is a gfx950; another
+// device is refused with FA_ERR_UNSUPPORTED and its architecture name. The name is read once
+// per device and cached. FLEXATTN_DEVICE_ARCH, when set, replaces the device's name (a test
+// hook: it lets the refusal be checked on a machine without that device).
+std::mutex g_arch_mu;
+std::string g_arch_name[kMaxDevices];
+
+bool arch_is_gfx950(const std::string& name) {
+  // hipDeviceProp_t::gcnArchName is "gfx950" followed by optional ":feature+/-" suffixes.
+  return name.compare(0, 6, "gfx950") == 0 && (name.size() == 6 || name[6] == ':');
+}
+
+fa_status check_device() {
+  std::string name;
+  const char* over = std::getenv("FLEXATTN_DEVICE_ARCH");
+  if (over != nullptr && *over != '\0') {
+    name = over;
+  } else {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(FA_ERR_DEVICE, "no current HIP device: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(FA_ERR_UNSUPPORTED, "device index %d above %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_arch_mu);
+    if (g_arch_name[dev].empty()) {
+      hipDeviceProp_t prop;
+      e = hipGetDeviceProperties(&prop, dev);
+      if (e != hipSuccess) return fail(FA_ERR_DEVICE, "cannot read device %d properties: %s", dev, hipGetErrorString(e));
+      g_arch_name[dev] = prop.gcnArchName[0] ? prop.gcnArchName : "unknown";
+    }
+    name = g_arch_name[dev];
+  }
+  if (!arch_is_gfx950(name))
+    return fail(FA_ERR_UNSUPPORTED, "device %s is not gfx950: the kernels are built for gfx950 only", name.c_str());
+  return FA_OK;
+}
 
 // Checks shared by the builder and the forward pass for the mask parameters.
 fa_status check_mask(int mask_kind, const fa_params* p, int Lq, int Lkv) {
@@ -84,7 +124,9 @@ fa_status check_build(int mask_kind, const fa_params* p, int B, int q_len, int k
   return FA_OK;
 }
 
-}  // namespace
+}  // namespace fa_api
+
+using namespace fa_api;
 
 extern "C" {
 
@@ -102,20 +144,24 @@ size_t flexattn_block_mask_count_bytes(int Bm, int Hm, int q_len, int q_block) {
   return (size_t)Bm * Hm * cdiv(q_len, q_block) * sizeof(int32_t);
 }
 
+size_t flexattn_block_mask_bytes(int Bm, int Hm, int q_len, int kv_len, int q_block, int kv_block) {
+  if (Bm <= 0 || Hm <= 0 || q_len < 0 || kv_len < 0 || q_block <= 0 || kv_block <= 0) return 0;
+  return 2 * flexattn_block_mask_index_bytes(Bm, Hm, q_len, kv_len, q_block, kv_block) +
+         2 * flexattn_block_mask_count_bytes(Bm, Hm, q_len, q_block);
+}
+
 size_t flexattn_block_mask_workspace_bytes(int mask_kind, int B, int q_len, int kv_len, int q_block, int kv_block) {
   if (!(mask_kind & FA_MASK_DOC) || B <= 0 || q_len < 0 || kv_len < 0 || q_block <= 0 || kv_block <= 0) return 0;
   return (size_t)B * (cdiv(q_len, q_block) + cdiv(kv_len, kv_block)) * 4 * sizeof(int32_t);
 }
 
-fa_status flexattn_block_mask_build(int mask_kind, const fa_params* p, int B, int q_len, int kv_len,
-                                    fa_block_mask* out, void* workspace, size_t workspace_bytes,
-                                    hipStream_t stream) {
-  fa_status st = check_build(mask_kind, p, B, q_len, kv_len, out);
-  if (st != FA_OK) return st;
-  const size_t need = flexattn_block_mask_workspace_bytes(mask_kind, B, q_len, kv_len, out->q_block, out->kv_block);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
-    return fail(FA_ERR_INVALID_ARG, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
-  if (need > 0 && !aligned16(workspace)) return fail(FA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+}  // extern "C"
+
+namespace fa_api {
+
+// Enqueue the device builder; `workspace` holds the per-block summaries (validated by the caller).
+fa_status launch_build(int mask_kind, const fa_params* p, int B, int q_len, int kv_len, fa_block_mask* out,
+                       void* workspace, size_t need, hipStream_t stream) {
   fa::BlockMaskArgs a{};
   a.flags = mask_kind;
   a.window = (mask_kind & FA_MASK_WINDOW) ? p->window : 0;
@@ -144,6 +190,24 @@ fa_status flexattn_block_mask_build(int mask_kind, const fa_params* p, int B, in
   if (e != hipSuccess) return fail(FA_ERR_DEVICE, "block mask launch failed: %s", hipGetErrorString(e));
   return ok();
 }
+
+}  // namespace fa_api
+
+extern "C" {
+
+fa_status flexattn_block_mask_build(int mask_kind, const fa_params* p, int B, int q_len, int kv_len,
+                                    fa_block_mask* out, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+  fa_status st = check_build(mask_kind, p, B, q_len, kv_len, out);
+  if (st != FA_OK) return st;
+  const size_t need = flexattn_block_mask_workspace_bytes(mask_kind, B, q_len, kv_len, out->q_block, out->kv_block);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(FA_ERR_INVALID_ARG, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+  if (need > 0 && !aligned16(workspace)) return fail(FA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  if ((st = check_device()) != FA_OK) return st;
+  return launch_build(mask_kind, p, B, q_len, kv_len, out, workspace, need, stream);
+}
+
 
 fa_status flexattn_block_mask_build_host(int mask_kind, const fa_params* p, int B, int q_len, int kv_len,
                                          fa_block_mask* out) {
@@ -245,6 +309,14 @@ static fa_status check_tensor(const fa_tensor* t, const char* name, int elem_ali
 static fa_status fwd_quantized(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_block_mask* bm,
                                int mask_kind, int score_kind, const fa_params* p, fa_tensor* out, float* lse,
                                int qk_block, const float* q_delta, hipStream_t stream);
+
+size_t flexattn_fwd_workspace_bytes(const fa_tensor* q, const fa_tensor* k, int mask_kind, int score_kind) {
+  (void)q;
+  (void)k;
+  (void)mask_kind;
+  (void)score_kind;
+  return 0;  // every forward form keeps its intermediates in registers and LDS
+}
 
 size_t flexattn_fwd_splitkv_workspace_bytes(int B, int Hq, int Lq, int n_splits) {
   if (B < 0 || Hq < 0 || Lq < 0 || n_splits < 1) return 0;
@@ -367,6 +439,7 @@ fa_status fwd_impl(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, c
   a.slopes = (score_kind & FA_SCORE_ALIBI) ? p->alibi_slopes : nullptr;
   a.total_wg = (int)total;
   a.nsplit = nsplit;
+  if ((st = check_device()) != FA_OK) return st;
   if (nsplit > 1) {
     a.part_o = static_cast<float*>(workspace);
     a.part_lse = a.part_o + (size_t)nsplit * B * q->H * Lq * 128;
@@ -488,6 +561,7 @@ static fa_status quantize_impl(const fa_tensor* q, const fa_tensor* k, const fa_
   a.q8 = dst(q8, cdiv(q->L, qk_block));
   a.k8 = dst(k8, cdiv(k->L, qk_block));
   a.v8 = dst(v8, 128);
+  if ((st = check_device()) != FA_OK) return st;
   hipError_t e = fa::launch_quantize(a, stream);
   if (e != hipSuccess) return fail(FA_ERR_DEVICE, "quantize launch failed: %s", hipGetErrorString(e));
   return ok();
@@ -544,6 +618,7 @@ static fa_status fwd_quantized(const fa_tensor* q, const fa_tensor* k, const fa_
   a.scale_log2 = sm * 1.4426950408889634f;
   a.sm_scale = sm;
   a.total_wg = (int)total;
+  if ((st = check_device()) != FA_OK) return st;
   hipError_t e = fa::launch_fwd_quant(a, stream);
   if (e != hipSuccess) return fail(FA_ERR_DEVICE, "forward launch failed: %s", hipGetErrorString(e));
   return ok();
@@ -587,6 +662,8 @@ fa_status flexattn_block_mask_transpose(const fa_block_mask* bm, fa_block_mask_t
   t.fullq_num = out->full_q_num_blocks;
   t.fullq_idx = out->full_q_indices;
   if (reinterpret_cast<uintptr_t>(out->col_order) & 3u) return fail(FA_ERR_INVALID_ARG, "col_order must be 4-byte aligned");
+  fa_status st = check_device();
+  if (st != FA_OK) return st;
   hipError_t e = fa::launch_block_mask_transpose(t, stream);
   if (e == hipSuccess && out->col_order && bm->n_kvb > 0) {
     fa::BlockMaskArgs o{};
@@ -707,6 +784,7 @@ fa_status flexattn_bwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* 
   a.lse2 = ws;
   a.delta = ws ? ws + rows4 : nullptr;
   a.slope_part = (dslopes != nullptr && ws) ? ws + 2 * rows4 : nullptr;  // read only when rows > 0
+  if ((st = check_device()) != FA_OK) return st;
   hipError_t e = fa::launch_bwd(a, score_kind, stream);
   if (e != hipSuccess) return fail(FA_ERR_DEVICE, "backward launch failed: %s", hipGetErrorString(e));
   return ok();

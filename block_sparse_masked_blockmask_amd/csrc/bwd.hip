@@ -387,8 +387,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   } else {
     const int bm = a.Bm == 1 ? 0 : b;
     const int64_t r = (int64_t)bm * a.nqb + qb;
-    nfull = a.full_num[r];
-    npart = a.kv_num[r];
+    nfull = clamp_count(a.full_num[r], a.nkvb);
+    npart = clamp_count(a.kv_num[r], a.nkvb);
     full = a.full_idx + r * a.nkvb;
     part = a.kv_idx + r * a.nkvb;
   }
@@ -396,7 +396,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   auto step_kv0 = [&](int s, bool& masked) {
     const int t = s >> 1;
     const bool partial = t >= nfull;
-    const int kb = partial ? part[t - nfull] : (a.all_full ? t : full[t]);
+    // An entry outside [0, n_kvb) becomes n_kvb: its rows lie past the keys, so the transfers
+    // clamp to the last key and every score of the step is masked (it adds nothing).
+    const int kb = partial ? sanitize_block(part[t - nfull], a.nkvb) : (a.all_full ? t : sanitize_block(full[t], a.nkvb));
     const int kv0 = kb * 128 + (s & 1) * kRows;
     masked = partial || kv0 + kRows > a.Lkv;
     return kv0;
@@ -580,8 +582,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
     } else {
       const int bm = a.Bm == 1 ? 0 : b, hm = a.Hm == 1 ? 0 : hq;
       const int64_t r = ((int64_t)bm * a.Hm + hm) * a.nkvb + kb;
-      nfull = a.fullq_num[r];
-      npart = a.q_num[r];
+      nfull = clamp_count(a.fullq_num[r], a.nqb);
+      npart = clamp_count(a.q_num[r], a.nqb);
       full = a.fullq_idx + r * a.nqb;
       part = a.q_idx + r * a.nqb;
     }
@@ -589,7 +591,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
     for (int s = 0; s < nsteps; ++s) {
       const int t = s >> 1;
       const bool masked = t >= nfull;
-      const int qbk = masked ? part[t - nfull] : (a.all_full ? t : full[t]);
+      // An entry outside [0, n_qb) becomes n_qb, whose rows lie past the queries: skipped.
+      const int qbk = masked ? sanitize_block(part[t - nfull], a.nqb) : (a.all_full ? t : sanitize_block(full[t], a.nqb));
       const int q0 = qbk * 128 + (s & 1) * kRows;
       if (q0 >= a.Lq) continue;  // uniform over the workgroup
 
@@ -719,8 +722,8 @@ __global__ __launch_bounds__(256) void bm_transpose_kernel(TransposeArgs t) {
     int cls = 0;
     if (qb < t.nqb) {
       const int64_t r = mrow * t.nqb + qb;
-      if (find(t.kv_idx + r * t.nkvb, t.kv_num[r], kb)) cls = 1;
-      else if (find(t.full_idx + r * t.nkvb, t.full_num[r], kb)) cls = 2;
+      if (find(t.kv_idx + r * t.nkvb, clamp_count(t.kv_num[r], t.nkvb), kb)) cls = 1;
+      else if (find(t.full_idx + r * t.nkvb, clamp_count(t.full_num[r], t.nkvb), kb)) cls = 2;
     }
     const unsigned long long mp = __ballot(cls == 1), mf = __ballot(cls == 2);
     if (cls == 1) qi_out[np + __popcll(mp & lt)] = qb;

@@ -73,6 +73,13 @@ __host__ __device__ inline int classify_closed(int flags, int window, int prefix
   return 3;
 }
 
+// BlockMask counts and list entries come from caller memory. Kernels that walk the lists clamp
+// each count into [0, cap] (cap = the list length) and replace an entry outside [0, n) by n, a
+// block past the last one, which every walker skips (its rows lie beyond the sequence), so that a
+// corrupt BlockMask cannot send a kernel outside its arrays.
+__host__ __device__ inline int clamp_count(int n, int cap) { return n < 0 ? 0 : (n > cap ? cap : n); }
+__host__ __device__ inline int sanitize_block(int x, int n) { return (x >= 0 && x < n) ? x : n; }
+
 // Schedule key of a BlockMask row (the optional row_order of fa_block_mask): rows are sorted by
 // increasing key, i.e. by decreasing estimated cost 4 * full + 5 * partial live tiles (a partial
 // tile also evaluates the mask on every score), ties by increasing query block. The cost is

@@ -67,6 +67,10 @@ def lib() -> ctypes.CDLL:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
         L = ctypes.CDLL(LIB_PATH)
+        L.flexattn_block_mask_bytes.argtypes = [c_int] * 6
+        L.flexattn_block_mask_bytes.restype = c_size_t
+        L.flexattn_fwd_workspace_bytes.argtypes = [c_void_p, c_void_p, c_int, c_int]
+        L.flexattn_fwd_workspace_bytes.restype = c_size_t
         L.flexattn_block_mask_index_bytes.argtypes = [c_int] * 6
         L.flexattn_block_mask_index_bytes.restype = c_size_t
         L.flexattn_block_mask_count_bytes.argtypes = [c_int] * 4
@@ -138,6 +142,21 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else t.data_ptr()
 
 
+def _record(stream, *tensors):
+    """Tensors that this binding allocated (on the current stream) and handed to kernels on
+    `stream`: record that use with the caching allocator, so that their memory is not given to
+    another allocation on the current stream while those kernels may still run. Outputs and
+    workspaces the caller passes in are the caller's to order."""
+    if stream is None:
+        return
+    s = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(int(stream))
+    if s.cuda_stream == torch.cuda.current_stream().cuda_stream:
+        return
+    for t in tensors:
+        if isinstance(t, torch.Tensor) and t.is_cuda:
+            t.record_stream(s)
+
+
 _DTYPES = {torch.float32: FA_F32, torch.bfloat16: FA_BF16, torch.int8: FA_I8, torch.uint8: FA_FP8_E4M3}
 if hasattr(torch, "float8_e4m3fn"):
     _DTYPES[torch.float8_e4m3fn] = FA_FP8_E4M3
@@ -154,6 +173,16 @@ def tensor_desc(t: torch.Tensor, scale: Optional[torch.Tensor] = None) -> FaTens
         raise ValueError("the D dimension must be contiguous")
     return FaTensor(t.data_ptr(), _DTYPES[t.dtype], B, H, L, D, t.stride(0), t.stride(1), t.stride(2),
                     _ptr(scale))
+
+
+def flexattn_block_mask_bytes(Bm, Hm, q_len, kv_len, q_block, kv_block) -> int:
+    return lib().flexattn_block_mask_bytes(Bm, Hm, q_len, kv_len, q_block, kv_block)
+
+
+def flexattn_fwd_workspace_bytes(q: torch.Tensor, k: torch.Tensor, mask_kind: int = FA_MASK_NONE,
+                                 score_kind: int = FA_SCORE_NONE) -> int:
+    tq, tk = tensor_desc(q), tensor_desc(k)
+    return lib().flexattn_fwd_workspace_bytes(ctypes.byref(tq), ctypes.byref(tk), mask_kind, score_kind)
 
 
 def flexattn_block_mask_index_bytes(Bm, Hm, q_len, kv_len, q_block, kv_block) -> int:
@@ -186,6 +215,10 @@ class BlockMask:
         self.full_kv_indices = torch.empty((Bm, Hm, self.n_qb, self.n_kvb), **z)
         self.row_order = torch.empty((Bm, Hm, self.n_qb), **z) if row_order else None
 
+    def arrays(self):
+        return [t for t in (self.kv_num_blocks, self.full_kv_num_blocks, self.kv_indices, self.full_kv_indices,
+                            self.row_order) if t is not None]
+
     def to(self, device) -> "BlockMask":
         """A copy of this BlockMask with its arrays on `device`."""
         bm = BlockMask.__new__(BlockMask)
@@ -216,17 +249,21 @@ def flexattn_block_mask_build(mask_kind: int, B: int, q_len: int, kv_len: int, q
     computed when out.row_order is allocated."""
     if device is None:
         device = q_doc.device if q_doc is not None else torch.device("cuda", torch.cuda.current_device())
+    tmp = []
     if out is None:
         Bm = B if (mask_kind & FA_MASK_DOC) else 1
         out = BlockMask(Bm, 1, q_len, kv_len, q_block, kv_block, device, row_order=row_order)
+        tmp += out.arrays()
     ws_bytes = flexattn_block_mask_workspace_bytes(mask_kind, B, q_len, kv_len, q_block, kv_block)
     if ws_bytes and workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=device)
+        tmp.append(workspace)
     p = _params(window=window, prefix_len=prefix_len, q_doc=q_doc, kv_doc=kv_doc)
     s = out.as_struct()
     _check(lib().flexattn_block_mask_build(mask_kind, ctypes.byref(p), B, q_len, kv_len, ctypes.byref(s),
                                            _ptr(workspace), workspace.numel() if workspace is not None else 0,
                                            _stream(stream)))
+    _record(stream, *tmp)
     return out
 
 
@@ -275,11 +312,14 @@ def flexattn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_mask: 
     For the quantized form pass the int8 q/k and E4M3 v codes with their scale arrays (as
     returned by flexattn_quantize_qkv); out is then bf16.
     """
+    tmp = []
     if out is None:
         odt = torch.bfloat16 if q.dtype == torch.int8 else q.dtype
         out = torch.empty(q.shape, dtype=odt, device=q.device)
+        tmp.append(out)
     if lse is None and return_lse:
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+        tmp.append(lse)
     if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != tuple(q.shape[:3])):
         raise ValueError("lse must be a contiguous float32 [B, Hq, Lq] tensor")
     tq, tk, tv, to = tensor_desc(q, q_scale), tensor_desc(k, k_scale), tensor_desc(v, v_scale), tensor_desc(out)
@@ -288,6 +328,7 @@ def flexattn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_mask: 
     bm = ctypes.byref(block_mask.as_struct()) if block_mask is not None else None
     _check(lib().flexattn_fwd(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), bm, mask_kind, score_kind,
                               ctypes.byref(p), ctypes.byref(to), _ptr(lse), _stream(stream)))
+    _record(stream, *tmp)
     return out, lse
 
 
@@ -303,15 +344,19 @@ def flexattn_fwd_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, bloc
                          return_lse: bool = True, stream=None):
     """Split-KV forward (flexattn_fwd_splitkv); returns (out, lse). The workspace is allocated
     when not given (flexattn_fwd_splitkv_workspace_bytes bytes)."""
+    tmp = []
     if out is None:
         out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+        tmp.append(out)
     if lse is None and return_lse:
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+        tmp.append(lse)
     if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != tuple(q.shape[:3])):
         raise ValueError("lse must be a contiguous float32 [B, Hq, Lq] tensor")
     ws_bytes = flexattn_fwd_splitkv_workspace_bytes(q.shape[0], q.shape[1], q.shape[2], n_splits) if n_splits > 1 else 0
     if ws_bytes and workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+        tmp.append(workspace)
     tq, tk, tv, to = tensor_desc(q), tensor_desc(k), tensor_desc(v), tensor_desc(out)
     p = _params(window=window, prefix_len=prefix_len, softcap=softcap, alibi_slopes=alibi_slopes,
                 q_doc=q_doc, kv_doc=kv_doc, sm_scale=sm_scale)
@@ -320,6 +365,7 @@ def flexattn_fwd_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, bloc
                                       score_kind, ctypes.byref(p), ctypes.byref(to), _ptr(lse), n_splits,
                                       _ptr(workspace), workspace.numel() if workspace is not None else 0,
                                       _stream(stream)))
+    _record(stream, *tmp)
     return out, lse
 
 
@@ -329,6 +375,7 @@ def flexattn_quantize_qkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, 
     [B,H,128]; `out` may supply these tensors (same keys) to avoid allocation."""
     def blocks(t):
         return -(-t.shape[2] // 128)
+    fresh = out is None
     if out is None:
         out = {
             "q8": torch.empty(q.shape, dtype=torch.int8, device=q.device),
@@ -341,6 +388,8 @@ def flexattn_quantize_qkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, 
     descs = [tensor_desc(q), tensor_desc(k), tensor_desc(v), tensor_desc(out["q8"], out["q_scale"]),
              tensor_desc(out["k8"], out["k_scale"]), tensor_desc(out["v8"], out["v_scale"])]
     _check(lib().flexattn_quantize_qkv(*[ctypes.byref(d) for d in descs], _stream(stream)))
+    if fresh:
+        _record(stream, *out.values())
     return out
 
 
@@ -355,6 +404,7 @@ def flexattn_quantize_qkv_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, 
     centering "k_mean" [B,Hkv,128] and "q_delta" [B,Hq,Lq] (float32)."""
     def blocks(t):
         return -(-t.shape[2] // qk_block)
+    fresh = out is None
     if out is None:
         out = {
             "q8": torch.empty(q.shape, dtype=torch.int8, device=q.device),
@@ -369,14 +419,17 @@ def flexattn_quantize_qkv_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, 
             out["q_delta"] = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     out["qk_block"] = qk_block
     ws_bytes = flexattn_quantize_qkv_ex_workspace_bytes(k.shape[0], k.shape[1], k.shape[2]) if center_k else 0
+    tmp = []
     if ws_bytes and workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+        tmp.append(workspace)
     descs = [tensor_desc(q), tensor_desc(k), tensor_desc(v), tensor_desc(out["q8"], out["q_scale"]),
              tensor_desc(out["k8"], out["k_scale"]), tensor_desc(out["v8"], out["v_scale"])]
     _check(lib().flexattn_quantize_qkv_ex(*[ctypes.byref(d) for d in descs], qk_block,
                                           _ptr(out.get("k_mean") if center_k else None),
                                           _ptr(out.get("q_delta") if center_k else None), _ptr(workspace),
                                           workspace.numel() if workspace is not None else 0, _stream(stream)))
+    _record(stream, *tmp, *(out.values() if fresh else ()))
     return out
 
 
@@ -385,16 +438,20 @@ def flexattn_fwd_quant(qz: dict, *, sm_scale: float = 0.0, out: Optional[torch.T
     """Quantized forward (flexattn_fwd_quant) on the dict returned by flexattn_quantize_qkv_ex
     (or flexattn_quantize_qkv, qk_block 128); returns (out bf16, lse)."""
     q8 = qz["q8"]
+    tmp = []
     if out is None:
         out = torch.empty(q8.shape, dtype=torch.bfloat16, device=q8.device)
+        tmp.append(out)
     if lse is None and return_lse:
         lse = torch.empty(q8.shape[:3], dtype=torch.float32, device=q8.device)
+        tmp.append(lse)
     tq, tk = tensor_desc(q8, qz["q_scale"]), tensor_desc(qz["k8"], qz["k_scale"])
     tv, to = tensor_desc(qz["v8"], qz["v_scale"]), tensor_desc(out)
     p = _params(sm_scale=sm_scale)
     _check(lib().flexattn_fwd_quant(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), qz.get("qk_block", 128),
                                     _ptr(qz.get("q_delta")), ctypes.byref(p), ctypes.byref(to), _ptr(lse),
                                     _stream(stream)))
+    _record(stream, *tmp)
     return out, lse
 
 
@@ -413,6 +470,10 @@ class BlockMaskTransposed:
         self.full_q_indices = torch.empty((self.Bm, self.Hm, self.n_kvb, self.n_qb), **z)
         self.col_order = torch.empty((self.Bm, self.Hm, self.n_kvb), **z) if col_order else None
 
+    def arrays(self):
+        return [t for t in (self.q_num_blocks, self.full_q_num_blocks, self.q_indices, self.full_q_indices,
+                            self.col_order) if t is not None]
+
     def as_struct(self) -> FaBlockMaskTransposed:
         return FaBlockMaskTransposed(self.Bm, self.Hm, self.q_len, self.kv_len, self.q_block, self.kv_block,
                                      self.n_qb, self.n_kvb, self.q_num_blocks.data_ptr(), self.q_indices.data_ptr(),
@@ -424,10 +485,13 @@ def flexattn_block_mask_transpose(block_mask: BlockMask, *, out: Optional[BlockM
                                   stream=None, col_order: bool = False) -> BlockMaskTransposed:
     """Column view of a device BlockMask (flexattn_block_mask_transpose); col_order=True (with
     out=None) also computes the column schedule."""
+    fresh = out is None
     if out is None:
         out = BlockMaskTransposed(block_mask, col_order=col_order)
     s, t = block_mask.as_struct(), out.as_struct()
     _check(lib().flexattn_block_mask_transpose(ctypes.byref(s), ctypes.byref(t), _stream(stream)))
+    if fresh:
+        _record(stream, *out.arrays())
     return out
 
 
@@ -443,18 +507,28 @@ def flexattn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.T
                  dq=None, dk=None, dv=None, dslopes=None, workspace: Optional[torch.Tensor] = None, stream=None):
     """Backward pass (flexattn_bwd); returns (dq, dk, dv, dslopes). The transposed BlockMask is built
     when a BlockMask is given without one; dslopes is computed when slope_grad is set (ALiBi)."""
+    tmp = []
     if block_mask is not None and block_mask_t is None:
         block_mask_t = flexattn_block_mask_transpose(block_mask, stream=stream)
-    dq = torch.empty(q.shape, dtype=q.dtype, device=q.device) if dq is None else dq
-    dk = torch.empty(k.shape, dtype=k.dtype, device=k.device) if dk is None else dk
-    dv = torch.empty(v.shape, dtype=v.dtype, device=v.device) if dv is None else dv
+        tmp += block_mask_t.arrays()
+    if dq is None:
+        dq = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+        tmp.append(dq)
+    if dk is None:
+        dk = torch.empty(k.shape, dtype=k.dtype, device=k.device)
+        tmp.append(dk)
+    if dv is None:
+        dv = torch.empty(v.shape, dtype=v.dtype, device=v.device)
+        tmp.append(dv)
     if slope_grad and dslopes is None:
         dslopes = torch.empty(q.shape[1], dtype=torch.float32, device=q.device)
+        tmp.append(dslopes)
     if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != tuple(q.shape[:3]):
         raise ValueError("lse must be a contiguous float32 [B, Hq, Lq] tensor")
     ws_bytes = flexattn_bwd_workspace_bytes(q.shape[0], q.shape[1], q.shape[2])
     if ws_bytes and workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+        tmp.append(workspace)
     descs = [tensor_desc(t) for t in (q, k, v, out, dout, dq, dk, dv)]
     p = _params(window=window, prefix_len=prefix_len, softcap=softcap, alibi_slopes=alibi_slopes,
                 q_doc=q_doc, kv_doc=kv_doc, sm_scale=sm_scale)
@@ -464,4 +538,5 @@ def flexattn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.T
                               ctypes.byref(p), *[ctypes.byref(d) for d in descs[5:]], _ptr(dslopes),
                               _ptr(workspace), workspace.numel() if workspace is not None else 0,
                               _stream(stream)))
+    _record(stream, *tmp)
     return dq, dk, dv, dslopes

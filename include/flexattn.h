@@ -21,6 +21,12 @@
  *   - Device pointers must point into memory of the current HIP device.
  *   - On any status other than FA_OK nothing has been enqueued and no output has been written;
  *     flexattn_last_error() gives the reason. There is no silent fallback path.
+ *   - The kernels are built for gfx950 (MI355X) only. Every entry point that enqueues work checks,
+ *     after validating its arguments, that the current device is a gfx950 and otherwise returns
+ *     FA_ERR_UNSUPPORTED naming the device's architecture (the FlashRT PR's convention that an
+ *     unserved site is refused with its reason). The name is read once per device. The
+ *     environment variable FLEXATTN_DEVICE_ARCH, when set, stands in for the device's name (it
+ *     exists so that the refusal can be tested on a machine without the device).
  *   - Calls are thread safe; calls that overlap on the same output buffers race.
  */
 #ifndef FLEXATTN_H
@@ -113,6 +119,12 @@ typedef struct {
   int32_t* row_order;
 } fa_block_mask;
 
+/* Bytes of all four BlockMask arrays together (two count arrays and two index arrays, int32)
+ * for the given dimensions; 0 on invalid dimensions. The optional row_order adds one count
+ * array's bytes. (The FlashRT PR's caller-owned workspace convention: the caller sizes and owns
+ * every buffer once per bound shape.) */
+size_t flexattn_block_mask_bytes(int Bm, int Hm, int q_len, int kv_len, int q_block, int kv_block);
+
 /* Bytes of ONE index array ([Bm][Hm][n_qb][n_kvb] int32) and of ONE count array
  * ([Bm][Hm][n_qb] int32) for the given dimensions; 0 on invalid dimensions. */
 size_t flexattn_block_mask_index_bytes(int Bm, int Hm, int q_len, int kv_len, int q_block, int kv_block);
@@ -185,6 +197,13 @@ fa_status flexattn_quantize_qkv_ex(const fa_tensor* q, const fa_tensor* k, const
  * and q_delta NULL). */
 fa_status flexattn_fwd_quant(const fa_tensor* q8, const fa_tensor* k8, const fa_tensor* v8, int qk_block,
                              const float* q_delta, const fa_params* p, fa_tensor* out, float* lse, hipStream_t stream);
+
+/* Device scratch of flexattn_fwd for the given operands: always 0. Every forward form (bf16, fp32,
+ * quantized) keeps its scores, probabilities and running softmax state in registers and LDS
+ * (FlexAttention guide, "Fused Triton JIT Kernel Compilation", item 3: intermediates stay on
+ * chip), so flexattn_fwd takes no workspace argument. Kept so that a caller following the
+ * caller-owned-workspace convention can size every call alike. */
+size_t flexattn_fwd_workspace_bytes(const fa_tensor* q, const fa_tensor* k, int mask_kind, int score_kind);
 
 /* Forward pass. q [B][Hq][Lq][D], k and v [B][Hkv][Lkv][D], out [B][Hq][Lq][D],
  * lse [B][Hq][Lq] float32 contiguous (natural log; may be NULL). Supported envelope:

@@ -280,3 +280,102 @@ def test_transpose_validation():
     for bad, needle in ((_bmt(Lq=101), "dimensions"), (_bmt(ptr=None), "NULL")):
         st = lib.flexattn_block_mask_transpose(ctypes.byref(bm), ctypes.byref(bad), None)
         assert st == fa.FA_ERR_INVALID_ARG and needle in fa.flexattn_last_error(), fa.flexattn_last_error()
+
+
+def test_block_mask_and_fwd_workspace_sizes():
+    # All four arrays: two counts [Bm][Hm][n_qb] and two index arrays [Bm][Hm][n_qb][n_kvb], int32.
+    assert fa.flexattn_block_mask_bytes(2, 1, 300, 200, 128, 64) == 2 * (2 * 3 * 4 * 4) + 2 * (2 * 3 * 4)
+    assert fa.flexattn_block_mask_bytes(1, 1, 134_449, 134_449, 128, 64) == \
+        2 * fa.flexattn_block_mask_index_bytes(1, 1, 134_449, 134_449, 128, 64) + \
+        2 * fa.flexattn_block_mask_count_bytes(1, 1, 134_449, 128)
+    assert fa.flexattn_block_mask_bytes(0, 1, 10, 10, 128, 128) == 0
+    assert fa.flexattn_block_mask_bytes(1, 1, 10, 10, 0, 128) == 0
+    assert fa.flexattn_block_mask_bytes(1, 1, 0, 10, 128, 128) == 0   # no query block, no entry
+    # The forward keeps every intermediate on chip: it needs no workspace in any form.
+    lib = fa.lib()
+    for dt in (fa.FA_BF16, fa.FA_F32, fa.FA_I8):
+        q = _t(dtype=dt)
+        for mask, score in ((0, 0), (fa.FA_MASK_DOC | fa.FA_MASK_CAUSAL, fa.FA_SCORE_SOFTCAP)):
+            assert lib.flexattn_fwd_workspace_bytes(ctypes.byref(q), ctypes.byref(q), mask, score) == 0
+
+
+def _arch_calls():
+    """One argument-valid call of every entry point that enqueues work (fake, aligned device
+    addresses: the calls are refused before any HIP call)."""
+    lib = fa.lib()
+    p = FaParams(0.0, 0, 0, 0.0, None, None, None)
+    t = _t()
+    q8 = FaTensor(256, fa.FA_I8, 1, 2, 100, 128, 2 * 100 * 128, 100 * 128, 128, 512)
+    k8 = FaTensor(256, fa.FA_I8, 1, 2, 100, 128, 2 * 100 * 128, 100 * 128, 128, 512)
+    v8 = FaTensor(256, fa.FA_FP8_E4M3, 1, 2, 100, 128, 2 * 100 * 128, 100 * 128, 128, 512)
+    bm, bmt = _bm(), _bmt()
+    r = lambda x: ctypes.byref(x)
+    need_kv = lib.flexattn_fwd_splitkv_workspace_bytes(1, 2, 100, 4)
+    need_b = lib.flexattn_bwd_workspace_bytes(1, 2, 100)
+    return {
+        "block_mask_build": lambda: lib.flexattn_block_mask_build(fa.FA_MASK_CAUSAL, r(p), 1, 100, 100, r(bm), None, 0,
+                                                                  None),
+        "fwd": lambda: lib.flexattn_fwd(r(t), r(t), r(t), r(bm), fa.FA_MASK_CAUSAL, 0, r(p), r(t), None, None),
+        "fwd_nomask": lambda: lib.flexattn_fwd(r(t), r(t), r(t), None, 0, 0, r(p), r(t), 8192, None),
+        "fwd_splitkv": lambda: lib.flexattn_fwd_splitkv(r(t), r(t), r(t), None, 0, 0, r(p), r(t), None, 4, 4096,
+                                                        need_kv, None),
+        "fwd_quantized": lambda: lib.flexattn_fwd(r(q8), r(k8), r(v8), None, 0, 0, r(p), r(t), None, None),
+        "fwd_quant": lambda: lib.flexattn_fwd_quant(r(q8), r(k8), r(v8), 32, None, r(p), r(t), None, None),
+        "quantize_qkv": lambda: lib.flexattn_quantize_qkv(r(t), r(t), r(t), r(q8), r(k8), r(v8), None),
+        "quantize_qkv_ex": lambda: lib.flexattn_quantize_qkv_ex(r(t), r(t), r(t), r(q8), r(k8), r(v8), 128, None,
+                                                                None, None, 0, None),
+        "block_mask_transpose": lambda: lib.flexattn_block_mask_transpose(r(bm), r(bmt), None),
+        "bwd": lambda: lib.flexattn_bwd(r(t), r(t), r(t), r(t), r(t), 8192, r(bm), r(bmt), fa.FA_MASK_CAUSAL, 0,
+                                        r(p), r(t), r(t), r(t), None, 4096, need_b, None),
+    }
+
+
+@pytest.mark.parametrize("arch", ["gfx942:sramecc+:xnack-", "gfx90a", "gfx9500", "gfx95"])
+@pytest.mark.parametrize("entry", sorted(_arch_calls()))
+def test_non_gfx950_device_is_refused(monkeypatch, arch, entry):
+    """Every entry point that enqueues work refuses another architecture with FA_ERR_UNSUPPORTED,
+    naming it, after validating its arguments and before any HIP call (the device name is
+    injected through FLEXATTN_DEVICE_ARCH)."""
+    monkeypatch.setenv("FLEXATTN_DEVICE_ARCH", arch)
+    st = _arch_calls()[entry]()
+    assert st == fa.FA_ERR_UNSUPPORTED, (st, fa.flexattn_last_error())
+    msg = fa.flexattn_last_error()
+    assert arch in msg and "gfx950" in msg, msg
+    # Invalid arguments still take precedence (validation first).
+    lib = fa.lib()
+    st = lib.flexattn_fwd(None, None, None, None, 0, 0, None, None, None, None)
+    assert st == fa.FA_ERR_INVALID_ARG
+
+
+def test_blockmask_clamp_helpers(tmp_path):
+    """The clamps the kernels apply to caller-provided BlockMask counts and entries (host build of
+    the shared header, with address and undefined-behaviour sanitizers)."""
+    import shutil
+    cxx = shutil.which("g++")
+    if cxx is None:
+        pytest.skip("no host C++ compiler")
+    src = tmp_path / "clamp.cpp"
+    src.write_text(r'''
+#include "tile_class.h"
+#include <cstdio>
+#include <climits>
+int main() {
+  int bad = 0;
+  const int cnt[][3] = {{-5, 7, 0}, {0, 7, 0}, {3, 7, 3}, {7, 7, 7}, {8, 7, 7}, {INT_MIN, 7, 0}, {INT_MAX, 7, 7},
+                        {5, 0, 0}};
+  for (auto& c : cnt) bad += fa::clamp_count(c[0], c[1]) != c[2];
+  const int blk[][3] = {{-1, 10, 10}, {0, 10, 0}, {9, 10, 9}, {10, 10, 10}, {INT_MIN, 10, 10}, {INT_MAX, 10, 10},
+                        {0, 0, 0}};
+  for (auto& b : blk) bad += fa::sanitize_block(b[0], b[1]) != b[2];
+  std::printf("%d\n", bad);
+  return bad != 0;
+}
+''')
+    exe = tmp_path / "clamp"
+    r = subprocess.run([cxx, "-std=c++17", "-O1", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+                        "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include", "-I" + os.path.join(ROOT, "include"),
+                        "-I" + os.path.join(ROOT, "block_sparse_masked_blockmask_amd", "csrc"), str(src), "-o", str(exe)],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, env=dict(os.environ, ASAN_OPTIONS="detect_leaks=0"))
+    assert r.returncode == 0 and r.stdout.strip() == "0", r.stdout + r.stderr
