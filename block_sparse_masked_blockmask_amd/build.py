@@ -58,5 +58,53 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# Host sources of the C-ABI layer (argument validation, the host BlockMask builder): the part a
+# sanitized build instruments.
+HOST_SOURCES = ["api.cpp"]
+SANITIZED_LIB = os.path.join(ROOT, "_build", "sanitized", "libflexattn_sanitized.so")
+
+
+def build_sanitized() -> str:
+    """Build the C-ABI layer with AddressSanitizer and UndefinedBehaviorSanitizer on its host code
+    only (-Xarch_host: the GPU code is not instrumented), linked against the regular library for
+    the kernel launchers. For the CPU tests of the host logic; load it with the sanitizer runtime
+    preloaded (sanitizer_runtime()) and FLEXATTN_LIBRARY pointing at it. Returns its path."""
+    if not os.path.exists(LIB):
+        build()
+    outdir = os.path.dirname(SANITIZED_LIB)
+    os.makedirs(outdir, exist_ok=True)
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+    objs = []
+    for src in HOST_SOURCES:
+        obj = os.path.join(outdir, src + ".o")
+        cmd = [HIPCC, *[f for f in FLAGS if f != "-O3"], "-O1", *san, "-c", os.path.join(CSRC, src), "-o", obj]
+        if src.endswith(".cpp"):
+            cmd[1:1] = ["-x", "hip"]
+        r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+        if r.returncode != 0:
+            raise RuntimeError(f"sanitized build of {src} failed:\n" + r.stdout.decode(errors="replace"))
+        objs.append(obj)
+    tmp = SANITIZED_LIB + ".tmp"
+    link = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *san, "-shared-libasan", "-o", tmp, *objs,
+            "-L" + HERE, "-l:libflexattn.so", "-Wl,-rpath," + HERE]
+    r = subprocess.run(link, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+    if r.returncode != 0:
+        raise RuntimeError("sanitized link failed:\n" + r.stdout.decode(errors="replace"))
+    os.replace(tmp, SANITIZED_LIB)
+    return SANITIZED_LIB
+
+
+def sanitizer_runtime() -> str:
+    """Path of the compiler's shared AddressSanitizer runtime (to preload into the test process)."""
+    out = subprocess.run([HIPCC, "-print-file-name=libclang_rt.asan-x86_64.so"], stdout=subprocess.PIPE,
+                         stderr=subprocess.DEVNULL).stdout.decode().strip()
+    if not out or not os.path.isabs(out) or not os.path.exists(out):
+        import glob
+        cands = glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so")
+        out = cands[0] if cands else ""
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))

@@ -81,6 +81,57 @@ fa_status check_device() {
   return FA_OK;
 }
 
+// FLEXATTN_VERIFY_BLOCKMASK (debug): when set to a non-empty value other than "0", the forward
+// and the backward copy the BlockMask lists they are given to the host, synchronising the
+// stream, and check them before enqueuing anything: every count in [0, n], every listed block in
+// [0, n) and strictly ascending, no block both full and partial in one row. A violation is
+// FA_ERR_INVALID_ARG naming the row. The kernels themselves clamp counts and skip entries out of
+// range (so that a corrupt BlockMask cannot send them outside its arrays), which hides such
+// errors; this mode shows them. It synchronises the host, so it is not for graph capture.
+bool verify_enabled() {
+  const char* v = std::getenv("FLEXATTN_VERIFY_BLOCKMASK");
+  return v != nullptr && *v != '\0' && std::strcmp(v, "0") != 0;
+}
+
+// rows lists of up to n entries (full and partial), counts [rows], indices [rows][n].
+fa_status verify_lists(const int32_t* full_num, const int32_t* full_idx, const int32_t* part_num,
+                       const int32_t* part_idx, int64_t rows, int n, const char* what, hipStream_t stream) {
+  if (rows <= 0 || n <= 0) return FA_OK;
+  std::vector<int32_t> fn(rows), pn(rows), fi((size_t)rows * n), pi((size_t)rows * n);
+  hipError_t e = hipSuccess;
+  const size_t cb = (size_t)rows * sizeof(int32_t), ib = (size_t)rows * n * sizeof(int32_t);
+  if (e == hipSuccess) e = hipMemcpyAsync(fn.data(), full_num, cb, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipMemcpyAsync(pn.data(), part_num, cb, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipMemcpyAsync(fi.data(), full_idx, ib, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipMemcpyAsync(pi.data(), part_idx, ib, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return fail(FA_ERR_DEVICE, "%s verification copy failed: %s", what, hipGetErrorString(e));
+  std::vector<unsigned char> seen(n);
+  for (int64_t r = 0; r < rows; ++r) {
+    if (fn[r] < 0 || fn[r] > n || pn[r] < 0 || pn[r] > n)
+      return fail(FA_ERR_INVALID_ARG, "%s row %lld: counts %d full, %d partial outside [0, %d]", what, (long long)r,
+                  fn[r], pn[r], n);
+    std::fill(seen.begin(), seen.end(), 0);
+    for (int list = 0; list < 2; ++list) {
+      const int32_t* idx = (list ? pi.data() : fi.data()) + (size_t)r * n;
+      const int cnt = list ? pn[r] : fn[r];
+      for (int i = 0; i < cnt; ++i) {
+        if (idx[i] < 0 || idx[i] >= n)
+          return fail(FA_ERR_INVALID_ARG, "%s row %lld: %s entry %d is %d, outside [0, %d)", what, (long long)r,
+                      list ? "partial" : "full", i, idx[i], n);
+        if (i > 0 && idx[i] <= idx[i - 1])
+          return fail(FA_ERR_INVALID_ARG, "%s row %lld: %s list not strictly ascending at entry %d", what,
+                      (long long)r, list ? "partial" : "full", i);
+        if (seen[idx[i]])
+          return fail(FA_ERR_INVALID_ARG, "%s row %lld: block %d is listed both full and partial", what,
+                      (long long)r, idx[i]);
+        seen[idx[i]] = 1;
+      }
+    }
+  }
+  return FA_OK;
+}
+
 // Checks shared by the builder and the forward pass for the mask parameters.
 fa_status check_mask(int mask_kind, const fa_params* p, int Lq, int Lkv) {
   if (mask_kind & ~kValidMask) return fail(FA_ERR_INVALID_ARG, "unknown mask_kind bits 0x%x", mask_kind);
@@ -394,6 +445,11 @@ fa_status fwd_impl(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, c
     a.kv_idx = bm->kv_indices;
     a.full_num = bm->full_kv_num_blocks;
     a.full_idx = bm->full_kv_indices;
+    if (verify_enabled()) {
+      st = verify_lists(bm->full_kv_num_blocks, bm->full_kv_indices, bm->kv_num_blocks, bm->kv_indices,
+                        (int64_t)bm->Bm * bm->Hm * bm->n_qb, bm->n_kvb, "BlockMask", stream);
+      if (st != FA_OK) return st;
+    }
   }
   if (nsplit > 1) {
     if (dt != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "split-KV serves bf16 tensors");
@@ -751,6 +807,14 @@ fa_status flexattn_bwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* 
     a.q_idx = bmt->q_indices;
     a.fullq_num = bmt->full_q_num_blocks;
     a.fullq_idx = bmt->full_q_indices;
+    if (verify_enabled()) {
+      if ((st = verify_lists(bm->full_kv_num_blocks, bm->full_kv_indices, bm->kv_num_blocks, bm->kv_indices,
+                             (int64_t)bm->Bm * bm->Hm * nqb, nkvb, "BlockMask", stream)) != FA_OK)
+        return st;
+      if ((st = verify_lists(bmt->full_q_num_blocks, bmt->full_q_indices, bmt->q_num_blocks, bmt->q_indices,
+                             (int64_t)bmt->Bm * bmt->Hm * nkvb, nqb, "transposed BlockMask", stream)) != FA_OK)
+        return st;
+    }
   }
   const size_t need = flexattn_bwd_workspace_bytes(B, Hq, Lq);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need))

@@ -14,7 +14,10 @@ from typing import Optional
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libflexattn.so")
+# FLEXATTN_LIBRARY selects another build of the same library (the tests load an
+# address/undefined-behaviour-sanitized build of the host-side layer this way).
+LIB_PATH = os.environ.get("FLEXATTN_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                               "libflexattn.so")
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_DEVICE = 0, 1, 2, 3
 FA_F32, FA_BF16, FA_I8, FA_FP8_E4M3 = 0, 1, 2, 3
