@@ -9,7 +9,8 @@ from .flexattn import (  # noqa: F401
     FA_SCORE_ALIBI, FA_SCORE_NONE, FA_SCORE_SOFTCAP,
     FA_OK, FA_ERR_DEVICE, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED,
     BlockMask, BlockMaskTransposed, FlexAttnError, LIB_PATH, block_mask_all_partial,
-    flexattn_block_mask_build, flexattn_block_mask_build_host, flexattn_block_mask_bytes,
+    flexattn_block_mask_build, flexattn_block_mask_build_host, flexattn_block_mask_build_noalloc,
+    flexattn_block_mask_bytes, flexattn_block_mask_noalloc_max_bytes,
     flexattn_block_mask_count_bytes, flexattn_fwd_workspace_bytes,
     flexattn_block_mask_index_bytes, flexattn_block_mask_transpose, flexattn_bwd, flexattn_bwd_workspace_bytes,
     flexattn_block_mask_workspace_bytes, flexattn_fwd, flexattn_fwd_splitkv, flexattn_fwd_splitkv_workspace_bytes,

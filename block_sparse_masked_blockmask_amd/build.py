@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libflexattn.so")
-SOURCES = ["api.cpp", "blockmask.hip", "fwd.hip", "quant.hip", "bwd.hip"]
+SOURCES = ["api.cpp", "blockmask.hip", "fwd.hip", "quant.hip", "bwd.hip", "noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -58,9 +58,9 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
-# Host sources of the C-ABI layer (argument validation, the host BlockMask builder): the part a
-# sanitized build instruments.
-HOST_SOURCES = ["api.cpp"]
+# Host sources of the C-ABI layer (argument validation, the host BlockMask builder, the
+# allocation-free entry point's bookkeeping): the part a sanitized build instruments.
+HOST_SOURCES = ["api.cpp", "noalloc.hip"]
 SANITIZED_LIB = os.path.join(ROOT, "_build", "sanitized", "libflexattn_sanitized.so")
 
 

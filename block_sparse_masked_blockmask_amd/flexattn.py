@@ -83,6 +83,11 @@ def lib() -> ctypes.CDLL:
         L.flexattn_block_mask_build.argtypes = [c_int, POINTER(FaParams), c_int, c_int, c_int,
                                                 POINTER(FaBlockMask), c_void_p, c_size_t, c_void_p]
         L.flexattn_block_mask_build.restype = c_int
+        L.flexattn_block_mask_noalloc_max_bytes.argtypes = []
+        L.flexattn_block_mask_noalloc_max_bytes.restype = c_size_t
+        L.flexattn_block_mask_build_noalloc.argtypes = [c_int, POINTER(FaParams), c_int, c_int, c_int,
+                                                        POINTER(FaBlockMask), c_void_p]
+        L.flexattn_block_mask_build_noalloc.restype = c_int
         L.flexattn_block_mask_build_host.argtypes = [c_int, POINTER(FaParams), c_int, c_int, c_int,
                                                      POINTER(FaBlockMask)]
         L.flexattn_block_mask_build_host.restype = c_int
@@ -267,6 +272,22 @@ def flexattn_block_mask_build(mask_kind: int, B: int, q_len: int, kv_len: int, q
                                            _ptr(workspace), workspace.numel() if workspace is not None else 0,
                                            _stream(stream)))
     _record(stream, *tmp)
+    return out
+
+
+def flexattn_block_mask_noalloc_max_bytes() -> int:
+    return lib().flexattn_block_mask_noalloc_max_bytes()
+
+
+def flexattn_block_mask_build_noalloc(mask_kind: int, B: int, q_len: int, kv_len: int, out: BlockMask, *,
+                                      q_doc=None, kv_doc=None, window: int = 0, prefix_len: int = 0,
+                                      stream=None) -> BlockMask:
+    """Build a BlockMask into the caller's `out` with the allocation-free entry point (its scratch
+    is a static device array; nothing is allocated by the library or here)."""
+    p = _params(window=window, prefix_len=prefix_len, q_doc=q_doc, kv_doc=kv_doc)
+    s = out.as_struct()
+    _check(lib().flexattn_block_mask_build_noalloc(mask_kind, ctypes.byref(p), B, q_len, kv_len, ctypes.byref(s),
+                                                   _stream(stream)))
     return out
 
 

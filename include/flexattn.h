@@ -149,6 +149,20 @@ fa_status flexattn_block_mask_build(int mask_kind, const fa_params* p, int B, in
                                     fa_block_mask* out, void* workspace, size_t workspace_bytes,
                                     hipStream_t stream);
 
+/* Allocation-free variant of flexattn_block_mask_build, for callers that cannot allocate device
+ * memory or pass a workspace: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc. Arguments, validation, kernels and results are those of
+ * flexattn_block_mask_build; the builder's scratch (the per-block document-id summaries, 16 bytes
+ * per query block and per kv block and batch, DOC only) comes from a static device array of
+ * flexattn_block_mask_noalloc_max_bytes() bytes (1 MiB) that each device holds for the life of the
+ * process. A request needing more is refused with FA_ERR_UNSUPPORTED before anything is enqueued.
+ * The call allocates nothing (no hipMalloc, no allocating library call). Calls that overlap on
+ * one device share the array and race; the caller orders them (one stream, or events). Nothing in
+ * the array needs to start at zero: every summary is written before it is read. */
+size_t flexattn_block_mask_noalloc_max_bytes(void);
+fa_status flexattn_block_mask_build_noalloc(int mask_kind, const fa_params* p, int B, int q_len, int kv_len,
+                                            fa_block_mask* out, hipStream_t stream);
+
 /* The same BlockMask built on the host, on the calling thread: p->q_doc / p->kv_doc (DOC) and the
  * four arrays of `out` are host memory; no workspace, no stream. Validation, block sizes and
  * results are those of flexattn_block_mask_build (exact classification; the two builders share

@@ -1,7 +1,7 @@
-"""CPU: the host-side layer of the C ABI (argument validation, the host BlockMask builder) under
-AddressSanitizer and UndefinedBehaviorSanitizer.
+"""CPU: the host-side layer of the C ABI (argument validation, the host BlockMask builder, the
+allocation-free entry point's bookkeeping) under AddressSanitizer and UndefinedBehaviorSanitizer.
 
-The sanitized build instruments api.cpp on the host only and takes the kernel
+The sanitized build instruments api.cpp and noalloc.hip on the host only and takes the kernel
 launchers from the regular library. The host-logic tests (test_abi_cpu.py and
 test_host_blockmask.py) run in a child process with the sanitizer runtime preloaded and
 FLEXATTN_LIBRARY pointing at the sanitized build; any report fails the run.
