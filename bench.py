@@ -40,6 +40,7 @@ BF16_PEAK_TFLOPS = 2516.6
 FP32_PEAK_TFLOPS = 157.3
 INT8_FP8_PEAK_TOPS = 5033.2  # dense int8 / fp8 MFMA (2x bf16)
 KERNEL_SOURCES = ["block_sparse_masked_blockmask_amd/csrc/fwd.hip",
+                  "block_sparse_masked_blockmask_amd/csrc/fwd_dense.hip",
                   "block_sparse_masked_blockmask_amd/csrc/quant.hip",
                   "block_sparse_masked_blockmask_amd/csrc/device_common.h",
                   "block_sparse_masked_blockmask_amd/csrc/tile_class.h"]

@@ -411,11 +411,13 @@ fa_status fwd_impl(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, c
 
   const int B = q->B, Lq = q->L, Lkv = k->L;
   int kv_block = 128, q_block = 128;
+  bool dense = false;
   fa::FwdArgs a{};
   if (bm == nullptr) {
     if (mask_kind != FA_MASK_NONE) return fail(FA_ERR_INVALID_ARG, "a BlockMask is required unless mask_kind is NONE");
-    // 256-query workgroups (bf16) once they still give at least one per CU.
-    if (dt == FA_BF16 && nsplit == 1 && (int64_t)B * q->H * cdiv(Lq, 256) >= 256) q_block = 256;
+    // bf16 without a BlockMask runs the software-pipelined every-tile-full kernel (128-query
+    // workgroups).
+    dense = dt == FA_BF16 && nsplit == 1;
     a.all_full = 1;
     a.Bm = a.Hm = 1;
     a.nqb = cdiv(Lq, q_block);
@@ -500,7 +502,8 @@ fa_status fwd_impl(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, c
     a.part_o = static_cast<float*>(workspace);
     a.part_lse = a.part_o + (size_t)nsplit * B * q->H * Lq * 128;
   }
-  hipError_t e = fa::launch_fwd(a, dt == FA_BF16 ? 1 : 0, q_block, kv_block, score_kind, stream);
+  hipError_t e = dense ? fa::launch_fwd_dense(a, score_kind, stream)
+                       : fa::launch_fwd(a, dt == FA_BF16 ? 1 : 0, q_block, kv_block, score_kind, stream);
   if (e != hipSuccess) return fail(FA_ERR_DEVICE, "forward launch failed: %s", hipGetErrorString(e));
   if (nsplit > 1) {
     fa::MergeArgs m{};

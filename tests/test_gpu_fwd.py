@@ -110,6 +110,32 @@ def test_null_block_mask_dense(dtype):
     check_close(out.float().cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref, dtype, "null bm")
 
 
+@pytest.mark.parametrize("Lkv", [1, 40, 64, 65, 128, 129, 191, 192, 257, 1000])
+@pytest.mark.parametrize("si", range(len(SCORES)))
+def test_null_block_mask_bf16_pipelined(Lkv, si):
+    """bf16 without a BlockMask runs the software-pipelined every-tile-full kernel: one, two, three
+    and many 64-key steps, exact and ragged last steps, every score transform, GQA 6:2, B = 2."""
+    kw = dict(SCORES[si])
+    w = random_case(5000 + 7 * Lkv + si, dtype="bf16", B=2, Hq=6, Hkv=2, Lq=150, Lkv=Lkv, **kw)
+    out, lse, _ = run_gpu(w, use_bm=False)
+    qf, kf, vf = w.qkv_f32()
+    o_ref, l_ref = ref_attn.attention(qf, kf, vf, spec_of(w))
+    check_close(out.float().cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref, "bf16", f"null bm Lkv {Lkv} score {si}")
+
+
+def test_null_block_mask_bf16_strided_and_scale():
+    import torch
+    fa = _fa()
+    w = random_case(5100, dtype="bf16", B=2, Hq=4, Lq=333, Lkv=333)
+    dev = torch.device("cuda", 0)
+    q, k, v = (to_device(x, "bf16", dev).transpose(1, 2).contiguous().transpose(1, 2) for x in (w.q, w.k, w.v))
+    out, lse = fa.flexattn_fwd(q, k, v, None, fa.FA_MASK_NONE, sm_scale=0.03)
+    torch.cuda.synchronize()
+    qf, kf, vf = w.qkv_f32()
+    o_ref, l_ref = ref_attn.attention(qf, kf, vf, dict(sm_scale=0.03))
+    check_close(out.float().cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref, "bf16", "null bm strided")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_fully_masked_rows_and_empty_rows(dtype):
     # Unsorted document ids with query ids absent from the keys: those rows have no allowed
