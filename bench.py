@@ -332,7 +332,10 @@ class Case:
     def kernel_name(self) -> str:
         if self.quantized:
             return "fwd_quant_kernel"
-        return "fwd_bf16_kernel" if self.w.dtype == "bf16" else "fwd_f32_kernel"
+        if self.w.dtype != "bf16":
+            return "fwd_f32_kernel"
+        # bf16 without a BlockMask runs the software-pipelined every-tile-full kernel.
+        return "fwd_bf16_kernel" if self.bm is not None else "fwd_bf16_dense_kernel"
 
     def flops(self) -> float:
         return 4.0 * self.w.D * allowed_pairs(self.w) * self.w.Hq

@@ -415,9 +415,10 @@ fa_status fwd_impl(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, c
   fa::FwdArgs a{};
   if (bm == nullptr) {
     if (mask_kind != FA_MASK_NONE) return fail(FA_ERR_INVALID_ARG, "a BlockMask is required unless mask_kind is NONE");
-    // bf16 without a BlockMask runs the software-pipelined every-tile-full kernel (128-query
+    // bf16 without a BlockMask runs the software-pipelined every-tile-full kernel (256-query
     // workgroups).
     dense = dt == FA_BF16 && nsplit == 1;
+    if (dense) q_block = 256;
     a.all_full = 1;
     a.Bm = a.Hm = 1;
     a.nqb = cdiv(Lq, q_block);

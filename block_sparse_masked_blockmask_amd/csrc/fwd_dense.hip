@@ -16,11 +16,12 @@
 // bf16 packing), then the 16 products of O += V(n)^T P(n). The row maximum of S(n) and the lazy
 // rescale come first in the iteration; the scores alternate between two register tiles.
 //
-// A workgroup is 4 waves (128 queries), two workgroups per CU. LDS: K slots for K(n+1) and K(n+2),
-// V slots for V(n) and V(n+1), 16 KB each (64 KB per workgroup): iteration n waits for K(n+1) and
-// V(n), passes one barrier, and refills the slots last read in iteration n-1. Each slot is an array
-// of its own, named at compile time, so that the compiler waits for a transfer only before reading
-// the slot it fills.
+// A workgroup is 8 waves (256 queries), one per CU at two waves per SIMD: the 8 waves share each
+// K and V tile, which halves the L2-to-LDS traffic of two 4-wave workgroups (measured 5% faster).
+// LDS: K slots for K(n+1) and K(n+2), V slots for V(n) and V(n+1), 16 KB each: iteration n waits
+// for K(n+1) and V(n), passes one barrier, and refills the slots last read in iteration n-1. Each
+// slot is an array of its own, named at compile time, so that the compiler waits for a transfer
+// only before reading the slot it fills.
 #include <hip/hip_runtime.h>
 
 #include <climits>
@@ -81,24 +82,25 @@ __device__ __forceinline__ float dscore(const FwdArgs& a, float acc, int qi, int
   }
 }
 
-// One step's K or V tile: 16 one-KB segments (4 rows each); wave w issues segments 4 i + w (rows
-// 16 i + 4 w + lane / 16). Rows past the last key are clamped to it (finite data, masked).
+// One step's K or V tile: 16 one-KB segments (4 rows each); wave w issues segments 8 i + w.
+// Rows past the last key are clamped to it (finite data, masked).
 template <bool K_SIDE>
 __device__ __forceinline__ void issue_tile(const FwdArgs& a, const DLane& c, int kv0, unsigned char* dst) {
-  const __bf16* base = K_SIDE ? c.kp : c.vp;
+  // The tile's first row is a uniform address; each lane adds a 32-bit byte offset.
   const int64_t sl = K_SIDE ? a.k_sl : a.v_sl;
+  const char* base = (const char*)(K_SIDE ? c.kp : c.vp) + (int64_t)kv0 * sl * 2;
   if (kv0 + kDStep <= a.Lkv) {
-    const int off = K_SIDE ? c.koff : c.voff;
+    const unsigned off = (unsigned)(K_SIDE ? c.koff : c.voff) * 2u;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ddma16(base + (int64_t)(kv0 + 16 * i) * sl + off, dst + (4 * i + c.wave) * 1024);
+    for (int i = 0; i < 2; ++i) ddma16(base + (int64_t)(32 * i) * sl * 2 + off, dst + (8 * i + c.wave) * 1024);
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int seg = 4 * i + c.wave;
+    for (int i = 0; i < 2; ++i) {
+      const int seg = 8 * i + c.wave;
       const int r = seg * 4 + (c.lane >> 4);
       const int ch = (c.lane & 15) ^ swz(r);
-      const int64_t kv = min(kv0 + r, a.Lkv - 1);
-      ddma16(base + kv * sl + ch * 8, dst + seg * 1024);
+      const int kr = min(kv0 + r, a.Lkv - 1) - kv0;
+      ddma16(base + (unsigned)(kr * (int)sl * 2 + ch * 16), dst + seg * 1024);
     }
   }
 }
@@ -266,7 +268,7 @@ __device__ __forceinline__ void dense_step(const FwdArgs& a, const DLane& c, con
 }  // namespace
 
 template <int SCORE>
-__global__ __launch_bounds__(256, 2) void fwd_bf16_dense_kernel(FwdArgs a) {
+__global__ __launch_bounds__(512, 1) void fwd_bf16_dense_kernel(FwdArgs a) {
   // Work order (as the block-sparse kernel without a schedule): each XCD takes a contiguous
   // range of work items; query heads of one kv head fastest, then query blocks from the last,
   // then the (batch, kv head) pairs, permuted so that every XCD mixes batches.
@@ -294,7 +296,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_dense_kernel(FwdArgs a) {
   c.lane = threadIdx.x & 63;
   c.hl = c.lane >> 5;
   c.lq = c.lane & 31;
-  c.qi = qb * 128 + c.wave * 32 + c.lq;
+  c.qi = qb * 256 + c.wave * 32 + c.lq;
   c.q_in = c.qi < a.Lq;
   c.kp = (const __bf16*)a.k + b * a.k_sb + hkv * a.k_sh;
   c.vp = (const __bf16*)a.v + b * a.v_sb + hkv * a.v_sh;
@@ -388,7 +390,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_dense_kernel(FwdArgs a) {
 
 hipError_t launch_fwd_dense(const FwdArgs& a, int score, hipStream_t stream) {
   if (a.total_wg == 0) return hipSuccess;
-  const dim3 grid(a.total_wg), block(256);
+  const dim3 grid(a.total_wg), block(512);
   switch (score) {
     case 0: hipLaunchKernelGGL((fwd_bf16_dense_kernel<0>), grid, block, 0, stream, a); break;
     case FA_SCORE_ALIBI: hipLaunchKernelGGL((fwd_bf16_dense_kernel<FA_SCORE_ALIBI>), grid, block, 0, stream, a); break;
