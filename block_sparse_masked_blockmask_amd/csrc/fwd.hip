@@ -150,6 +150,17 @@ __device__ __forceinline__ float score_log2(const FwdArgs& a, float acc, int qi,
   }
 }
 
+// Soft-cap only: the reciprocal r = 1 / (1 + 2^u) of score_log2, which gives the logit as
+// sc_out + sc_out2 * r with sc_out2 < 0. The forward keeps r per score: the logit decreases with
+// r, so the row maximum is sc_out + sc_out2 * (row minimum of r), and the exponent argument
+// logit - m is one FMA, r * sc_out2 + (sc_out - m). A masked score has r = +inf (logit -inf).
+template <int SCORE>
+__device__ __forceinline__ float softcap_r(const FwdArgs& a, float acc, int qi, int kv, float slope) {
+  float u = acc * a.sc_in;
+  if constexpr (SCORE & FA_SCORE_ALIBI) u = fmaf(-slope, fabsf((float)(qi - kv)), u);
+  return __builtin_amdgcn_rcpf(1.0f + fast_exp2(u));
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------------------------
@@ -452,8 +463,10 @@ __device__ __forceinline__ void compute_step(const FwdArgs& a, const Ctx& c, con
     }
 
     // Scores (log2 domain) and the mask. Without a score_mod the 1/sqrt(d) * log2(e) scale is
-    // folded into the exponent below, and the maximum is taken on the raw products.
-    float mx = -INFINITY;
+    // folded into the exponent below, and the maximum is taken on the raw products. With the
+    // soft-cap the tile keeps r (see softcap_r) and the row minimum of r gives the maximum.
+    constexpr bool CAP = (SCORE & FA_SCORE_SOFTCAP) != 0;
+    float mx = CAP ? INFINITY : -INFINITY;
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       if (!(L & (1u << nb))) continue;
@@ -475,18 +488,21 @@ __device__ __forceinline__ void compute_step(const FwdArgs& a, const Ctx& c, con
         for (int e = 0; e < 4; ++e) {
           const int i = g * 4 + e;
           const int off = g * 8 + e;
-          float x = SCORE == 0 ? sacc[nb][i] : score_log2<SCORE>(a, sacc[nb][i], qi, kbase + off, c.slope);
+          float x = SCORE == 0 ? sacc[nb][i]
+                    : CAP         ? softcap_r<SCORE>(a, sacc[nb][i], qi, kbase + off, c.slope)
+                                  : score_log2<SCORE>(a, sacc[nb][i], qi, kbase + off, c.slope);
           if constexpr (MASKED) {
+            constexpr unsigned kMasked = CAP ? 0x7f800000u : 0xff800000u;  // +inf (r) or -inf
             const int keep = (int)(abits << (31 - off)) >> 31;
-            x = __int_as_float((__float_as_int(x) & keep) | (int)(0xff800000u & ~(unsigned)keep));
-            if constexpr (DOC) x = kd4[e] == c.qdoc ? x : -INFINITY;
+            x = __int_as_float((__float_as_int(x) & keep) | (int)(kMasked & ~(unsigned)keep));
+            if constexpr (DOC) x = kd4[e] == c.qdoc ? x : __uint_as_float(kMasked);
           }
           sacc[nb][i] = x;
-          mx = fmaxf(mx, x);
+          mx = CAP ? fminf(mx, x) : fmaxf(mx, x);
         }
       }
     }
-    mx = half_swap_max(mx);
+    mx = CAP ? fmaf(a.sc_out2, half_swap_min(mx), a.sc_out) : half_swap_max(mx);
     const float scale = SCORE == 0 ? a.scale_log2 : 1.0f;
     const float m_cand = fmaxf(st.m_run, mx * scale);
     const bool raise = m_cand > st.m_run + kRescaleSlack;
@@ -496,6 +512,7 @@ __device__ __forceinline__ void compute_step(const FwdArgs& a, const Ctx& c, con
     // and copied all 64 accumulators on every step.
     auto finish = [&]() {
       const float m_eff = st.m_run == -INFINITY ? 0.f : st.m_run;  // rows with no allowed key so far
+      const float cap_off = a.sc_out - m_eff;
       // P = exp2(t - m); P^T goes straight into the B operand of O^T = V^T P^T as bf16.
       bf16x8 pb[2][2];
 #pragma unroll
@@ -503,7 +520,7 @@ __device__ __forceinline__ void compute_step(const FwdArgs& a, const Ctx& c, con
         if (!(L & (1u << nb))) continue;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float p = fast_exp2(fmaf(sacc[nb][i], scale, -m_eff));
+          const float p = fast_exp2(CAP ? fmaf(sacc[nb][i], a.sc_out2, cap_off) : fmaf(sacc[nb][i], scale, -m_eff));
           st.l_run += p;
           pb[nb][i >> 3][i & 7] = (__bf16)p;
         }

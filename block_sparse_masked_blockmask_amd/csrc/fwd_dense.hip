@@ -82,6 +82,16 @@ __device__ __forceinline__ float dscore(const FwdArgs& a, float acc, int qi, int
   }
 }
 
+// Soft-cap only: r = 1 / (1 + 2^u), the logit being sc_out + sc_out2 * r with sc_out2 < 0 (as in
+// the block-sparse kernel's softcap_r). The tile keeps r; the row maximum comes from the row
+// minimum of r, and the exponent argument is r * sc_out2 + (sc_out - m). Masked: r = +inf.
+template <int SCORE>
+__device__ __forceinline__ float dscore_r(const FwdArgs& a, float acc, int qi, int kv, float slope) {
+  float u = acc * a.sc_in;
+  if constexpr (SCORE & FA_SCORE_ALIBI) u = fmaf(-slope, fabsf((float)(qi - kv)), u);
+  return __builtin_amdgcn_rcpf(1.0f + fast_exp2(u));
+}
+
 // One step's K or V tile: 16 one-KB segments (4 rows each); wave w issues segments 8 i + w.
 // Rows past the last key are clamped to it (finite data, masked).
 template <bool K_SIDE>
@@ -144,19 +154,20 @@ __device__ __forceinline__ void dense_part_a(const FwdArgs& a, const DLane& c, c
                                              const unsigned char* sK) {
   int kx0 = c.kx0;
   asm volatile("" : "+v"(kx0));
-  float mx = -INFINITY;
+  constexpr bool CAP = (SCORE & FA_SCORE_SOFTCAP) != 0;
+  float mx = CAP ? INFINITY : -INFINITY;  // CAP: row minimum of r
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int key = kv0 + nb * 32 + (i >> 2) * 8 + c.hl * 4 + (i & 3);
-      float x = dscore<SCORE>(a, s[nb][i], c.qi, key, c.slope);
-      if constexpr (TAIL) x = key < a.Lkv ? x : -INFINITY;
+      float x = CAP ? dscore_r<SCORE>(a, s[nb][i], c.qi, key, c.slope) : dscore<SCORE>(a, s[nb][i], c.qi, key, c.slope);
+      if constexpr (TAIL) x = key < a.Lkv ? x : (CAP ? INFINITY : -INFINITY);
       s[nb][i] = x;
-      mx = fmaxf(mx, x);
+      mx = CAP ? fminf(mx, x) : fmaxf(mx, x);
     }
   }
-  mx = half_swap_max(mx);
+  mx = CAP ? fmaf(a.sc_out2, half_swap_min(mx), a.sc_out) : half_swap_max(mx);
   const float scale = SCORE == 0 ? a.scale_log2 : 1.0f;
   const float m_cand = fmaxf(st.m, mx * scale);
   const bool raise = m_cand > st.m + kDSlack;
@@ -170,6 +181,7 @@ __device__ __forceinline__ void dense_part_a(const FwdArgs& a, const DLane& c, c
     st.m = m_new;
   }
   const float neg_m = -st.m;
+  const float cap_off = a.sc_out - st.m;
   if constexpr (HAS_NEXT) {
     // 16 products of S(n+1) in a fixed order (channel block k / 2, sub-block k % 2), each K
     // fragment read kReadAhead products ahead, and beside product k the exponentials of elements
@@ -191,7 +203,7 @@ __device__ __forceinline__ void dense_part_a(const FwdArgs& a, const DLane& c, c
                                                           0);
       static_for<2>([&](auto ec) {
         constexpr int e = 2 * k + decltype(ec)::value;
-        pe[e] = fast_exp2(fmaf(s[e >> 4][e & 15], scale, neg_m));
+        pe[e] = fast_exp2(CAP ? fmaf(s[e >> 4][e & 15], a.sc_out2, cap_off) : fmaf(s[e >> 4][e & 15], scale, neg_m));
       });
       if constexpr (k > 0) {
         static_for<2>([&](auto ec) {
@@ -212,7 +224,7 @@ __device__ __forceinline__ void dense_part_a(const FwdArgs& a, const DLane& c, c
     for (int nb = 0; nb < 2; ++nb) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float p = fast_exp2(fmaf(s[nb][i], scale, neg_m));
+        const float p = fast_exp2(CAP ? fmaf(s[nb][i], a.sc_out2, cap_off) : fmaf(s[nb][i], scale, neg_m));
         st.l[i & 3] += p;
         pb[nb][i >> 3][i & 7] = (__bf16)p;
       }
