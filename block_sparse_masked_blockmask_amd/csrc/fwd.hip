@@ -386,6 +386,28 @@ __device__ __forceinline__ void compute_step(const FwdArgs& a, const Ctx& c, con
   // Live 32-key sub-blocks for this wave (wave-uniform).
   unsigned live = 3;
   if constexpr (MASKED) {
+    // Document-id range of each sub-block's keys, both at once: lane l reads key l's id (ids
+    // past the last key repeat the last key's, which lies in the same sub-block), and each
+    // 32-lane half is reduced to its minimum and maximum by DPP moves within 16-lane rows and
+    // the two rows' results. lq + 32 hl is the lane: lq is recovered from kx0 (row lq times 256
+    // plus a chunk offset below 256), which is live here; c.lq itself would be kept in a spilled
+    // register.
+    int kd_min[2] = {0, 0}, kd_max[2] = {0, 0};
+    if constexpr (DOC) {
+      int mx = sD[(kx0 >> 8) + 8 * dx], mn = mx;
+      mx = max(mx, dpp<kDppXor1>(mx));
+      mn = min(mn, dpp<kDppXor1>(mn));
+      mx = max(mx, dpp<kDppXor2>(mx));
+      mn = min(mn, dpp<kDppXor2>(mn));
+      mx = max(mx, dpp<kDppHalfMirror>(mx));
+      mn = min(mn, dpp<kDppHalfMirror>(mn));
+      mx = max(mx, dpp<kDppMirror>(mx));
+      mn = min(mn, dpp<kDppMirror>(mn));
+      kd_max[0] = max(__builtin_amdgcn_readlane(mx, 0), __builtin_amdgcn_readlane(mx, 16));
+      kd_max[1] = max(__builtin_amdgcn_readlane(mx, 32), __builtin_amdgcn_readlane(mx, 48));
+      kd_min[0] = min(__builtin_amdgcn_readlane(mn, 0), __builtin_amdgcn_readlane(mn, 16));
+      kd_min[1] = min(__builtin_amdgcn_readlane(mn, 32), __builtin_amdgcn_readlane(mn, 48));
+    }
     live = 0;
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
@@ -396,13 +418,7 @@ __device__ __forceinline__ void compute_step(const FwdArgs& a, const Ctx& c, con
       if (a.flags & FA_MASK_CAUSAL) dead = dead || c.qw1 < k0;
       if (a.flags & FA_MASK_WINDOW) dead = dead || c.qw0 - k1 >= a.window;
       if (a.flags & FA_MASK_PREFIX_LM) dead = dead || (k0 >= a.prefix_len && c.qw1 < k0);
-      if (DOC && !dead) {
-        // lq recovered from kx0 (row lq times 256 plus a chunk offset below 256), which is live
-        // here; c.lq itself would be kept in a spilled register.
-        const int d = sD[min(nb * 32 + (kx0 >> 8), k1 - kv0)];
-        const int dmax = wave_max32(d), dmin = wave_min32(d);
-        dead = (dmax < c.qd_min) | (dmin > c.qd_max);
-      }
+      if (DOC) dead = dead || (kd_max[nb] < c.qd_min) | (kd_min[nb] > c.qd_max);
       if (!dead) live |= 1u << nb;
     }
     live = __builtin_amdgcn_readfirstlane(live);
@@ -832,6 +848,36 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(FwdArgs
 }
 
 // ---------------------------------------------------------------------------------------------
+// One BK-key tile of K and V (fp32) into LDS rows of P floats, 256 threads. Every load of a
+// thread is issued before any is waited for, so a tile costs one memory round trip (a rolled
+// loop waited for each of its 16 pairs of loads in turn). Rows past the last key are zero; their
+// loads read the last key's row instead.
+template <int BK, int P>
+__device__ __forceinline__ void stage_f32_tile(const FwdArgs& a, const float* kp, const float* vp, int kv0, int tid,
+                                               float* sK, float* sV) {
+  constexpr int IT = BK * 32 / 256;  // float4 chunks per thread and tensor
+  f32x4 kx[IT], vx[IT];
+#pragma unroll
+  for (int j = 0; j < IT; ++j) {
+    const int id = tid + j * 256;
+    const int64_t kv = min(kv0 + (id >> 5), a.Lkv - 1);
+    kx[j] = *(const f32x4*)(kp + kv * a.k_sl + (id & 31) * 4);
+    vx[j] = *(const f32x4*)(vp + kv * a.v_sl + (id & 31) * 4);
+  }
+#pragma unroll
+  for (int j = 0; j < IT; ++j) {
+    const int id = tid + j * 256;
+    const int r = id >> 5, c4 = id & 31;
+    const bool in = kv0 + r < a.Lkv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sK[r * P + c4 * 4 + e] = in ? kx[j][e] : 0.f;
+      sV[r * P + c4 * 4 + e] = in ? vx[j][e] : 0.f;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
 // f32 kernel: same decomposition with v_mfma_f32_32x32x2_f32 (true fp32 products and sums).
 // The MFMA's two k positions per instruction are the lane halves; for S^T the k index is the
 // channel d = 2*ks + hl, for O^T it is the key of accumulator element i.
@@ -876,24 +922,11 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_kernel(FwdArgs a) {
     const bool masked = partial || (kv0 + BK > a.Lkv);
 
     __syncthreads();
-    for (int id = tid; id < BK * 32; id += 256) {  // float4 chunks
-      const int r = id >> 5, c4 = id & 31;
-      const int kv = kv0 + r;
-      f32x4 kx = f32x4{}, vx = f32x4{};
-      if (kv < a.Lkv) {
-        kx = *(const f32x4*)(kp + (int64_t)kv * a.k_sl + c4 * 4);
-        vx = *(const f32x4*)(vp + (int64_t)kv * a.v_sl + c4 * 4);
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sK[r * P + c4 * 4 + e] = kx[e];
-        sV[r * P + c4 * 4 + e] = vx[e];
-      }
-    }
-    if (masked && (a.flags & FA_MASK_DOC) && tid < BK) {
-      const int kv = kv0 + tid;
-      sDoc[tid] = kv < a.Lkv ? a.kv_doc[(int64_t)it.b * a.Lkv + kv] : 0;
-    }
+    // The tile's document ids are loaded with K and V (same round trip).
+    const bool tile_doc = masked && (a.flags & FA_MASK_DOC) && tid < BK;
+    const int kdoc = tile_doc ? a.kv_doc[(int64_t)it.b * a.Lkv + min(kv0 + tid, a.Lkv - 1)] : 0;
+    stage_f32_tile<BK, P>(a, kp, vp, kv0, tid, sK, sV);
+    if (tile_doc) sDoc[tid] = kv0 + tid < a.Lkv ? kdoc : 0;
     __syncthreads();
 
     f32x16 sacc[NB];
@@ -1034,24 +1067,11 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_split_kernel(FwdArgs a) {
     const bool masked = partial || (kv0 + BK > a.Lkv);
 
     __syncthreads();
-    for (int id = tid; id < BK * 32; id += 256) {  // float4 chunks
-      const int r = id >> 5, c4 = id & 31;
-      const int kv = kv0 + r;
-      f32x4 kx = f32x4{}, vx = f32x4{};
-      if (kv < a.Lkv) {
-        kx = *(const f32x4*)(kp + (int64_t)kv * a.k_sl + c4 * 4);
-        vx = *(const f32x4*)(vp + (int64_t)kv * a.v_sl + c4 * 4);
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sK[r * P + c4 * 4 + e] = kx[e];
-        sV[r * P + c4 * 4 + e] = vx[e];
-      }
-    }
-    if (masked && (a.flags & FA_MASK_DOC) && tid < BK) {
-      const int kv = kv0 + tid;
-      sDoc[tid] = kv < a.Lkv ? a.kv_doc[(int64_t)it.b * a.Lkv + kv] : 0;
-    }
+    // The tile's document ids are loaded with K and V (same round trip).
+    const bool tile_doc = masked && (a.flags & FA_MASK_DOC) && tid < BK;
+    const int kdoc = tile_doc ? a.kv_doc[(int64_t)it.b * a.Lkv + min(kv0 + tid, a.Lkv - 1)] : 0;
+    stage_f32_tile<BK, P>(a, kp, vp, kv0, tid, sK, sV);
+    if (tile_doc) sDoc[tid] = kv0 + tid < a.Lkv ? kdoc : 0;
     __syncthreads();
 
     for (int nb = wave; nb < NB; nb += 4) {
