@@ -1021,13 +1021,63 @@ constexpr int kF32SplitBelow = 256;
 // end the partial results are merged in a fixed wave order through LDS:
 //   m = max_w m_w,  f_w = 2^(m_w - m),  l = sum_w f_w l_w,  O = (sum_w f_w O_w) / l.
 // A wave reads each K/V sub-block once, so a tile costs each wave a quarter of the products.
+//
+// Latency is what matters at these sizes, so every phase is one round trip or one barrier:
+//   - the workgroup's 32 Q rows are loaded once, coalesced, with the first tile's K and V, and
+//     handed to the waves through LDS (per-lane loads of the Q^T operand, 64 four-byte loads per
+//     lane, took a third of the kernel);
+//   - tile rows past the last key are not loaded;
+//   - the four P.V product chains (one per 32-channel block) are interleaved, and S^T is summed
+//     in two interleaved chains;
+//   - the merge writes each wave's scaled partial O into its own LDS slab and sums the slabs in
+//     wave order after a single barrier.
 // ---------------------------------------------------------------------------------------------
+template <int BK>
+struct F32Tile {
+  static constexpr int IT = BK * 32 / 256;  // float4 chunks per thread and tensor
+  f32x4 k[IT], v[IT];
+};
+
+// Loads of one BK-key tile (rows past the last key are skipped).
+template <int BK>
+__device__ __forceinline__ void f32_tile_load(F32Tile<BK>& tt, const FwdArgs& a, const float* kp, const float* vp,
+                                              int kv0, int tid) {
+#pragma unroll
+  for (int j = 0; j < F32Tile<BK>::IT; ++j) {
+    const int id = tid + j * 256;
+    const int kv = kv0 + (id >> 5);
+    tt.k[j] = f32x4{};
+    tt.v[j] = f32x4{};
+    if (kv < a.Lkv) {
+      tt.k[j] = *(const f32x4*)(kp + (int64_t)kv * a.k_sl + (id & 31) * 4);
+      tt.v[j] = *(const f32x4*)(vp + (int64_t)kv * a.v_sl + (id & 31) * 4);
+    }
+  }
+}
+
+template <int BK, int P>
+__device__ __forceinline__ void f32_tile_store(const F32Tile<BK>& tt, float* sK, float* sV, int tid) {
+#pragma unroll
+  for (int j = 0; j < F32Tile<BK>::IT; ++j) {
+    const int id = tid + j * 256;
+    const int r = id >> 5, c4 = id & 31;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sK[r * P + c4 * 4 + e] = tt.k[j][e];
+      sV[r * P + c4 * 4 + e] = tt.v[j][e];
+    }
+  }
+}
+
 template <int BK, int SCORE>
 __global__ __launch_bounds__(256, 1) void fwd_f32_split_kernel(FwdArgs a) {
   constexpr int NB = BK / 32;
-  constexpr int P = 130;
-  __shared__ float sK[BK * P];
-  __shared__ float sV[BK * P];
+  constexpr int P = 130;   // K/V/Q row stride in floats
+  constexpr int PO = 132;  // merge slab row stride (16-byte rows)
+  constexpr int KV_FLOATS = BK * P > 2 * 32 * PO ? BK * P : 2 * 32 * PO;  // a tile, or two merge slabs
+  __shared__ __attribute__((aligned(16))) float sK[KV_FLOATS];
+  __shared__ __attribute__((aligned(16))) float sV[KV_FLOATS];
+  __shared__ float sQ[32 * P];
   __shared__ int sDoc[BK];
   __shared__ float s_m[4][32];
   __shared__ float s_l[4][32];
@@ -1045,9 +1095,16 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_split_kernel(FwdArgs a) {
   const float* kp = (const float*)a.k + it.b * a.k_sb + it.hkv * a.k_sh;
   const float* vp = (const float*)a.v + it.b * a.v_sb + it.hkv * a.v_sh;
 
-  float qreg[64];
+  // The slice's Q rows, coalesced: 32 rows x 32 float4 chunks, 4 per thread (rows past the last
+  // query are zero).
+  f32x4 qst[4];
 #pragma unroll
-  for (int ks = 0; ks < 64; ++ks) qreg[ks] = q_in ? qp[(int64_t)qi * a.q_sl + 2 * ks + hl] : 0.f;
+  for (int j = 0; j < 4; ++j) {
+    const int id = tid + j * 256;
+    const int r = q0 + (id >> 5);
+    qst[j] = f32x4{};
+    if (r < a.Lq) qst[j] = *(const f32x4*)(qp + (int64_t)r * a.q_sl + (id & 31) * 4);
+  }
   const int qdoc = ((a.flags & FA_MASK_DOC) && q_in) ? a.q_doc[(int64_t)it.b * a.Lq + qi] : 0;
   const float slope = (SCORE & FA_SCORE_ALIBI) ? a.slopes[it.hq] * a.slope_mul : 0.f;
   const MaskSpec ms{a.flags, a.window, a.prefix_len};
@@ -1056,9 +1113,11 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_split_kernel(FwdArgs a) {
 #pragma unroll
   for (int db = 0; db < 4; ++db) oacc[db] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
+  float qreg[64];
 
   const TileList tl = tile_list(a, it);
   const int ntiles = tl.nfull + tl.npart;
+  bool q_staged = false;
   for (int t = 0; t < ntiles; ++t) {
     const bool partial = t >= tl.nfull;
     const int kb = partial ? tl.part[t - tl.nfull] : (a.all_full ? t : tl.full[t]);
@@ -1066,20 +1125,41 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_split_kernel(FwdArgs a) {
     const int kv0 = kb * BK;
     const bool masked = partial || (kv0 + BK > a.Lkv);
 
-    __syncthreads();
-    // The tile's document ids are loaded with K and V (same round trip).
+    // The tile's K, V and document ids are loaded in one round trip (with Q, for the first).
     const bool tile_doc = masked && (a.flags & FA_MASK_DOC) && tid < BK;
     const int kdoc = tile_doc ? a.kv_doc[(int64_t)it.b * a.Lkv + min(kv0 + tid, a.Lkv - 1)] : 0;
-    stage_f32_tile<BK, P>(a, kp, vp, kv0, tid, sK, sV);
+    F32Tile<BK> tt;
+    f32_tile_load<BK>(tt, a, kp, vp, kv0, tid);
+    __syncthreads();  // the previous tile's reads are done
+    if (!q_staged) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int id = tid + j * 256;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sQ[(id >> 5) * P + (id & 31) * 4 + e] = qst[j][e];
+      }
+    }
+    f32_tile_store<BK, P>(tt, sK, sV, tid);
     if (tile_doc) sDoc[tid] = kv0 + tid < a.Lkv ? kdoc : 0;
     __syncthreads();
+    if (!q_staged) {
+      // Q^T as the B operand: lane holds Q[qi][2 ks + hl].
+#pragma unroll
+      for (int ks = 0; ks < 64; ++ks) qreg[ks] = sQ[lq * P + 2 * ks + hl];
+      q_staged = true;
+    }
 
     for (int nb = wave; nb < NB; nb += 4) {
       if (kv0 + nb * 32 >= a.Lkv) break;  // this and later sub-blocks lie past the last key
-      f32x16 sacc = f32x16{};
+      // S^T in two interleaved chains (even and odd k-steps), summed at the end.
+      f32x16 s0 = f32x16{}, s1 = f32x16{};
       const float* krow = sK + (nb * 32 + lq) * P + hl;
 #pragma unroll
-      for (int ks = 0; ks < 64; ++ks) sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(krow[2 * ks], qreg[ks], sacc, 0, 0, 0);
+      for (int ks = 0; ks < 64; ks += 2) {
+        s0 = __builtin_amdgcn_mfma_f32_32x32x2f32(krow[2 * ks], qreg[ks], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x2f32(krow[2 * ks + 2], qreg[ks + 1], s1, 0, 0, 0);
+      }
+      f32x16 sacc = s0 + s1;
 
       float mx = -INFINITY;
 #pragma unroll
@@ -1108,13 +1188,14 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_split_kernel(FwdArgs a) {
       }
       l_run = l_run * alpha + rs;
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        oacc[db] *= alpha;
+      for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
+      // O^T += V^T P^T, the four channel blocks' chains interleaved.
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int r = nb * 32 + (i >> 2) * 8 + hl * 4 + (i & 3);
+      for (int i = 0; i < 16; ++i) {
+        const int r = nb * 32 + (i >> 2) * 8 + hl * 4 + (i & 3);
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(sV[r * P + db * 32 + lq], sacc[i], oacc[db], 0, 0, 0);
-        }
       }
     }
   }
@@ -1138,33 +1219,35 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_split_kernel(FwdArgs a) {
     l += f * s_l[w][lq];
     if (w == wave) f_self = f;
   }
-  // Partial outputs accumulate in sK viewed as [32 queries][128 channels], one wave after the
-  // other; the element layout is the accumulator's, identical in every wave.
-  float* sO = sK;
-  for (int w = 0; w < 4; ++w) {
-    if (w == wave) {
+  // Slab of wave w: [32 queries][PO], in sK (waves 0, 1) or sV (waves 2, 3). Lane (lq, hl) holds
+  // channels 32 db + 8 gq + 4 hl + 0..3 of its query.
+  float* slab = (wave < 2 ? sK : sV) + (wave & 1) * 32 * PO;
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
+  for (int db = 0; db < 4; ++db) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int ch = db * 32 + (i >> 2) * 8 + hl * 4 + (i & 3);
-          const float v = oacc[db][i] * f_self;
-          sO[lq * 128 + ch] = w == 0 ? v : sO[lq * 128 + ch] + v;
-        }
-      }
+    for (int gq = 0; gq < 4; ++gq) {
+      f32x4 o4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o4[e] = oacc[db][gq * 4 + e] * f_self;
+      *(f32x4*)(slab + lq * PO + db * 32 + gq * 8 + hl * 4) = o4;
     }
-    __syncthreads();
   }
+  __syncthreads();
   const float inv = l > 0.f ? 1.0f / l : 0.f;
-  // Store: wave w writes channels [32 w, 32 w + 32) of the 32 rows (lane = row, two halves of 16).
+  // Store: wave w writes channels [32 w, 32 w + 32) of the 32 rows (lane = row, two halves of 16),
+  // each the sum of the four slabs in wave order.
   if (q_in) {
     float* op = (float*)a.o + it.b * a.o_sb + it.hq * a.o_sh + (int64_t)qi * a.o_sl;
 #pragma unroll
     for (int c4 = 0; c4 < 4; ++c4) {
       const int ch = wave * 32 + hl * 16 + c4 * 4;
+      const f32x4 v0 = *(const f32x4*)(sK + lq * PO + ch);
+      const f32x4 v1 = *(const f32x4*)(sK + 32 * PO + lq * PO + ch);
+      const f32x4 v2 = *(const f32x4*)(sV + lq * PO + ch);
+      const f32x4 v3 = *(const f32x4*)(sV + 32 * PO + lq * PO + ch);
       f32x4 o4;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o4[e] = sO[lq * 128 + ch + e] * inv;
+      for (int e = 0; e < 4; ++e) o4[e] = (((v0[e] + v1[e]) + v2[e]) + v3[e]) * inv;
       *(f32x4*)(op + ch) = o4;
     }
     if (a.lse && wave == 0 && hl == 0) {
