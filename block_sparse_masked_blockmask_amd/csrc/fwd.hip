@@ -1151,15 +1151,27 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_split_kernel(FwdArgs a) {
 
     for (int nb = wave; nb < NB; nb += 4) {
       if (kv0 + nb * 32 >= a.Lkv) break;  // this and later sub-blocks lie past the last key
-      // S^T in two interleaved chains (even and odd k-steps), summed at the end.
-      f32x16 s0 = f32x16{}, s1 = f32x16{};
+      // S^T in two interleaved chains (even and odd k-steps), summed at the end. All 64 K operands
+      // are read before the chain (read next to each product, every pair waited for its read).
+      float kf[64];
       const float* krow = sK + (nb * 32 + lq) * P + hl;
 #pragma unroll
+      for (int ks = 0; ks < 64; ++ks) kf[ks] = krow[2 * ks];
+      f32x16 s0 = f32x16{}, s1 = f32x16{};
+#pragma unroll
       for (int ks = 0; ks < 64; ks += 2) {
-        s0 = __builtin_amdgcn_mfma_f32_32x32x2f32(krow[2 * ks], qreg[ks], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_32x32x2f32(krow[2 * ks + 2], qreg[ks + 1], s1, 0, 0, 0);
+        s0 = __builtin_amdgcn_mfma_f32_32x32x2f32(kf[ks], qreg[ks], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x2f32(kf[ks + 1], qreg[ks + 1], s1, 0, 0, 0);
       }
       f32x16 sacc = s0 + s1;
+      // The 64 V operands of this sub-block, read while the softmax below runs.
+      float vf[64];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = nb * 32 + (i >> 2) * 8 + hl * 4 + (i & 3);
+#pragma unroll
+        for (int db = 0; db < 4; ++db) vf[i * 4 + db] = sV[r * P + db * 32 + lq];
+      }
 
       float mx = -INFINITY;
 #pragma unroll
@@ -1192,10 +1204,9 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_split_kernel(FwdArgs a) {
       // O^T += V^T P^T, the four channel blocks' chains interleaved.
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int r = nb * 32 + (i >> 2) * 8 + hl * 4 + (i & 3);
 #pragma unroll
         for (int db = 0; db < 4; ++db)
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(sV[r * P + db * 32 + lq], sacc[i], oacc[db], 0, 0, 0);
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vf[i * 4 + db], sacc[i], oacc[db], 0, 0, 0);
       }
     }
   }
