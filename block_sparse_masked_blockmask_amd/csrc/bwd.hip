@@ -30,13 +30,14 @@
 //                       then dV^T += dO^T P and dK^T += Q^T dA, both A operands read transposed
 //                       from LDS. GQA sums over the group inside the workgroup (no atomics).
 //                       K^T, V^T and both accumulators hold 192 registers, so it runs at one
-//                       wave per SIMD; Q and dO tiles are staged through registers (with LDS-DMA
-//                       at one wave per SIMD, issuing the transfers stalled the only wave and
-//                       measured slower; splitting dK and dV into two kernels spilled);
+//                       wave per SIMD; Q and dO tiles of a whole 128-query block per step are
+//                       staged through registers (with LDS-DMA at one wave per SIMD, issuing the
+//                       transfers stalled the only wave and measured slower; splitting dK and dV
+//                       into two kernels spilled);
 //   bwd_slope_kernel    sums the per-block slope partials into dslopes[h] (deterministic).
 //
 // Accumulator layout (32x32 MFMA): element i of lane l holds row 8*(i/4) + 4*(l/32) + i%4 and
-// column l%32. Tiles in LDS are [64 rows][128 bf16] with 16-byte chunks XOR-swizzled by row
+// column l%32. Tiles in LDS are [rows][128 bf16] with 16-byte chunks XOR-swizzled by row
 // (tile_off), which serves both the row reads of A operands and the transposed reads.
 #include <hip/hip_runtime.h>
 
@@ -168,16 +169,19 @@ template <int N> __device__ __forceinline__ void sched_tr() {
   }
 }
 
-// Stage rows [r0, r0 + 64) of two [L][128] bf16 tensors into registers (4 chunks of 16 bytes
-// per thread and tensor); rows at or past L read row L - 1 and are zeroed when stored.
+// Stage rows [r0, r0 + ROWS) of two [L][128] bf16 tensors into registers (ROWS / 16 chunks of
+// 16 bytes per thread and tensor); rows at or past L read row L - 1 and are zeroed when stored.
+template <int ROWS>
 struct Stage {
-  i32x4 x[4], y[4];
+  static constexpr int U = ROWS * 16 / 256;
+  i32x4 x[U], y[U];
 };
 
-__device__ __forceinline__ void stage_load(Stage& st, const __bf16* xp, int64_t xsl, const __bf16* yp, int64_t ysl,
-                                           int r0, int L, int tid) {
+template <int ROWS>
+__device__ __forceinline__ void stage_load(Stage<ROWS>& st, const __bf16* xp, int64_t xsl, const __bf16* yp,
+                                           int64_t ysl, int r0, int L, int tid) {
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < Stage<ROWS>::U; ++u) {
     const int id = tid + 256 * u;
     const int r = min(r0 + (id >> 4), L - 1);
     const int ch = id & 15;
@@ -186,10 +190,11 @@ __device__ __forceinline__ void stage_load(Stage& st, const __bf16* xp, int64_t 
   }
 }
 
-__device__ __forceinline__ void stage_store(const Stage& st, unsigned char* sx, unsigned char* sy, int r0, int L,
+template <int ROWS>
+__device__ __forceinline__ void stage_store(const Stage<ROWS>& st, unsigned char* sx, unsigned char* sy, int r0, int L,
                                             int tid) {
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < Stage<ROWS>::U; ++u) {
     const int id = tid + 256 * u;
     const int r = id >> 4, ch = id & 15;
     const bool in = r0 + r < L;
@@ -513,11 +518,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------------------------
 template <int SCORE>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(1024))) unsigned char sQ[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char sO[kTileBytes];
-  __shared__ __attribute__((aligned(16))) float sL[kRows];
-  __shared__ __attribute__((aligned(16))) float sDl[kRows];
-  __shared__ __attribute__((aligned(16))) int sDoc[kRows];
+  // One step takes a whole 128-query block (two 64-row halves took one exposed round trip of
+  // staging loads each, at one wave per SIMD).
+  constexpr int QR = 128;
+  __shared__ __attribute__((aligned(1024))) unsigned char sQ[QR * 256];
+  __shared__ __attribute__((aligned(1024))) unsigned char sO[QR * 256];
+  __shared__ __attribute__((aligned(16))) float sL[QR];
+  __shared__ __attribute__((aligned(16))) float sDl[QR];
+  __shared__ __attribute__((aligned(16))) int sDoc[QR];
 
   // Order: key blocks from first to last (the longest columns under causal masks first), then
   // (batch, kv head) pairs; each XCD takes one contiguous range, pairs permuted as in dQ.
@@ -587,20 +595,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
       full = a.fullq_idx + r * a.nqb;
       part = a.q_idx + r * a.nqb;
     }
-    const int nsteps = 2 * (nfull + npart);
-    for (int s = 0; s < nsteps; ++s) {
-      const int t = s >> 1;
+    const int nsteps = nfull + npart;
+    for (int t = 0; t < nsteps; ++t) {
       const bool masked = t >= nfull;
       // An entry outside [0, n_qb) becomes n_qb, whose rows lie past the queries: skipped.
       const int qbk = masked ? sanitize_block(part[t - nfull], a.nqb) : (a.all_full ? t : sanitize_block(full[t], a.nqb));
-      const int q0 = qbk * 128 + (s & 1) * kRows;
+      const int q0 = qbk * 128;
       if (q0 >= a.Lq) continue;  // uniform over the workgroup
 
-      Stage st;
-      stage_load(st, qp, a.q_sl, dop, a.do_sl, q0, a.Lq, tid);
+      Stage<QR> st;
+      stage_load<QR>(st, qp, a.q_sl, dop, a.do_sl, q0, a.Lq, tid);
       float lv = INFINITY, dv = 0.f;
       int dd = 0;
-      if (tid < kRows) {
+      if (tid < QR) {
         const int qr = q0 + tid;
         if (qr < a.Lq) {
           lv = a.lse2[rowbase + qr];
@@ -609,8 +616,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
         }
       }
       __syncthreads();  // the previous step's reads are done
-      stage_store(st, sQ, sO, q0, a.Lq, tid);
-      if (tid < kRows) {
+      stage_store<QR>(st, sQ, sO, q0, a.Lq, tid);
+      if (tid < QR) {
         sL[tid] = lv;
         sDl[tid] = dv;
         sDoc[tid] = dd;
@@ -618,7 +625,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
       __syncthreads();
 
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
+      for (int sub = 0; sub < QR / 32; ++sub) {
         f32x16 sacc = f32x16{}, dpacc = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
