@@ -42,6 +42,8 @@
 #include <hip/hip_runtime.h>
 
 #include <climits>
+#include <type_traits>
+#include <utility>
 
 #include "device_common.h"
 #include "launch.h"
@@ -105,6 +107,16 @@ __device__ __forceinline__ bf16x8 read_xt(const unsigned char* tile, int row0, i
 // A operand of X (row = row0 + lq, k = channels 16 ks + 8 hl .. +8); kx0 = tile_off(lq, hl).
 __device__ __forceinline__ bf16x8 read_x(const unsigned char* tile, int row0, int ks, int kx0) {
   return *(const bf16x8*)(tile + row0 * 256 + (kx0 ^ (32 * ks)));
+}
+
+template <class F, int... I>
+__device__ __forceinline__ void bwd_static_for_impl(F& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+// f(integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time.
+template <int N, class F>
+__device__ __forceinline__ void bwd_static_for(F&& f) {
+  bwd_static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 // Score and its derivative factor for one pair: returns f (natural units) and sets dfac =
@@ -564,7 +576,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
     vreg[ks] = *(const bf16x8*)(vp + ks * 16 + hl * 8);
   }
   const int kdoc = doc ? a.kv_doc[(int64_t)b * a.Lkv + kc] : 0;
-  const MaskSpec ms{a.flags, a.window, a.prefix_len};
+  const PairMask pm = make_pair_mask(a);
   const int tb = tr_base(lane), kx0 = tile_off(lq, hl);
 
   f32x16 dkacc[4], dvacc[4];
@@ -624,46 +636,83 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
       }
       __syncthreads();
 
-#pragma unroll
-      for (int sub = 0; sub < QR / 32; ++sub) {
-        f32x16 sacc = f32x16{}, dpacc = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_x(sQ, sub * 32, ks, kx0), kreg[ks], sacc, 0, 0, 0);
-          dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_x(sO, sub * 32, ks, kx0), vreg[ks], dpacc, 0, 0, 0);
-        }
-        bf16x8 pb[2], dsb[2];
+      // The step's four 32-query sub-blocks, software-pipelined: while sub-block s's vector work
+      // turns its scores into P and dA, the MFMA pipe runs the dV/dK products of sub-block s - 1
+      // and the S^T/dP^T products of sub-block s + 1. The order is fixed at compile time: each
+      // slot (one score's vector work and one pair of products) ends with a scheduling barrier.
+      // Full and partial tiles share this code; a partial tile's P and dA are masked afterwards
+      // (a select per score), before its dV/dK products.
+      f32x16 sa[2], da[2];        // S^T and dP^T of sub-blocks s (s % 2)
+      bf16x8 pb[2][2], dsb[2][2];  // P and dA of sub-blocks s (s % 2), as B operands
+      auto sdp = [&](auto sc, auto kc) {  // S^T / dP^T products of k-step ks
+        constexpr int sb = decltype(sc)::value, ks = decltype(kc)::value;
+        sa[sb & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_x(sQ, sb * 32, ks, kx0), kreg[ks],
+                                                             ks ? sa[sb & 1] : f32x16{}, 0, 0, 0);
+        da[sb & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_x(sO, sb * 32, ks, kx0), vreg[ks],
+                                                             ks ? da[sb & 1] : f32x16{}, 0, 0, 0);
+      };
+      auto dkv = [&](auto sc, auto jc) {  // dV / dK products of channel block j / 2, key half j % 2
+        constexpr int sb = decltype(sc)::value, j = decltype(jc)::value;
+        constexpr int db = j >> 1, h = j & 1;
+        dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_xt(sO, sb * 32 + h * 16, db, tb), pb[sb & 1][h],
+                                                            dvacc[db], 0, 0, 0);
+        dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_xt(sQ, sb * 32 + h * 16, db, tb), dsb[sb & 1][h],
+                                                            dkacc[db], 0, 0, 0);
+      };
+      f32x4 l4, d4;  // row values of the current group of four scores
+      auto rows = [&](auto sc, auto gc) {
+        constexpr int sb = decltype(sc)::value, gq = decltype(gc)::value;
+        const int r4 = sb * 32 + 8 * gq + 4 * hl;
+        l4 = *(const f32x4*)(sL + r4);
+        d4 = *(const f32x4*)(sDl + r4);
+      };
+      auto elem = [&](auto sc, auto ic) {  // score i of the lane: P and dA (unmasked)
+        constexpr int sb = decltype(sc)::value, i = decltype(ic)::value;
+        constexpr int e = i & 3;
+        const int qi = q0 + sb * 32 + 8 * (i >> 2) + 4 * hl + e;
+        float dfac;
+        const float f = score_f<SCORE>(a, sa[sb & 1][i], qi, kj, slope, dfac);
+        const float p = fast_exp2(fmaf(f, kLog2e, -l4[e]));
+        float dA = p * (da[sb & 1][i] - d4[e]);
+        if constexpr (SCORE & FA_SCORE_SOFTCAP) dA *= dfac;
+        pb[sb & 1][i >> 3][i & 7] = (__bf16)p;
+        dsb[sb & 1][i >> 3][i & 7] = (__bf16)dA;
+      };
+      auto mask_sub = [&](auto sc) {  // partial tiles: masked pairs get P = dA = 0
+        constexpr int sb = decltype(sc)::value;
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
-          const int r4 = sub * 32 + 8 * gq + 4 * hl;
-          const f32x4 l4 = *(const f32x4*)(sL + r4);
-          const f32x4 d4 = *(const f32x4*)(sDl + r4);
+          const int r4 = sb * 32 + 8 * gq + 4 * hl;
           const i32x4 c4 = *(const i32x4*)(sDoc + r4);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = 4 * gq + e;
-            const int qi = q0 + r4 + e;
-            float dfac;
-            const float f = score_f<SCORE>(a, sacc[i], qi, kj, slope, dfac);
-            float p = fast_exp2(fmaf(f, kLog2e, -l4[e]));
-            if (masked) p = mask_pair(ms, qi, kj, c4[e], kdoc) ? p : 0.f;
-            float da = p * (dpacc[i] - d4[e]);
-            if constexpr (SCORE & FA_SCORE_SOFTCAP) da *= dfac;
-            pb[i >> 3][i & 7] = (__bf16)p;
-            dsb[i >> 3][i & 7] = (__bf16)da;
+            if (!pair_ok(pm, q0 + r4 + e, kj, c4[e], kdoc)) {
+              pb[sb & 1][i >> 3][i & 7] = (__bf16)0.0f;
+              dsb[sb & 1][i >> 3][i & 7] = (__bf16)0.0f;
+            }
           }
         }
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_xt(sO, sub * 32 + h * 16, db, tb), pb[h],
-                                                                dvacc[db], 0, 0, 0);
-            dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_xt(sQ, sub * 32 + h * 16, db, tb), dsb[h],
-                                                                dkacc[db], 0, 0, 0);
+      };
+      bwd_static_for<8>([&](auto kc) { sdp(std::integral_constant<int, 0>{}, kc); });
+      bwd_static_for<QR / 32>([&](auto sc) {
+        constexpr int sb = decltype(sc)::value;
+        constexpr bool PREV = sb > 0, NEXT = sb + 1 < QR / 32;
+        __builtin_amdgcn_sched_barrier(0);
+        bwd_static_for<16>([&](auto ic) {
+          constexpr int i = decltype(ic)::value;
+          if constexpr ((i & 3) == 0) rows(sc, std::integral_constant<int, i / 4>{});
+          if constexpr ((i & 1) == 0) {
+            if constexpr (PREV) dkv(std::integral_constant<int, sb - 1>{}, std::integral_constant<int, i / 2>{});
+          } else {
+            if constexpr (NEXT) sdp(std::integral_constant<int, sb + 1>{}, std::integral_constant<int, i / 2>{});
           }
-        }
-      }
+          elem(sc, ic);
+          __builtin_amdgcn_sched_barrier(0);
+        });
+        if (masked) mask_sub(sc);
+      });
+      bwd_static_for<8>([&](auto jc) { dkv(std::integral_constant<int, QR / 32 - 1>{}, jc); });
     }
   }
 
