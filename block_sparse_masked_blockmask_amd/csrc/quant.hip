@@ -376,13 +376,10 @@ __device__ __forceinline__ void qcompute(const QuantFwdArgs& a, const QCtx& c, c
   // Exact running maximum (P <= 1 keeps 448 P inside the E4M3 range).
   const float m_new = fmaxf(st.m_run, mx);
   const bool raise = m_new > st.m_run;
-  if (__builtin_amdgcn_readfirstlane(__ballot(raise) != 0)) {
-    const float alpha = raise ? fast_exp2(st.m_run - m_new) : 1.0f;
-    st.l_run *= alpha;
-#pragma unroll
-    for (int db = 0; db < 4; ++db) st.oacc[db] *= alpha;
-    st.m_run = m_new;
-  }
+  // The numerators and P.V products follow in two copies, one per outcome of the rescale test:
+  // with one copy after a conditional rescale, the compiler kept O in two register sets and copied
+  // all 64 accumulators on every step.
+  auto finish = [&]() {
   // P^T as the fp8 B operand: byte j of the 32 holds key position (j / 16, element j % 16).
   // 448 P <= 448 up to the exponential's last-place error, far below 464, where the conversion
   // stops rounding to 448.
@@ -414,6 +411,17 @@ __device__ __forceinline__ void qcompute(const QuantFwdArgs& a, const QCtx& c, c
     }
     // Formats 0/0: both operands E4M3; scale exponents 127 mean a factor of 1.
     st.oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pb, st.oacc[db], 0, 0, 0, 127, 0, 127);
+  }
+  };
+  if (__builtin_amdgcn_readfirstlane(__ballot(raise) != 0)) {
+    const float alpha = raise ? fast_exp2(st.m_run - m_new) : 1.0f;
+    st.l_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) st.oacc[db] *= alpha;
+    st.m_run = m_new;
+    finish();
+  } else {
+    finish();
   }
 }
 
