@@ -1078,7 +1078,7 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_split_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) float sK[KV_FLOATS];
   __shared__ __attribute__((aligned(16))) float sV[KV_FLOATS];
   __shared__ float sQ[32 * P];
-  __shared__ int sDoc[BK];
+  __shared__ __attribute__((aligned(16))) int sDoc[BK];
   __shared__ float s_m[4][32];
   __shared__ float s_l[4][32];
 
@@ -1107,7 +1107,10 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_split_kernel(FwdArgs a) {
   }
   const int qdoc = ((a.flags & FA_MASK_DOC) && q_in) ? a.q_doc[(int64_t)it.b * a.Lq + qi] : 0;
   const float slope = (SCORE & FA_SCORE_ALIBI) ? a.slopes[it.hq] * a.slope_mul : 0.f;
-  const MaskSpec ms{a.flags, a.window, a.prefix_len};
+  // This lane's allowed key interval [klo, khi) under the index predicates and the key count.
+  int klo, khi;
+  key_interval(a, qi, klo, khi);
+  const bool docm = (a.flags & FA_MASK_DOC) != 0;
 
   f32x16 oacc[4];
 #pragma unroll
@@ -1173,18 +1176,21 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_split_kernel(FwdArgs a) {
         for (int db = 0; db < 4; ++db) vf[i * 4 + db] = sV[r * P + db * 32 + lq];
       }
 
+      // Mask without branches: the key interval and, under DOC, the ids of 4 keys per LDS read.
       float mx = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int kv = kv0 + nb * 32 + (i >> 2) * 8 + hl * 4 + (i & 3);
-        float x = score_log2<SCORE>(a, sacc[i], qi, kv, slope);
-        if (masked) {
-          const int kvdoc = (a.flags & FA_MASK_DOC) ? sDoc[kv - kv0] : 0;
-          const bool keep = kv < a.Lkv && mask_pair(ms, qi, kv, qdoc, kvdoc);
+      for (int g = 0; g < 4; ++g) {
+        const i32x4 kd4 = *(const i32x4*)(sDoc + nb * 32 + g * 8 + hl * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * g + e;
+          const int kv = kv0 + nb * 32 + g * 8 + hl * 4 + e;
+          float x = score_log2<SCORE>(a, sacc[i], qi, kv, slope);
+          const bool keep = !masked | ((kv >= klo) & (kv < khi) & (!docm | (kd4[e] == qdoc)));
           x = keep ? x : -INFINITY;
+          sacc[i] = x;
+          mx = fmaxf(mx, x);
         }
-        sacc[i] = x;
-        mx = fmaxf(mx, x);
       }
       mx = half_swap_max(mx);
       const float m_new = fmaxf(m_run, mx);
