@@ -41,6 +41,8 @@ FP32_PEAK_TFLOPS = 157.3
 INT8_FP8_PEAK_TOPS = 5033.2  # dense int8 / fp8 MFMA (2x bf16)
 KERNEL_SOURCES = ["block_sparse_masked_blockmask_amd/csrc/fwd.hip",
                   "block_sparse_masked_blockmask_amd/csrc/fwd_dense.hip",
+                  "block_sparse_masked_blockmask_amd/csrc/fwd_pipe.hip",
+                  "block_sparse_masked_blockmask_amd/csrc/work_order.h",
                   "block_sparse_masked_blockmask_amd/csrc/quant.hip",
                   "block_sparse_masked_blockmask_amd/csrc/device_common.h",
                   "block_sparse_masked_blockmask_amd/csrc/tile_class.h"]
@@ -334,8 +336,14 @@ class Case:
             return "fwd_quant_kernel"
         if self.w.dtype != "bf16":
             return "fwd_f32_kernel"
-        # bf16 without a BlockMask runs the software-pipelined every-tile-full kernel.
-        return "fwd_bf16_kernel" if self.bm is not None else "fwd_bf16_dense_kernel"
+        # bf16 without a BlockMask runs the software-pipelined every-tile-full kernel; with a
+        # BlockMask of 128-query blocks and a mask without document ids, the software-pipelined
+        # block-sparse kernel.
+        if self.bm is None:
+            return "fwd_bf16_dense_kernel"
+        if self.launch["q_block"] == 128 and not self.w.doc:
+            return "fwd_bf16_pipe_kernel"
+        return "fwd_bf16_kernel"
 
     def flops(self) -> float:
         return 4.0 * self.w.D * allowed_pairs(self.w) * self.w.Hq

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libflexattn.so")
-SOURCES = ["api.cpp", "blockmask.hip", "fwd.hip", "fwd_dense.hip", "quant.hip", "bwd.hip", "noalloc.hip"]
+SOURCES = ["api.cpp", "blockmask.hip", "fwd.hip", "fwd_dense.hip", "fwd_pipe.hip", "quant.hip", "bwd.hip", "noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

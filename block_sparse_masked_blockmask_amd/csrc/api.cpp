@@ -503,8 +503,14 @@ fa_status fwd_impl(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, c
     a.part_o = static_cast<float*>(workspace);
     a.part_lse = a.part_o + (size_t)nsplit * B * q->H * Lq * 128;
   }
+  // bf16 with a BlockMask of 128-query blocks and a mask without document ids (one key interval
+  // per query) runs the software-pipelined block-sparse kernel; document masks, 256-query blocks,
+  // split-KV and fp32 run the kernels of fwd.hip.
+  const bool pipe = !dense && dt == FA_BF16 && nsplit == 1 && bm != nullptr && q_block == 128 &&
+                    !(mask_kind & FA_MASK_DOC);
   hipError_t e = dense ? fa::launch_fwd_dense(a, score_kind, stream)
-                       : fa::launch_fwd(a, dt == FA_BF16 ? 1 : 0, q_block, kv_block, score_kind, stream);
+                 : pipe ? fa::launch_fwd_pipe(a, kv_block, score_kind, stream)
+                        : fa::launch_fwd(a, dt == FA_BF16 ? 1 : 0, q_block, kv_block, score_kind, stream);
   if (e != hipSuccess) return fail(FA_ERR_DEVICE, "forward launch failed: %s", hipGetErrorString(e));
   if (nsplit > 1) {
     fa::MergeArgs m{};

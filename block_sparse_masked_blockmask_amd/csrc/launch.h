@@ -182,6 +182,9 @@ hipError_t launch_fwd(const FwdArgs& a, int dtype, int q_block, int kv_block, in
 hipError_t launch_splitkv_merge(const MergeArgs& m, hipStream_t stream);
 // bf16 forward with every tile full (no BlockMask), software-pipelined, 256-query blocks.
 hipError_t launch_fwd_dense(const FwdArgs& a, int score, hipStream_t stream);
+// bf16 block-sparse forward, software-pipelined, 128-query blocks, masks without document ids
+// (nsplit 1); kv_block in {64, 128}.
+hipError_t launch_fwd_pipe(const FwdArgs& a, int kv_block, int score, hipStream_t stream);
 // Backward: delta/lse2 preparation, dq (+ slope partials), dk/dv, slope reduction.
 hipError_t launch_bwd(const BwdArgs& a, int score, hipStream_t stream);
 hipError_t launch_block_mask_transpose(const TransposeArgs& t, hipStream_t stream);

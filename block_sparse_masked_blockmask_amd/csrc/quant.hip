@@ -13,6 +13,8 @@
 // then times scale_Q * scale_K * sm_scale) and O^T += V8^T P8^T on the 32x32x64 fp8 MFMA.
 #include <hip/hip_runtime.h>
 
+#include <cfloat>
+
 #include <climits>
 
 #include "device_common.h"
@@ -279,7 +281,10 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream) {
 // ---------------------------------------------------------------------------------------------
 // Quantized forward. One workgroup of 4 waves per (batch, query head, 128-query block); wave w
 // owns 32 queries, as in the bf16 kernel. Keys in steps of 64: the int8 K rows and fp8 V rows
-// of a step (8 KB each) stream into one of two LDS buffers with global_load_lds_dwordx4.
+// of a step (8 KB each) stream into a ring of kQBuf LDS buffers with global_load_lds_dwordx4,
+// kQBuf - 1 steps ahead of the step being computed (64 KB of LDS, two workgroups per CU). A step's
+// int8 and fp8 products take half the time of the bf16 ones, so one step of lead time left each
+// step waiting for its transfers.
 //
 // LDS rows are 128 bytes (8 chunks of 16); chunk c of row r is stored at position c ^ ((r/2)%8),
 // which spreads 16 consecutive rows read at one chunk over distinct banks. V rows are stored
@@ -291,14 +296,25 @@ namespace {
 
 constexpr int kQStep = 64;
 constexpr int kQStepBytes = kQStep * 128;
+constexpr int kQBuf = 4;  // LDS ring buffers (steps in flight: kQBuf - 1)
 
+// Each buffer is a distinct LDS object named at compile time, so that the compiler does not wait
+// for the transfers into the other buffers before reading one.
 __shared__ __attribute__((aligned(1024))) unsigned char q_k0[kQStepBytes];
 __shared__ __attribute__((aligned(1024))) unsigned char q_v0[kQStepBytes];
 __shared__ __attribute__((aligned(1024))) unsigned char q_k1[kQStepBytes];
 __shared__ __attribute__((aligned(1024))) unsigned char q_v1[kQStepBytes];
+__shared__ __attribute__((aligned(1024))) unsigned char q_k2[kQStepBytes];
+__shared__ __attribute__((aligned(1024))) unsigned char q_v2[kQStepBytes];
+__shared__ __attribute__((aligned(1024))) unsigned char q_k3[kQStepBytes];
+__shared__ __attribute__((aligned(1024))) unsigned char q_v3[kQStepBytes];
 
-template <int B> __device__ __forceinline__ unsigned char* qkbuf() { return B ? q_k1 : q_k0; }
-template <int B> __device__ __forceinline__ unsigned char* qvbuf() { return B ? q_v1 : q_v0; }
+template <int B> __device__ __forceinline__ unsigned char* qkbuf() {
+  return B == 0 ? q_k0 : B == 1 ? q_k1 : B == 2 ? q_k2 : q_k3;
+}
+template <int B> __device__ __forceinline__ unsigned char* qvbuf() {
+  return B == 0 ? q_v0 : B == 1 ? q_v1 : B == 2 ? q_v2 : q_v3;
+}
 
 __device__ __forceinline__ int qswz(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int qoff(int r, int chunk) { return r * 128 + ((chunk ^ qswz(r)) << 4); }
@@ -308,7 +324,21 @@ __device__ __forceinline__ int vperm(int p) { return (p & ~15) | ((p & 3) | ((p 
 __device__ __forceinline__ void qdma16(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, 0);
 }
-__device__ __forceinline__ void qwait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// The compiler does not track the LDS writes of global_load_lds: wait for them explicitly, with at
+// most N vector-memory operations of this wave still outstanding.
+template <int N> __device__ __forceinline__ void qwait_vmem() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Workgroup barrier without the memory fence of __syncthreads(): that fence makes the compiler
+// wait for every outstanding transfer into LDS (vmcnt(0)), including the ones for later steps.
+// Each wave has waited for its own transfers of the step explicitly, and its LDS reads of the
+// previous step have returned before their products; the empty asm statements keep the compiler
+// from moving LDS accesses or transfers across the barrier.
+__device__ __forceinline__ void qbarrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 struct QCtx {
   int wave, lane, hl, lq, g16, s16, qi;
@@ -317,6 +347,12 @@ struct QCtx {
   const unsigned char* vp;
   const float* ks;   // K block scales of this (b, hkv)
   float qscale;      // scale_Q * sm_scale * log2(e)
+  int koff, voff;    // byte offsets of this lane's first K and V transfer chunks from a step's row 0
+  // Byte offsets in a step buffer of this lane's first K-operand read (row lq, chunk hl) and first
+  // transposed V read; the others follow by XOR and add (the swizzle's fields are disjoint bit
+  // ranges): K sub-block nb, k-step ks at (kx0 ^ 32 ks) + 4096 nb; V channel block db, row group rr
+  // at (vx0 ^ 32 db) + 2048 rr.
+  int kx0, vx0;
 };
 
 struct QState {
@@ -326,16 +362,30 @@ struct QState {
 
 template <int B>
 __device__ __forceinline__ void qissue(const QuantFwdArgs& a, const QCtx& c, int kv0) {
-  // 8 KB per tensor = 8 segments of 1 KB (8 rows); wave w loads segments w and w + 4.
+  // 8 KB per tensor = 8 segments of 1 KB (8 rows); wave w loads segments w and w + 4, physical rows
+  // 8 w + lane / 8 and 32 more. The chunk swizzle and the V row order repeat every 16 rows, so the
+  // second segment's lane offsets are the first's plus 32 rows: a step inside the keys needs only
+  // the uniform row address and the lane's constant offsets.
+  if (kv0 + kQStep <= a.Lkv) {
+    const signed char* kb = c.kp + (int64_t)kv0 * a.k_sl;
+    const unsigned char* vb = c.vp + (int64_t)kv0 * a.v_sl;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int seg = i * 4 + c.wave;
-    const int p = seg * 8 + (c.lane >> 3);  // physical row written by this lane
-    const int pos = c.lane & 7;             // physical chunk position
-    const int kr = min(kv0 + p, a.Lkv - 1);
-    const int vr = min(kv0 + vperm(p), a.Lkv - 1);
-    qdma16(c.kp + (int64_t)kr * a.k_sl + ((pos ^ qswz(p)) << 4), qkbuf<B>() + seg * 1024);
-    qdma16(c.vp + (int64_t)vr * a.v_sl + ((pos ^ qswz(p)) << 4), qvbuf<B>() + seg * 1024);
+    for (int i = 0; i < 2; ++i) {
+      const int seg = i * 4 + c.wave;
+      qdma16(kb + (int64_t)(32 * i) * a.k_sl + c.koff, qkbuf<B>() + seg * 1024);
+      qdma16(vb + (int64_t)(32 * i) * a.v_sl + c.voff, qvbuf<B>() + seg * 1024);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int seg = i * 4 + c.wave;
+      const int p = seg * 8 + (c.lane >> 3);  // physical row written by this lane
+      const int pos = c.lane & 7;             // physical chunk position
+      const int kr = min(kv0 + p, a.Lkv - 1);
+      const int vr = min(kv0 + vperm(p), a.Lkv - 1);
+      qdma16(c.kp + (int64_t)kr * a.k_sl + ((pos ^ qswz(p)) << 4), qkbuf<B>() + seg * 1024);
+      qdma16(c.vp + (int64_t)vr * a.v_sl + ((pos ^ qswz(p)) << 4), qvbuf<B>() + seg * 1024);
+    }
   }
 }
 
@@ -348,31 +398,41 @@ __device__ __forceinline__ void qcompute(const QuantFwdArgs& a, const QCtx& c, c
                                          int kv0, float2 kscale) {
   const unsigned char* sK = qkbuf<B>();
   const unsigned char* sV = qvbuf<B>();
+  // Re-defined here (no instruction is emitted) so that the compiler forms buffer + offset inside
+  // the step, where the buffer address folds into the instruction's immediate offset, instead of
+  // keeping one hoisted register per buffer and read.
+  int kx0 = c.kx0, vx0 = c.vx0;
+  asm volatile("" : "+v"(kx0), "+v"(vx0));
   // S^T = K8 Q8^T: exact int32 dot products, 4 k-steps of 32 channels per 32-key sub-block.
   i32x16 iacc[2];
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
-    const int r = nb * 32 + c.lq;
     iacc[nb] = i32x16{};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const i32x4 kf = *(const i32x4*)(sK + qoff(r, 2 * ks + c.hl));
+      const i32x4 kf = *(const i32x4*)(sK + nb * 4096 + (kx0 ^ (32 * ks)));
       iacc[nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qreg[ks], iacc[nb], 0, 0, 0);
     }
   }
-  const float scs[2] = {c.qscale * kscale.x, c.qscale * kscale.y};  // per 32-key sub-block
+  // Per 32-key sub-block: the log2-domain score of a product is its value times the sub-block's
+  // scale. The row maximum is taken on the products of each sub-block and scaled once (rounding is
+  // monotone, so this is the maximum of the rounded scores); the exponent below applies the scale
+  // in its FMA. A zero scale (an all-zero block) is raised to the smallest normal float, so that a
+  // masked product (-inf) stays -inf instead of giving -inf * 0; the scores it gives (at most
+  // 2^21 times that) are zero to fp32 precision once the maximum is subtracted.
+  const float scs[2] = {fmaxf(c.qscale * kscale.x, FLT_MIN), fmaxf(c.qscale * kscale.y, FLT_MIN)};
   float t[2][16];
-  float mx = -INFINITY;
+  float mxs[2] = {-INFINITY, -INFINITY};
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int kv = kv0 + nb * 32 + (i >> 2) * 8 + c.hl * 4 + (i & 3);
-      t[nb][i] = (!RAGGED || kv < a.Lkv) ? (float)iacc[nb][i] * scs[nb] : -INFINITY;
-      mx = fmaxf(mx, t[nb][i]);
+      t[nb][i] = (!RAGGED || kv < a.Lkv) ? (float)iacc[nb][i] : -INFINITY;
+      mxs[nb] = fmaxf(mxs[nb], t[nb][i]);
     }
   }
-  mx = half_swap_max(mx);
+  float mx = half_swap_max(fmaxf(mxs[0] * scs[0], mxs[1] * scs[1]));
   // Exact running maximum (P <= 1 keeps 448 P inside the E4M3 range).
   const float m_new = fmaxf(st.m_run, mx);
   const bool raise = m_new > st.m_run;
@@ -388,8 +448,10 @@ __device__ __forceinline__ void qcompute(const QuantFwdArgs& a, const QCtx& c, c
 #pragma unroll
   for (int w = 0; w < 8; ++w) {
     const int nb = w >> 2, i0 = (w & 3) * 4;
-    const float p0 = fast_exp2(t[nb][i0] - m448), p1 = fast_exp2(t[nb][i0 + 1] - m448);
-    const float p2 = fast_exp2(t[nb][i0 + 2] - m448), p3 = fast_exp2(t[nb][i0 + 3] - m448);
+    const float p0 = fast_exp2(fmaf(t[nb][i0], scs[nb], -m448));
+    const float p1 = fast_exp2(fmaf(t[nb][i0 + 1], scs[nb], -m448));
+    const float p2 = fast_exp2(fmaf(t[nb][i0 + 2], scs[nb], -m448));
+    const float p3 = fast_exp2(fmaf(t[nb][i0 + 3], scs[nb], -m448));
     st.l_run += (p0 + p1) + (p2 + p3);
     int word = 0;
     word = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, word, false);
@@ -400,12 +462,10 @@ __device__ __forceinline__ void qcompute(const QuantFwdArgs& a, const QCtx& c, c
   // row base + s/2 and channels d0 + 8*(s%2); lane i receives channel d0 + i of rows base..+7.
 #pragma unroll
   for (int db = 0; db < 4; ++db) {
-    const int d = db * 32 + 16 * (c.g16 & 1) + 8 * (c.s16 & 1);
     i32x8 vf;
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
-      const int p = rr * 16 + (c.g16 >> 1) * 8 + (c.s16 >> 1);
-      const i32x2 v2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(sV + qoff(p, d >> 4) + (d & 15)));
+      const i32x2 v2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(sV + rr * 2048 + (vx0 ^ (32 * db))));
       vf[2 * rr] = v2[0];
       vf[2 * rr + 1] = v2[1];
     }
@@ -427,6 +487,8 @@ __device__ __forceinline__ void qcompute(const QuantFwdArgs& a, const QCtx& c, c
 
 }  // namespace
 
+// QKB: tokens per Q/K scale (128 or 32).
+template <int QKB>
 __global__ __launch_bounds__(256, 2) void fwd_quant_kernel(QuantFwdArgs a) {
   int w = xcd_remap(blockIdx.x, a.total_wg);
   const int g = w % a.group;
@@ -448,36 +510,59 @@ __global__ __launch_bounds__(256, 2) void fwd_quant_kernel(QuantFwdArgs a) {
   c.kp = a.k + b * a.k_sb + hkv * a.k_sh;
   c.vp = a.v + b * a.v_sb + hkv * a.v_sh;
   c.ks = a.k_scale + ((int64_t)b * a.Hkv + hkv) * a.nkb;
+  {
+    const int p0 = c.wave * 8 + (c.lane >> 3), ch = ((c.lane & 7) ^ qswz(p0)) << 4;
+    c.koff = p0 * (int)a.k_sl + ch;
+    c.voff = vperm(p0) * (int)a.v_sl + ch;
+  }
+  c.kx0 = qoff(c.lq, c.hl);
+  {
+    const int d0 = 16 * (c.g16 & 1) + 8 * (c.s16 & 1);
+    c.vx0 = qoff((c.g16 >> 1) * 8 + (c.s16 >> 1), d0 >> 4) + (d0 & 15);
+  }
   // Q scale of this wave's 32 queries: one per 128-query block, or one per wave (32-token
   // blocks); a wave past the end reads the last block's scale (its rows are not written).
-  const int qsb = a.qk_block == 32 ? min(qb * 4 + c.wave, a.nqb - 1) : qb;
+  const int qsb = QKB == 32 ? min(qb * 4 + c.wave, a.nqb - 1) : qb;
   c.qscale = a.q_scale[((int64_t)b * a.Hq + hq) * a.nqb + qsb] * a.scale_log2;
 
   const int nsteps = (a.Lkv + kQStep - 1) / kQStep;
   // K scales of step s for its two 32-key sub-blocks: a 64-key step lies inside one 128-key
   // block; with 32-token blocks each sub-block has its own (past the end: the last one, whose
-  // keys are masked). Each step's scales are loaded with its transfers, one step ahead, so
-  // that their wait is the step's own.
+  // keys are masked). Each step's scales are loaded with its transfers, so that their wait is the
+  // step's own.
+  // Read through the constant address space (the scales do not change during the kernel): with a
+  // uniform address these are scalar loads, which the vector-memory waits of the steps do not
+  // count, and the values stay in scalar registers.
+  const __attribute__((address_space(4))) float* ksv = (const __attribute__((address_space(4))) float*)c.ks;
   auto kscales = [&](int kv0) {
-    if (a.qk_block == 32) {
+    if constexpr (QKB == 32) {
       const int i0 = kv0 >> 5;
-      return make_float2(c.ks[i0], c.ks[min(i0 + 1, a.nkb - 1)]);
+      const float x = ksv[i0];
+      const float y = ksv[min(i0 + 1, a.nkb - 1)];
+      return make_float2(x, y);
     }
-    const float x = c.ks[kv0 >> 7];
+    const float x = ksv[kv0 >> 7];
     return make_float2(x, x);
   };
-  float2 ks_cur = make_float2(0.f, 0.f);
-  if (nsteps > 0) {
-    qissue<0>(a, c, 0);
-    ks_cur = kscales(0);
-  }
+  constexpr int OPS = 4;  // vector-memory operations per lane and step (the transfers)
+  static_assert(kQBuf == 4, "the prologue and the step loop below are written for four buffers");
 
-  // Q8^T as the int8 B operand: lane holds Q8[qi][32*ks + 16*hl .. +16] for ks = 0..3.
+  // Q8^T as the int8 B operand: lane holds Q8[qi][32*ks + 16*hl .. +16] for ks = 0..3. Loaded
+  // before the prologue's transfers, so that it is in when the first step's are.
   const signed char* qp = a.q + b * a.q_sb + hq * a.q_sh;
   i32x4 qreg[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
     qreg[ks] = c.q_in ? *(const i32x4*)(qp + (int64_t)c.qi * a.q_sl + ks * 32 + c.hl * 16) : i32x4{};
+
+  // Prologue: steps 0 .. kQBuf-2 in flight.
+  float2 ks_ring[kQBuf];
+#pragma unroll
+  for (int j = 0; j < kQBuf; ++j) ks_ring[j] = make_float2(0.f, 0.f);
+  if (nsteps > 0) { qissue<0>(a, c, 0); ks_ring[0] = kscales(0); }
+  if (nsteps > 1) { qissue<1>(a, c, kQStep); ks_ring[1] = kscales(kQStep); }
+  if (nsteps > 2) { qissue<2>(a, c, 2 * kQStep); ks_ring[2] = kscales(2 * kQStep); }
+
 
   QState st;
 #pragma unroll
@@ -485,29 +570,30 @@ __global__ __launch_bounds__(256, 2) void fwd_quant_kernel(QuantFwdArgs a) {
   st.m_run = -INFINITY;
   st.l_run = 0.f;
 
-  for (int s = 0; s < nsteps; s += 2) {
-    qwait_vmem();
-    __syncthreads();
-    float2 ks_nxt = make_float2(0.f, 0.f);
-    if (s + 1 < nsteps) {
-      qissue<1>(a, c, (s + 1) * kQStep);
-      ks_nxt = kscales((s + 1) * kQStep);
+  // Step s: wait for its transfers (the kQBuf - 2 later steps' may stay in flight; near the end,
+  // where fewer were issued, for all), make sure every wave is done with the buffer about to be
+  // refilled (step s - 1's), refill it with step s + kQBuf - 1, compute.
+  auto step = [&](auto bufc, int s) {
+    constexpr int B = decltype(bufc)::value;
+    constexpr int NB = (B + kQBuf - 1) % kQBuf;
+    if (s + kQBuf - 2 < nsteps) qwait_vmem<(kQBuf - 2) * OPS>();
+    else qwait_vmem<0>();
+    qbarrier();
+    const int sn = s + kQBuf - 1;
+    if (sn < nsteps) {
+      qissue<NB>(a, c, sn * kQStep);
+      ks_ring[NB] = kscales(sn * kQStep);
     }
-    if ((s + 1) * kQStep <= a.Lkv) qcompute<0, false>(a, c, qreg, st, s * kQStep, ks_cur);
-    else qcompute<0, true>(a, c, qreg, st, s * kQStep, ks_cur);
-    ks_cur = ks_nxt;
-    if (s + 1 < nsteps) {
-      qwait_vmem();
-      __syncthreads();
-      if (s + 2 < nsteps) {
-        qissue<0>(a, c, (s + 2) * kQStep);
-        ks_nxt = kscales((s + 2) * kQStep);
-      }
-      if ((s + 2) * kQStep <= a.Lkv) qcompute<1, false>(a, c, qreg, st, (s + 1) * kQStep, ks_cur);
-      else qcompute<1, true>(a, c, qreg, st, (s + 1) * kQStep, ks_cur);
-      ks_cur = ks_nxt;
-    }
+    if ((s + 1) * kQStep <= a.Lkv) qcompute<B, false>(a, c, qreg, st, s * kQStep, ks_ring[B]);
+    else qcompute<B, true>(a, c, qreg, st, s * kQStep, ks_ring[B]);
+  };
+  for (int s = 0; s < nsteps; s += kQBuf) {
+    step(std::integral_constant<int, 0>{}, s);
+    if (s + 1 < nsteps) step(std::integral_constant<int, 1>{}, s + 1);
+    if (s + 2 < nsteps) step(std::integral_constant<int, 2>{}, s + 2);
+    if (s + 3 < nsteps) step(std::integral_constant<int, 3>{}, s + 3);
   }
+  qwait_vmem<0>();  // no transfer may outlive the workgroup's LDS
 
   // Epilogue: out = O * scale_V[channel] / (448 l), bf16 (l_tot is already 448 l); lse in
   // natural log.
@@ -516,17 +602,23 @@ __global__ __launch_bounds__(256, 2) void fwd_quant_kernel(QuantFwdArgs a) {
   if (c.q_in) {
     const float* vs = a.v_scale + ((int64_t)b * a.Hkv + hkv) * 128;
     __bf16* op = a.o + b * a.o_sb + hq * a.o_sh + (int64_t)c.qi * a.o_sl;
+    // All channel scales first: interleaved with the stores, each load waited for the one before.
+    f32x4 s4[4][4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) s4[db][gq] = *(const f32x4*)(vs + db * 32 + gq * 8 + c.hl * 4);
+    }
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
         const int d = db * 32 + gq * 8 + c.hl * 4;
-        const f32x4 s4 = *(const f32x4*)(vs + d);
         bf16x4 o4;
-        o4[0] = (__bf16)(st.oacc[db][gq * 4 + 0] * s4[0] * inv);
-        o4[1] = (__bf16)(st.oacc[db][gq * 4 + 1] * s4[1] * inv);
-        o4[2] = (__bf16)(st.oacc[db][gq * 4 + 2] * s4[2] * inv);
-        o4[3] = (__bf16)(st.oacc[db][gq * 4 + 3] * s4[3] * inv);
+        o4[0] = (__bf16)(st.oacc[db][gq * 4 + 0] * s4[db][gq][0] * inv);
+        o4[1] = (__bf16)(st.oacc[db][gq * 4 + 1] * s4[db][gq][1] * inv);
+        o4[2] = (__bf16)(st.oacc[db][gq * 4 + 2] * s4[db][gq][2] * inv);
+        o4[3] = (__bf16)(st.oacc[db][gq * 4 + 3] * s4[db][gq][3] * inv);
         *(bf16x4*)(op + d) = o4;
       }
     }
@@ -541,7 +633,8 @@ __global__ __launch_bounds__(256, 2) void fwd_quant_kernel(QuantFwdArgs a) {
 
 hipError_t launch_fwd_quant(const QuantFwdArgs& a, hipStream_t stream) {
   if (a.total_wg == 0) return hipSuccess;
-  hipLaunchKernelGGL(fwd_quant_kernel, dim3(a.total_wg), dim3(256), 0, stream, a);
+  if (a.qk_block == 32) hipLaunchKernelGGL(fwd_quant_kernel<32>, dim3(a.total_wg), dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL(fwd_quant_kernel<128>, dim3(a.total_wg), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
