@@ -266,9 +266,23 @@ __device__ __forceinline__ void dma4(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 4, 0, 0);
 }
 // The compiler does not track the LDS writes of global_load_lds: at most N vector-memory
-// operations of this wave may still be outstanding after this.
+// operations of this wave may still be outstanding after this. Emitted with the builtin, whose
+// encoding the compiler reads (vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at
+// their maxima), so that it also knows the older transfers are complete; an asm wait is opaque
+// to it, and it then waited for every transfer before reading a buffer filled earlier.
 template <int N> __device__ __forceinline__ void wait_vmem() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// Workgroup barrier without the memory fence of __syncthreads(): that fence makes the compiler
+// wait for every outstanding transfer into LDS (vmcnt(0)), including the next step's, which then
+// never overlaps the current step. Each wave waits for its own transfers of the step explicitly
+// (wait_vmem), and its LDS reads of a step have returned before their products or vector work;
+// the empty asm statements keep the compiler from moving LDS accesses or transfers across.
+__device__ __forceinline__ void step_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 struct Lane {
@@ -330,6 +344,7 @@ __device__ __forceinline__ void issue_rowvals(const Lane& c, const void* base, b
 // ---------------------------------------------------------------------------------------------
 // dQ (and the slope-gradient partials): one workgroup per (b, hq, 128-query block).
 // ---------------------------------------------------------------------------------------------
+
 template <int SCORE>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char sK0[kTileBytes];
@@ -367,6 +382,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     b = pair / a.Hkv;
     hq = hkv * a.group + g;
   }
+  // Wave-uniform, but computed by vector divisions: in scalar registers the K, V and document
+  // pointers derived from them stay scalar too (in vector registers they were spilled, and each
+  // reload inside a step's transfers waited for all of them).
+  qb = __builtin_amdgcn_readfirstlane(qb);
+  hq = __builtin_amdgcn_readfirstlane(hq);
+  hkv = __builtin_amdgcn_readfirstlane(hkv);
+  b = __builtin_amdgcn_readfirstlane(b);
   const Lane c = make_lane();
   const int hl = c.hl, lq = c.lq;
   const int qi = qb * 128 + c.wave * 32 + lq;
@@ -410,21 +432,43 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     part = a.kv_idx + r * a.nkvb;
   }
   const int nsteps = 2 * (nfull + npart);
+  // List entries, 64 per register: lane j holds the key block of tile chunk_base + j (without a
+  // BlockMask, block t itself). Steps are looked up in increasing order (each once, when it is
+  // issued), so the register moves forward only.
+  const int ntiles = nfull + npart;
+  auto load_chunk = [&](int base) -> int {
+    const int t = base + c.lane;
+    if (a.all_full || t >= ntiles) return t;
+    return t < nfull ? full[t] : part[t - nfull];
+  };
+  int chunk_base = 0;
+  int chunk = load_chunk(0);
   auto step_kv0 = [&](int s, bool& masked) {
     const int t = s >> 1;
+    if (t >= chunk_base + 64) {
+      chunk_base = t & ~63;
+      chunk = load_chunk(chunk_base);
+    }
     const bool partial = t >= nfull;
     // An entry outside [0, n_kvb) becomes n_kvb: its rows lie past the keys, so the transfers
     // clamp to the last key and every score of the step is masked (it adds nothing).
-    const int kb = partial ? sanitize_block(part[t - nfull], a.nkvb) : (a.all_full ? t : sanitize_block(full[t], a.nkvb));
+    const int kb = a.all_full ? t : sanitize_block(__builtin_amdgcn_readlane(chunk, t - chunk_base), a.nkvb);
     const int kv0 = kb * 128 + (s & 1) * kRows;
     masked = partial || kv0 + kRows > a.Lkv;
     return kv0;
   };
-  auto issue = [&](int s, unsigned char* sK, unsigned char* sV, int* sD) {
-    bool m;
-    const int kv0 = step_kv0(s, m);
-    issue_tiles(c, kp, a.k_sl, koff, vp, a.v_sl, voff, kv0, a.Lkv, sK, sV);
-    issue_rowvals(c, kvdoc, doc, kv0, a.Lkv, sD);
+  auto issue = [&](int kv0, unsigned char* sK, unsigned char* sV, int* sD) {
+    // Everything the transfers need is materialised before the first of them: the uniform bases
+    // in scalar registers and the lane offsets re-defined here (hoisted, pointer plus offset
+    // became one 64-bit register per tensor, kept across the loop and spilled). A value reloaded
+    // from scratch between two transfers waits for both, which leaves nothing in flight.
+    const __bf16* kpu = kp;
+    const __bf16* vpu = vp;
+    const int* kdu = kvdoc;
+    asm volatile("" : "+s"(kpu), "+s"(vpu), "+s"(kdu));
+    const int ko = launder(koff), vo = launder(voff);
+    issue_rowvals(c, kdu, doc, kv0, a.Lkv, sD);
+    issue_tiles(c, kpu, a.k_sl, ko, vpu, a.v_sl, vo, kv0, a.Lkv, sK, sV);
   };
 
   f32x16 dqacc[4];
@@ -432,17 +476,18 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   for (int db = 0; db < 4; ++db) dqacc[db] = f32x16{};
   float slope_acc = 0.f;
 
-  auto compute = [&](int s, const unsigned char* sK, const unsigned char* sV, const int* sD) {
-    bool masked;
-    const int kv0 = step_kv0(s, masked);
-    const int kx0 = launder(c.kx0), tb = launder(c.tb);
+  auto compute = [&](int kv0, bool masked, const unsigned char* sK, const unsigned char* sV, const int* sD) {
+    // The V reads take their own copy of the offset: with one, the compiler formed the V address
+    // as the K address plus the distance between the arrays, lost track of which buffer it reads,
+    // and waited for every transfer in flight (the next step's) before it.
+    const int kx0 = launder(c.kx0), kxv = launder(c.kx0), tb = launder(c.tb);
 #pragma unroll 1
     for (int nb = 0; nb < 2; ++nb) {
       f32x16 sacc = f32x16{}, dpacc = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_x(sK, nb * 32, ks, kx0), qreg[ks], sacc, 0, 0, 0);
-        dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_x(sV, nb * 32, ks, kx0), doreg[ks], dpacc, 0, 0, 0);
+        dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_x(sV, nb * 32, ks, kxv), doreg[ks], dpacc, 0, 0, 0);
       }
       sched_pairs<8>();
       bf16x8 dsb[2];
@@ -477,28 +522,43 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 
   // Two LDS buffers, selected at compile time (the loop handles two steps per iteration):
   // step s + 1 is issued into the other buffer before step s is waited for and computed.
-  if (nsteps > 0) issue(0, sK0, sV0, sD0);
+  // The row's operands are complete before the first transfer: loads still pending at the loop
+  // made the compiler wait for every outstanding transfer (vmcnt(0)) at their first use in each
+  // step, the next step's included.
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) asm volatile("" ::"v"(qreg[ks]), "v"(doreg[ks]));
+  asm volatile("" ::"v"(lse2), "v"(delta), "v"(qdoc), "v"(chunk));
+  // Each step's key offset is looked up once, when it is issued, and kept for its compute.
+  bool m0 = false, m1 = false;
+  int kv_0 = 0, kv_1 = 0;
+  if (nsteps > 0) {
+    kv_0 = step_kv0(0, m0);
+    issue(kv_0, sK0, sV0, sD0);
+  }
   for (int s = 0; s < nsteps; s += 2) {
     if (s + 1 < nsteps) {
-      issue(s + 1, sK1, sV1, sD1);
+      kv_1 = step_kv0(s + 1, m1);
+      issue(kv_1, sK1, sV1, sD1);
       wait_vmem<kOps>();
     } else {
       wait_vmem<0>();
     }
-    __syncthreads();
-    compute(s, sK0, sV0, sD0);
-    __syncthreads();
+    step_barrier();
+    compute(kv_0, m0, sK0, sV0, sD0);
+    step_barrier();
     if (s + 1 >= nsteps) break;
     if (s + 2 < nsteps) {
-      issue(s + 2, sK0, sV0, sD0);
+      kv_0 = step_kv0(s + 2, m0);
+      issue(kv_0, sK0, sV0, sD0);
       wait_vmem<kOps>();
     } else {
       wait_vmem<0>();
     }
-    __syncthreads();
-    compute(s + 1, sK1, sV1, sD1);
-    __syncthreads();
+    step_barrier();
+    compute(kv_1, m1, sK1, sV1, sD1);
+    step_barrier();
   }
+  wait_vmem<0>();  // no transfer may outlive the workgroup's LDS
 
   // dQ[qi][channel]: lane holds channels 32 db + 8 gq + 4 hl + 0..3 of its query.
   if (q_in) {
