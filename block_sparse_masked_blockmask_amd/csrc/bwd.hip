@@ -448,6 +448,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     if (t >= chunk_base + 64) {
       chunk_base = t & ~63;
       chunk = load_chunk(chunk_base);
+      asm volatile("" ::"v"(chunk));  // waited for here, not at every step's readlane
     }
     const bool partial = t >= nfull;
     // An entry outside [0, n_kvb) becomes n_kvb: its rows lie past the keys, so the transfers
