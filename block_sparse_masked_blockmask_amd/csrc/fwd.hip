@@ -747,6 +747,41 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(FwdArgs
     }
     return;
   }
+  if constexpr (WAVES == 4) {
+    // O goes out through LDS, so that each store writes whole rows: in registers a lane holds 4
+    // channels of each of 16 channel groups of its row, and stored from there every instruction
+    // wrote 16 bytes into each of 32 rows. Waves 0-1 stage their 32 x 256-byte rows in the first
+    // K buffer, waves 2-3 in the first V buffer (free once every wave is past its last step), in
+    // the swizzled tile layout; each wave reads back only its own rows.
+    __syncthreads();
+    unsigned char* const ob = (c.wave < 2 ? kbuf<0>() : vbuf<0>()) + (c.wave & 1) * (32 * 256);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        bf16x4 o4;
+        o4[0] = (__bf16)(st.oacc[db][gq * 4 + 0] * inv);
+        o4[1] = (__bf16)(st.oacc[db][gq * 4 + 1] * inv);
+        o4[2] = (__bf16)(st.oacc[db][gq * 4 + 2] * inv);
+        o4[3] = (__bf16)(st.oacc[db][gq * 4 + 3] * inv);
+        *(bf16x4*)(ob + tile_off(c.lq, db * 4 + gq) + c.hl * 8) = o4;
+      }
+    }
+    // Row r of the wave (4 rows per instruction), 16-byte chunk lane % 16.
+    __bf16* const op0 = (__bf16*)a.o + it.b * a.o_sb + it.hq * a.o_sh;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = 4 * j + (c.lane >> 4), ch = c.lane & 15;
+      const bf16x8 v8 = *(const bf16x8*)(ob + tile_off(r, ch));
+      const int q = c.qw0 + r;
+      if (q < a.Lq) *(bf16x8*)(op0 + (int64_t)q * a.o_sl + ch * 8) = v8;
+    }
+    if (c.q_in && a.lse && c.hl == 0) {
+      a.lse[((int64_t)it.b * a.Hq + it.hq) * a.Lq + c.qi] =
+          l_tot > 0.f ? (st.m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+    }
+    return;
+  }
   if (c.q_in) {
     __bf16* op = (__bf16*)a.o + it.b * a.o_sb + it.hq * a.o_sh + (int64_t)c.qi * a.o_sl;
 #pragma unroll

@@ -10,7 +10,9 @@
 // maximum of S(n) and the lazy rescale, issues the 16 products of S(n+1) beside the exponentials,
 // row sums and bf16 packing of P(n), then the 16 products of O += V(n)^T P(n). Here the steps come
 // from the BlockMask's tile lists (full tiles first, then partial ones), and on a partial tile or
-// the ragged last step the key interval of each query masks S(n) before its maximum is taken.
+// the ragged last step the key interval of each query masks S(n) before its maximum is taken. The
+// score_mod's vector work for S(n+1) runs beside the P(n).V(n) products, so iteration n starts
+// from transformed scores.
 // Unlike fwd.hip, a wave does not skip the 32x32 sub-blocks that its mask leaves empty: their
 // products run and their probabilities come out exactly 0.
 //
@@ -472,23 +474,35 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_pipe_kernel(FwdArgs a) {
   // lse = -inf).
   const float l_tot = half_swap_sum((st.l[0] + st.l[1]) + (st.l[2] + st.l[3]));
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-  if (c.q_in) {
-    __bf16* op = (__bf16*)a.o + it.b * a.o_sb + it.hq * a.o_sh + (int64_t)c.qi * a.o_sl;
+  // O goes out through LDS, so that each store writes whole rows (from the registers, each
+  // instruction wrote 16 bytes into each of 32 rows): waves 0-1 stage their 32 x 256-byte rows in
+  // the first K slot, waves 2-3 in the first V slot (free once every wave is past its last step),
+  // swizzled; each wave reads back only its own rows.
+  __syncthreads();
+  unsigned char* const ob = (c.wave < 2 ? p_k0 : p_v0) + (c.wave & 1) * (32 * 256);
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
+  for (int db = 0; db < 4; ++db) {
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        bf16x4 o4;
-        o4[0] = (__bf16)(st.o[db][gq * 4 + 0] * inv);
-        o4[1] = (__bf16)(st.o[db][gq * 4 + 1] * inv);
-        o4[2] = (__bf16)(st.o[db][gq * 4 + 2] * inv);
-        o4[3] = (__bf16)(st.o[db][gq * 4 + 3] * inv);
-        *(bf16x4*)(op + db * 32 + gq * 8 + c.hl * 4) = o4;
-      }
+    for (int gq = 0; gq < 4; ++gq) {
+      bf16x4 o4;
+      o4[0] = (__bf16)(st.o[db][gq * 4 + 0] * inv);
+      o4[1] = (__bf16)(st.o[db][gq * 4 + 1] * inv);
+      o4[2] = (__bf16)(st.o[db][gq * 4 + 2] * inv);
+      o4[3] = (__bf16)(st.o[db][gq * 4 + 3] * inv);
+      *(bf16x4*)(ob + tile_off(lq, db * 4 + gq) + c.hl * 8) = o4;
     }
-    if (a.lse && c.hl == 0)
-      a.lse[((int64_t)it.b * a.Hq + it.hq) * a.Lq + c.qi] = l_tot > 0.f ? (st.m + __log2f(l_tot)) * kLn2 : -INFINITY;
   }
+  // Row r of the wave (4 rows per instruction), 16-byte chunk lane % 16.
+  __bf16* const op0 = (__bf16*)a.o + it.b * a.o_sb + it.hq * a.o_sh;
+  const int qw0 = it.qb * 128 + c.wave * 32;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = 4 * j + (c.lane >> 4), ch = c.lane & 15;
+    const bf16x8 v8 = *(const bf16x8*)(ob + tile_off(r, ch));
+    if (qw0 + r < a.Lq) *(bf16x8*)(op0 + (int64_t)(qw0 + r) * a.o_sl + ch * 8) = v8;
+  }
+  if (c.q_in && a.lse && c.hl == 0)
+    a.lse[((int64_t)it.b * a.Hq + it.hq) * a.Lq + c.qi] = l_tot > 0.f ? (st.m + __log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
 template <int HALVES>
