@@ -561,9 +561,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   }
   wait_vmem<0>();  // no transfer may outlive the workgroup's LDS
 
-  // dQ[qi][channel]: lane holds channels 32 db + 8 gq + 4 hl + 0..3 of its query.
-  if (q_in) {
-    __bf16* op = (__bf16*)a.dq + b * a.dq_sb + hq * a.dq_sh + (int64_t)qi * a.dq_sl;
+  // dQ[qi][channel]: lane holds channels 32 db + 8 gq + 4 hl + 0..3 of its query. The rows go out
+  // through LDS so that each store writes whole 256-byte rows (from the registers, each store
+  // wrote 16 bytes into each of 32 rows): waves 0-1 stage their 32 rows in the first K tile,
+  // waves 2-3 in the first V tile (every wave has passed the barrier after its last step), and
+  // each wave reads back only its own rows.
+  {
+    unsigned char* const ob = (c.wave < 2 ? sK0 : sV0) + (c.wave & 1) * (32 * 256);
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
 #pragma unroll
@@ -571,8 +575,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
         bf16x4 o4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(dqacc[db][gq * 4 + e] * a.sm_scale);
-        *(bf16x4*)(op + db * 32 + gq * 8 + hl * 4) = o4;
+        *(bf16x4*)(ob + tile_off(lq, db * 4 + gq) + hl * 8) = o4;
       }
+    }
+    __bf16* const op0 = (__bf16*)a.dq + b * a.dq_sb + hq * a.dq_sh;
+    const int qw0 = qb * 128 + c.wave * 32;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = 4 * j + (c.lane >> 4), ch = c.lane & 15;
+      const bf16x8 v8 = *(const bf16x8*)(ob + tile_off(r, ch));
+      if (qw0 + r < a.Lq) *(bf16x8*)(op0 + (int64_t)(qw0 + r) * a.dq_sl + ch * 8) = v8;
     }
   }
   if constexpr (SCORE & FA_SCORE_ALIBI) {
@@ -777,9 +789,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
     }
   }
 
-  if (k_in) {
-    __bf16* kop = (__bf16*)a.dk + b * a.dk_sb + hkv * a.dk_sh + (int64_t)kj * a.dk_sl;
-    __bf16* vop = (__bf16*)a.dv + b * a.dv_sb + hkv * a.dv_sh + (int64_t)kj * a.dv_sl;
+  // dK and dV rows go out through LDS, as in the dQ kernel: wave w stages its 32 dK rows at
+  // sQ + 8 KB w and its 32 dV rows at sO + 8 KB w (after a barrier: the last step's tiles may
+  // still be read by other waves), and reads back only its own rows, 4 whole rows per store.
+  __syncthreads();
+  {
+    unsigned char* const kb8 = sQ + wave * (32 * 256);
+    unsigned char* const vb8 = sO + wave * (32 * 256);
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
 #pragma unroll
@@ -790,8 +806,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
           k4[e] = (__bf16)(dkacc[db][gq * 4 + e] * a.sm_scale);
           v4[e] = (__bf16)dvacc[db][gq * 4 + e];
         }
-        *(bf16x4*)(kop + db * 32 + gq * 8 + hl * 4) = k4;
-        *(bf16x4*)(vop + db * 32 + gq * 8 + hl * 4) = v4;
+        *(bf16x4*)(kb8 + tile_off(lq, db * 4 + gq) + hl * 8) = k4;
+        *(bf16x4*)(vb8 + tile_off(lq, db * 4 + gq) + hl * 8) = v4;
+      }
+    }
+    __bf16* const kop0 = (__bf16*)a.dk + b * a.dk_sb + hkv * a.dk_sh;
+    __bf16* const vop0 = (__bf16*)a.dv + b * a.dv_sb + hkv * a.dv_sh;
+    const int kw0 = kb * 128 + wave * 32;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = 4 * j + (lane >> 4), ch = lane & 15;
+      const bf16x8 k8 = *(const bf16x8*)(kb8 + tile_off(r, ch));
+      const bf16x8 v8 = *(const bf16x8*)(vb8 + tile_off(r, ch));
+      if (kw0 + r < a.Lkv) {
+        *(bf16x8*)(kop0 + (int64_t)(kw0 + r) * a.dk_sl + ch * 8) = k8;
+        *(bf16x8*)(vop0 + (int64_t)(kw0 + r) * a.dv_sl + ch * 8) = v8;
       }
     }
   }
