@@ -13,8 +13,6 @@
 // P is recomputed from the forward's lse, so nothing of size Lq x Lkv is stored.
 //
 // Kernels:
-//   bwd_prep_kernel     delta = rowsum(dO * O) and lse2 = lse * log2(e) (+inf for a row with no
-//                       allowed key, so its probabilities are exactly 0);
 //   bwd_dq_kernel       one workgroup of 4 waves per (b, query head, 128-query block), walking the
 //                       row's BlockMask tiles in steps of 64 keys. Orientation of the forward:
 //                       each wave computes S^T = K Q^T and dP^T = V dO^T with Q^T and dO^T held
@@ -22,7 +20,10 @@
 //                       dQ^T += K^T dA^T with dA^T straight from the accumulators as the B
 //                       operand and K^T read from LDS with ds_read_b64_tr_b16. K and V tiles
 //                       stream into two LDS buffers by global_load_lds, one step ahead; two
-//                       waves per SIMD. Also sums the ALiBi-slope gradient of its rows;
+//                       waves per SIMD. Its prologue computes each row's delta = dO . O and
+//                       lse2 = lse * log2(e) (+inf for a row with no allowed key, so its
+//                       probabilities are exactly 0) and writes them for the dK/dV pass, which
+//                       runs after it. Also sums the ALiBi-slope gradient of its rows;
 //   bwd_dkdv_kernel     one workgroup of 4 waves per (b, kv head, 128-key block), walking the
 //                       column's q blocks (the transposed BlockMask) for every query head of the
 //                       group, in steps of 64 queries. Mirrored orientation: S = Q K^T and
@@ -223,31 +224,6 @@ __device__ __forceinline__ float wave_sum(float x) {
 
 }  // namespace
 
-// delta = rowsum(dO * O) in fp32 and lse2 = lse * log2(e) (+inf where lse = -inf); 16 threads
-// per row, 16 rows per workgroup.
-__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
-  const int64_t rows = (int64_t)a.B * a.Hq * a.Lq;
-  const int64_t r = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int c = threadIdx.x & 15;
-  float acc = 0.f;
-  if (r < rows) {
-    const int qi = (int)(r % a.Lq);
-    const int64_t t = r / a.Lq;
-    const int hq = (int)(t % a.Hq), b = (int)(t / a.Hq);
-    const bf16x8 o = *(const bf16x8*)((const __bf16*)a.o + b * a.o_sb + hq * a.o_sh + (int64_t)qi * a.o_sl + c * 8);
-    const bf16x8 d = *(const bf16x8*)((const __bf16*)a.dout + b * a.do_sb + hq * a.do_sh + (int64_t)qi * a.do_sl + c * 8);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc = fmaf((float)o[e], (float)d[e], acc);
-  }
-#pragma unroll
-  for (int off = 8; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (c == 0 && r < rows) {
-    a.delta[r] = acc;
-    const float l = a.lse[r];
-    a.lse2[r] = l == -INFINITY ? INFINITY : l * kLog2e;
-  }
-}
-
 // ---------------------------------------------------------------------------------------------
 // Tile transfers. Each step moves 64 rows of two [L][128] bf16 tensors into LDS with
 // global_load_lds_dwordx4 (LDS written directly, no registers): 16 one-KB segments of 4 rows per
@@ -406,8 +382,27 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     doreg[ks] = *(const bf16x8*)(dop + ks * 16 + hl * 8);
   }
   const int64_t row = ((int64_t)b * a.Hq + hq) * a.Lq + qc;
-  const float lse2 = q_in ? a.lse2[row] : INFINITY;
-  const float delta = q_in ? a.delta[row] : 0.f;
+  // delta = dO . O of the row (the lane's 64 channels, then the other half's by lane swap) and
+  // lse2 = lse * log2(e), +inf for a row with no allowed key. Written for the dK/dV pass.
+  float lse2, delta;
+  {
+    const __bf16* orow = (const __bf16*)a.o + b * a.o_sb + hq * a.o_sh + (int64_t)qc * a.o_sl;
+    float dacc = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const bf16x8 o8 = *(const bf16x8*)(orow + ks * 16 + hl * 8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dacc = fmaf((float)o8[e], (float)doreg[ks][e], dacc);
+    }
+    const float dfull = half_swap_sum(dacc);
+    const float l = a.lse[row];
+    lse2 = q_in ? (l == -INFINITY ? INFINITY : l * kLog2e) : INFINITY;
+    delta = q_in ? dfull : 0.f;
+    if (q_in && hl == 0) {
+      a.delta[row] = delta;
+      a.lse2[row] = lse2;
+    }
+  }
   const int qdoc = doc ? a.q_doc[(int64_t)b * a.Lq + qc] : 0;
   const float slope = (SCORE & FA_SCORE_ALIBI) ? a.slopes[hq] : 0.f;
   const PairMask pm = make_pair_mask(a);
@@ -888,8 +883,8 @@ __global__ __launch_bounds__(256) void bm_transpose_kernel(TransposeArgs t) {
 template <int SCORE>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   // With no query rows, only dk / dv (zeros) and dslopes (zeros) are written.
-  const int64_t rows = (int64_t)a.B * a.Hq * a.Lq;
-  if (rows > 0) hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream, a);
+  // The dQ pass writes each row's delta and lse2, which the dK/dV pass reads: same stream, in
+  // this order.
   const int64_t nq = (int64_t)a.B * a.Hq * a.nqb;
   if (nq > 0) hipLaunchKernelGGL((bwd_dq_kernel<SCORE>), dim3((unsigned)nq), dim3(256), 0, stream, a);
   const int64_t nk = (int64_t)a.B * a.Hkv * a.nkvb;

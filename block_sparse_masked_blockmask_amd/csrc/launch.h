@@ -185,7 +185,7 @@ hipError_t launch_fwd_dense(const FwdArgs& a, int score, hipStream_t stream);
 // bf16 block-sparse forward, software-pipelined, 128-query blocks, masks without document ids
 // (nsplit 1); kv_block in {64, 128}.
 hipError_t launch_fwd_pipe(const FwdArgs& a, int kv_block, int score, hipStream_t stream);
-// Backward: delta/lse2 preparation, dq (+ slope partials), dk/dv, slope reduction.
+// Backward: dq (with the rows' delta and lse2, and the slope partials), dk/dv, slope reduction.
 hipError_t launch_bwd(const BwdArgs& a, int score, hipStream_t stream);
 hipError_t launch_block_mask_transpose(const TransposeArgs& t, hipStream_t stream);
 // Sort nsets row sets of a.nqb entries by row_order_key of (a.full_num, a.kv_num) into
