@@ -97,3 +97,20 @@ def test_dense_workload_refined():
         assert np.abs(l[0, hq, rows] - l_ref).max() <= 5e-2
     c = cosine(np.concatenate(outs), np.concatenate(refs))
     assert c >= 0.999, c
+
+
+@pytest.mark.parametrize("qk_block", [128, 32])
+@pytest.mark.parametrize("Lkv", [1, 40, 64, 65, 128, 150, 192, 256, 300])
+def test_short_rows_every_step_count(qk_block, Lkv):
+    """Key counts of 1 to 5 steps of 64 keys, ragged and whole: the forward keeps up to three
+    steps' transfers in flight and waits for all of them in the last two steps, so every step
+    count from 1 to 5 takes a different path through the ring. Cosine against the fp64 oracle on
+    the unquantized inputs, and lse within the quantized form's error."""
+    w = random_case(1300 + Lkv + qk_block, dtype="bf16", B=1, Hq=2, Hkv=2, Lq=130, Lkv=Lkv)
+    print(f"Lkv {Lkv} qk_block {qk_block}", flush=True)
+    _, out, lse = _run(w, qk_block, False)
+    qf, kf, vf = w.qkv_f32()
+    o_ref, l_ref = ref_attn.attention(qf, kf, vf, {})
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    assert cosine(out, o_ref) >= 0.999
+    assert np.abs(lse - l_ref).max() < 5e-2
