@@ -123,6 +123,21 @@ def test_null_block_mask_bf16_pipelined(Lkv, si):
     check_close(out.float().cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref, "bf16", f"null bm Lkv {Lkv} score {si}")
 
 
+@pytest.mark.parametrize("Lkv", [1, 40, 64, 65, 128, 129, 191, 192, 257])
+@pytest.mark.parametrize("kw", [dict(causal=True, softcap=20.0), dict(window=97, alibi=True), dict()])
+def test_interval_masks_bf16_pipelined_short_rows(Lkv, kw):
+    """bf16 with a 128-query BlockMask and a mask without document ids runs the software-pipelined
+    block-sparse kernel: lists of one to five 64-key steps (64- and 128-key tiles), exact and
+    ragged last tiles, halves of 128-key tiles past the last key, GQA 4:2."""
+    w = random_case(5200 + 7 * Lkv + len(kw), dtype="bf16", B=1, Hq=4, Hkv=2, Lq=150, Lkv=Lkv, **kw)
+    qf, kf, vf = w.qkv_f32()
+    o_ref, l_ref = ref_attn.attention(qf, kf, vf, spec_of(w))
+    for kvb in (64, 128):
+        out, lse, _ = run_gpu(w, kv_block=kvb, q_block=128)
+        check_close(out.float().cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref, "bf16",
+                    f"interval masks Lkv {Lkv} {sorted(kw)} kv{kvb}")
+
+
 def test_null_block_mask_bf16_strided_and_scale():
     import torch
     fa = _fa()
