@@ -110,11 +110,12 @@ def test_null_block_mask_dense(dtype):
     check_close(out.float().cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref, dtype, "null bm")
 
 
-@pytest.mark.parametrize("Lkv", [1, 40, 64, 65, 128, 129, 191, 192, 257, 1000])
+@pytest.mark.parametrize("Lkv", [1, 40, 64, 65, 128, 129, 191, 192, 256, 257, 320, 383, 384, 449, 1000])
 @pytest.mark.parametrize("si", range(len(SCORES)))
 def test_null_block_mask_bf16_pipelined(Lkv, si):
-    """bf16 without a BlockMask runs the software-pipelined every-tile-full kernel: one, two, three
-    and many 64-key steps, exact and ragged last steps, every score transform, GQA 6:2, B = 2."""
+    """bf16 without a BlockMask runs the software-pipelined every-tile-full kernel: one to eight and
+    sixteen 64-key steps (from three steps on the two wave groups run alternating phases, with one
+    or two steps after them), exact and ragged last steps, every score transform, GQA 6:2, B = 2."""
     kw = dict(SCORES[si])
     w = random_case(5000 + 7 * Lkv + si, dtype="bf16", B=2, Hq=6, Hkv=2, Lq=150, Lkv=Lkv, **kw)
     out, lse, _ = run_gpu(w, use_bm=False)
