@@ -558,6 +558,10 @@ fa_status flexattn_fwd_quant(const fa_tensor* q8, const fa_tensor* k8, const fa_
   return fwd_quantized(q8, k8, v8, nullptr, FA_MASK_NONE, FA_SCORE_NONE, p, out, lse, qk_block, q_delta, stream);
 }
 
+// A quantized tensor's scale array may be NULL only where it has no entries: Q and K scales are
+// per block of rows (none without rows), V scales per channel (always some while B > 0).
+static bool needs_scale(const fa_tensor* t, int rows) { return t->scale == nullptr && (int64_t)t->B * rows > 0; }
+
 static fa_status check_q_tensor(const fa_tensor* t, const char* name, int dtype, int elem_align) {
   if (t == nullptr) return fail(FA_ERR_INVALID_ARG, "%s is NULL", name);
   if (t->dtype != dtype) return fail(FA_ERR_INVALID_ARG, "%s has dtype %d, expected %d", name, t->dtype, dtype);
@@ -589,13 +593,15 @@ static fa_status quantize_impl(const fa_tensor* q, const fa_tensor* k, const fa_
   if ((st = check_q_tensor(k8, "k8", FA_I8, 16)) != FA_OK) return st;
   if ((st = check_q_tensor(v8, "v8", FA_FP8_E4M3, 16)) != FA_OK) return st;
   if (q->scale || k->scale || v->scale) return fail(FA_ERR_INVALID_ARG, "bf16 sources carry no scale");
-  if (!q8->scale || !k8->scale || !v8->scale) return fail(FA_ERR_INVALID_ARG, "q8, k8 and v8 need scale arrays");
+  if (needs_scale(q8, q8->L) || needs_scale(k8, k8->L) || needs_scale(v8, 1))
+    return fail(FA_ERR_INVALID_ARG, "q8, k8 and v8 need scale arrays");
   if (q8->B != q->B || q8->H != q->H || q8->L != q->L || k8->B != k->B || k8->H != k->H || k8->L != k->L ||
       v8->B != v->B || v8->H != v->H || v8->L != v->L)
     return fail(FA_ERR_INVALID_ARG, "quantized outputs must have the shapes of their sources");
   if ((int64_t)q->B * q->H > 65535 || (int64_t)k->B * k->H > 65535 || q->B > 65535)
     return fail(FA_ERR_UNSUPPORTED, "B and H above the grid limits");
-  if ((k_mean == nullptr) != (q_delta == nullptr))
+  // q_delta has one entry per query row: NULL is fine without rows.
+  if (k_mean == nullptr ? q_delta != nullptr : (q_delta == nullptr && (int64_t)q->B * q->L > 0))
     return fail(FA_ERR_INVALID_ARG, "K centering needs both k_mean and q_delta (or neither)");
   if (q->H % k->H != 0) return fail(FA_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", q->H, k->H);
   if (k_mean && (q->B != k->B)) return fail(FA_ERR_INVALID_ARG, "batch sizes differ");
@@ -654,7 +660,8 @@ static fa_status fwd_quantized(const fa_tensor* q, const fa_tensor* k, const fa_
   if ((st = check_q_tensor(k, "k", FA_I8, 16)) != FA_OK) return st;
   if ((st = check_q_tensor(v, "v", FA_FP8_E4M3, 16)) != FA_OK) return st;
   if ((st = check_q_tensor(out, "out", FA_BF16, 8)) != FA_OK) return st;
-  if (!q->scale || !k->scale || !v->scale) return fail(FA_ERR_INVALID_ARG, "quantized q, k and v need scale arrays");
+  if (needs_scale(q, q->L) || needs_scale(k, k->L) || needs_scale(v, 1))
+    return fail(FA_ERR_INVALID_ARG, "quantized q, k and v need scale arrays");
   if (out->scale) return fail(FA_ERR_INVALID_ARG, "out->scale must be NULL");
   if (mask_kind != FA_MASK_NONE || score_kind != FA_SCORE_NONE || bm != nullptr)
     return fail(FA_ERR_UNSUPPORTED, "the quantized form serves unmasked attention without score_mod (no BlockMask)");

@@ -72,7 +72,8 @@ enum { FA_MASK_NONE = 0, FA_MASK_DOC = 1, FA_MASK_CAUSAL = 2, FA_MASK_WINDOW = 4
 enum { FA_SCORE_NONE = 0, FA_SCORE_ALIBI = 1, FA_SCORE_SOFTCAP = 2 };
 
 /* A [B, H, L, D] tensor in device memory; element strides, the D dimension contiguous.
- * `scale` (device, float32) is used by the quantized dtypes only and must be NULL otherwise. */
+ * `scale` (device, float32) is used by the quantized dtypes only and must be NULL otherwise; a
+ * quantized Q or K tensor with no rows (B * L = 0) may leave it NULL, having no scales. */
 typedef struct {
   void* data;
   int32_t dtype;                 /* fa_dtype */
@@ -194,7 +195,8 @@ fa_status flexattn_quantize_qkv(const fa_tensor* q, const fa_tensor* k, const fa
  *     a double) / L, rounded to float32, written to k_mean (float32 [B][Hkv][128]); K is quantized
  *     as K - mean (one float32 subtraction per element), which leaves softmax(q.k) unchanged and
  *     moves each score row by -(q . mean) * sm_scale; q_delta (float32 [B][Hq][Lq], required with
- *     k_mean) receives q_i . mean of the row's kv head, which flexattn_fwd_quant adds back to lse;
+ *     k_mean unless B * Lq = 0) receives q_i . mean of the row's kv head, which
+ *     flexattn_fwd_quant adds back to lse;
  *   - workspace: flexattn_quantize_qkv_ex_workspace_bytes(B, Hkv, Lkv) bytes, 16-byte aligned,
  *     used only with centering (fp64 partial sums of the mean; contents afterwards unspecified).
  * qk_block other than 128 or 32 is FA_ERR_UNSUPPORTED. */

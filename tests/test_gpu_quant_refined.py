@@ -114,3 +114,31 @@ def test_short_rows_every_step_count(qk_block, Lkv):
     assert np.isfinite(out).all() and np.isfinite(lse).all()
     assert cosine(out, o_ref) >= 0.999
     assert np.abs(lse - l_ref).max() < 5e-2
+
+
+@pytest.mark.parametrize("qk_block", [128, 32])
+@pytest.mark.parametrize("center_k", [False, True])
+def test_empty_inputs(qk_block, center_k):
+    """No queries: nothing is launched and nothing written. No keys: every output row is 0 with
+    lse = -inf (the oracle's convention for a row without allowed keys), also with K centering,
+    whose mean over zero rows is 0."""
+    import torch
+    fa = _fa()
+    dev = torch.device("cuda", 0)
+    g = torch.Generator(device="cpu").manual_seed(77)
+    k = torch.randn((1, 2, 50, 128), generator=g).bfloat16().to(dev)
+    q0 = torch.zeros((1, 2, 0, 128), dtype=torch.bfloat16, device=dev)
+    print(f"empty q qk_block {qk_block} center {center_k}", flush=True)
+    qz = fa.flexattn_quantize_qkv_ex(q0, k, k, qk_block=qk_block, center_k=center_k)
+    out, lse = fa.flexattn_fwd_quant(qz)
+    torch.cuda.synchronize()
+    assert out.shape == (1, 2, 0, 128) and lse.shape == (1, 2, 0)
+    q = torch.randn((1, 4, 70, 128), generator=g).bfloat16().to(dev)
+    k0 = torch.zeros((1, 2, 0, 128), dtype=torch.bfloat16, device=dev)
+    print(f"empty kv qk_block {qk_block} center {center_k}", flush=True)
+    qz = fa.flexattn_quantize_qkv_ex(q, k0, k0, qk_block=qk_block, center_k=center_k)
+    out = torch.full((1, 4, 70, 128), float("nan"), dtype=torch.bfloat16, device=dev)
+    lse = torch.full((1, 4, 70), float("nan"), dtype=torch.float32, device=dev)
+    out, lse = fa.flexattn_fwd_quant(qz, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
